@@ -1,0 +1,119 @@
+"""Oracle attention: explicit frame masks and float64 softmax.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Notation (per layer): T tokens per latent frame, C frames per chunk, S sink
+frames, W window frames (the window includes the chunk being generated),
+H heads, D head dimension.  Token t of the generation history belongs to frame
+``t // T``; chunk c covers frames ``[c*C, (c+1)*C)``.
+
+What is computed, and where it is stated:
+
+* Frame-level autoregression with a KV cache: each chunk of latent frames is
+  generated conditioned on the cached keys/values of earlier chunks
+  (LongLive: Real-time Interactive Long Video Generation, Abstract and §3.2
+  "Streaming long tuning").  Causality is across chunks only: every query of a
+  chunk sees the same key set, which includes the whole current chunk.
+* Short-window attention: attention is restricted to a fixed window of the most
+  recent frames (same paper, §3.3 "Efficient long inference", short window
+  attention; Fig. 5 caption: window 9 latent frames + sink 3).
+* Frame sink: the tokens of the first frame chunk stay in the cache for good and
+  are concatenated to every layer's keys and values, so they are always
+  attendable; they share one softmax with the window (same paper, §3.3, frame
+  sink; §4 "Implementation": all tokens of the first frame chunk are the sink).
+* Text cross-attention: the prompt is injected by cross-attention layers that
+  alternate with self-attention in each DiT block (same paper, §3.1
+  "KV recache").  It is plain unmasked softmax attention to the text K/V.
+"""
+
+import numpy as np
+
+
+def allowed_frames(chunk, *, frames_per_chunk, sink_frames, window_frames):
+    """Set of frame indices the queries of chunk ``chunk`` may attend.
+
+    The sink is frames ``[0, S)``; the window is the W most recent frames
+    ending with the last frame of the current chunk, ``[(c+1)C - W, (c+1)C)``
+    clipped at 0.  The union is taken, so a frame in both is counted once
+    (LongLive paper, §3.3: sink tokens concatenated to the windowed K/V).
+    """
+    C, S, W = frames_per_chunk, sink_frames, window_frames
+    end = (chunk + 1) * C
+    start = max(0, end - W)
+    return set(range(0, min(S, end))) | set(range(start, end))
+
+
+def frame_mask(n_keys, chunk, *, tokens_per_frame, frames_per_chunk,
+               sink_frames, window_frames):
+    """Boolean key mask of length ``n_keys`` over the token history.
+
+    Key j is allowed iff its frame ``j // T`` is in :func:`allowed_frames`.
+    The mask is the same for every query of the chunk (no causal mask inside a
+    chunk: causality is across chunks).
+    """
+    frames = np.arange(n_keys) // tokens_per_frame
+    ok = allowed_frames(chunk, frames_per_chunk=frames_per_chunk,
+                        sink_frames=sink_frames, window_frames=window_frames)
+    return np.isin(frames, np.fromiter(ok, dtype=np.int64, count=len(ok)))
+
+
+def masked_attention(q, k, v, key_mask, scale, query_block=512):
+    """Softmax attention with an explicit key mask, in float64.
+
+    q: [n_q, H, D]; k: [n_k, H, D]; v: [n_k, H, Dv]; key_mask: bool [n_k]
+    (None = all keys).
+    Returns (out [n_q, H, Dv] float64, lse [H, n_q] float64), where
+    ``lse = log(sum_j exp(scale * q.k_j))`` over the allowed keys.
+
+    Logits are formed for every key and the masked ones set to -inf before the
+    softmax, so masked keys get probability exactly 0.  Queries are processed in
+    blocks only to bound memory; each block is the same plain formula.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if key_mask is None:
+        key_mask = np.ones(n_k, dtype=bool)
+    if not key_mask.any():
+        raise ValueError("attention over an empty key set is undefined")
+    out = np.empty((n_q, H, v.shape[2]), dtype=np.float64)
+    lse = np.empty((H, n_q), dtype=np.float64)
+    for h in range(H):
+        kh = k[:, h, :]
+        vh = v[:, h, :]
+        for q0 in range(0, n_q, query_block):
+            qb = q[q0:q0 + query_block, h, :]
+            logits = scale * (qb @ kh.T)                  # [b, n_k]
+            logits[:, ~key_mask] = -np.inf
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            s = e.sum(axis=1, keepdims=True)
+            p = e / s
+            out[q0:q0 + query_block, h, :] = p @ vh
+            lse[h, q0:q0 + query_block] = (m + np.log(s))[:, 0]
+    return out, lse
+
+
+def sink_window_attention(q, hist_k, hist_v, chunk, *, tokens_per_frame,
+                          frames_per_chunk, sink_frames, window_frames, scale,
+                          query_block=512):
+    """Attention of chunk ``chunk``'s queries over the frame sink + window.
+
+    ``hist_k``/``hist_v`` hold the layer's whole token history in generation
+    order, [n_hist, H, D]: every earlier chunk as it was appended (or as a
+    KV-recache rewrote it), followed by the current chunk's keys/values when
+    the call includes them.  Nothing is dropped from the history; the frame
+    mask alone decides which keys take part.
+    """
+    mask = frame_mask(hist_k.shape[0], chunk, tokens_per_frame=tokens_per_frame,
+                      frames_per_chunk=frames_per_chunk, sink_frames=sink_frames,
+                      window_frames=window_frames)
+    return masked_attention(q, hist_k, hist_v, mask, scale, query_block)
+
+
+def cross_attention(q, k_txt, v_txt, scale, query_block=512):
+    """Unmasked softmax attention of the chunk's queries to the prompt's text
+    K/V (LongLive paper, §3.1: cross-attention layers inject the prompt)."""
+    return masked_attention(q, k_txt, v_txt, None, scale, query_block)

@@ -1,0 +1,474 @@
+"""Pins for the oracle, checked against things other than the oracle itself:
+a hand-derived golden table, a streaming simulation in pure Python, library
+attention (torch SDPA in float64), closed forms and invariants.
+
+Paper: LongLive: Real-time Interactive Long Video Generation (§3.1 KV recache,
+§3.3 short window attention + frame sink, §4 implementation, §4.5 ablation).
+"""
+
+import math
+import os
+from collections import deque
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+from oracle import (allowed_frames, frame_mask, masked_attention,
+                    sink_window_attention, cross_attention, CacheGeometry,
+                    LayerHistory, quantize_int8, dequantize_int8)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "attended_chunks.txt")
+
+
+# --------------------------------------------------------------------------
+# golden: attended chunks for the paper's window/sink settings
+# --------------------------------------------------------------------------
+
+def _golden_rows():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, chunks, frames = [p.strip() for p in line.split("|")]
+        name, C, S, W = head.split()
+        c, lst = chunks.split(":")
+        rows.append((name, int(C), int(S), int(W), int(c),
+                     [int(x) for x in lst.split()], int(frames)))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: f"{r[0]}-c{r[4]}")
+def test_golden_attended_chunks(row):
+    _, C, S, W, c, chunks, frames = row
+    ok = allowed_frames(c, frames_per_chunk=C, sink_frames=S, window_frames=W)
+    got_chunks = sorted({f // C for f in ok})
+    assert got_chunks == chunks
+    assert len(ok) == frames
+    # the token mask agrees with the frame set (T = 2 tokens per frame)
+    T = 2
+    n = (c + 1) * C * T
+    m = frame_mask(n, c, tokens_per_frame=T, frames_per_chunk=C,
+                   sink_frames=S, window_frames=W)
+    assert sorted({j // (C * T) for j in np.nonzero(m)[0]}) == chunks
+
+
+# --------------------------------------------------------------------------
+# brute force: streaming simulation with pure-Python loops
+# --------------------------------------------------------------------------
+
+def _bf_attend(qrow, keys, vals, scale):
+    """Pure-Python softmax attention of one query row over lists of rows."""
+    logits = [scale * sum(a * b for a, b in zip(qrow, k)) for k in keys]
+    m = max(logits)
+    e = [math.exp(x - m) for x in logits]
+    s = sum(e)
+    D = len(vals[0])
+    out = [sum(e[j] / s * vals[j][d] for j in range(len(keys))) for d in range(D)]
+    return out, m + math.log(s)
+
+
+def _streaming_bruteforce(qs, ks, vs, T, C, S, W, scale, recache_at=None):
+    """Streaming generation with an explicit cache: a sink list that fills with
+    the first S frames' tokens and a FIFO of window chunks that evicts the
+    oldest.  Every query of chunk c attends sink + cached window + chunk c.
+
+    ``recache_at``: {chunk index: (k_payload, v_payload)}, applied before that
+    chunk, rewriting the cached window chunks oldest first (sink kept).
+    Returns per chunk (out [n,H,D], lse [H,n]) as nested lists.
+    """
+    ct = C * T
+    R = (W - C) // C
+    sink_k, sink_v = [], []            # token rows, per head
+    fifo = deque()                     # (k_rows, v_rows) per window chunk
+    H = qs[0].shape[1]
+    results = []
+    for c in range(len(qs)):
+        if recache_at and c in recache_at:
+            pk, pv = recache_at[c]
+            new = deque()
+            for i in range(len(fifo)):
+                new.append((pk[i * ct:(i + 1) * ct], pv[i * ct:(i + 1) * ct]))
+            fifo = new
+        out = np.zeros(qs[c].shape)
+        lse = np.zeros((H, ct))
+        for h in range(H):
+            keys = [r[h].tolist() for r in sink_k]
+            vals = [r[h].tolist() for r in sink_v]
+            for (ck, cv) in fifo:
+                keys += [r[h].tolist() for r in ck]
+                vals += [r[h].tolist() for r in cv]
+            keys += [r[h].tolist() for r in ks[c]]
+            vals += [r[h].tolist() for r in vs[c]]
+            for i in range(ct):
+                o, l = _bf_attend(qs[c][i, h].tolist(), keys, vals, scale)
+                out[i, h] = o
+                lse[h, i] = l
+        results.append((out, lse))
+        # append chunk c: sink first, then the FIFO window
+        if len(sink_k) < S * T:
+            sink_k += list(ks[c])
+            sink_v += list(vs[c])
+        elif R > 0:
+            if len(fifo) == R:
+                fifo.popleft()
+            fifo.append((ks[c], vs[c]))
+    return results
+
+
+def _draw(rng, n_chunks, ct, H, D):
+    f = lambda: [rng.standard_normal((ct, H, D)) for _ in range(n_chunks)]
+    return f(), f(), f()
+
+
+def _oracle_stream(qs, ks, vs, g, scale, recache_at=None):
+    hist = LayerHistory(g)
+    res = []
+    for c in range(len(qs)):
+        if recache_at and c in recache_at:
+            hist.recache(*recache_at[c])
+        hk, hv = hist.keys(ks[c], vs[c])
+        res.append(sink_window_attention(
+            qs[c], hk, hv, c, tokens_per_frame=g.tokens_per_frame,
+            frames_per_chunk=g.frames_per_chunk, sink_frames=g.sink_frames,
+            window_frames=g.window_frames, scale=scale))
+        hist.append(ks[c], vs[c])
+    return res
+
+
+geom_strategy = st.tuples(
+    st.integers(1, 4),            # T
+    st.integers(1, 3),            # C
+    st.integers(0, 2),            # sink chunks
+    st.integers(0, 4),            # ring slots
+    st.integers(1, 2),            # H
+    st.sampled_from([4, 8]),      # D
+    st.integers(0, 2 ** 31 - 1),  # seed
+)
+
+
+@settings(max_examples=40, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(geom_strategy)
+def test_bruteforce_streaming(params):
+    """P1: oracle (explicit frame mask over the full history) equals a
+    pure-Python streaming simulation (sink list + FIFO window)."""
+    T, C, nsc, R, H, D, seed = params
+    S, W = nsc * C, (R + 1) * C
+    g = CacheGeometry(T, C, S, W)
+    rng = np.random.default_rng(seed)
+    n_chunks = nsc + R + 3
+    qs, ks, vs = _draw(rng, n_chunks, C * T, H, D)
+    scale = 1.0 / math.sqrt(D)
+    want = _streaming_bruteforce(qs, ks, vs, T, C, S, W, scale)
+    got = _oracle_stream(qs, ks, vs, g, scale)
+    for (wo, wl), (go, gl) in zip(want, got):
+        np.testing.assert_allclose(go, wo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gl, wl, rtol=0, atol=1e-12)
+
+
+@settings(max_examples=15, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(geom_strategy)
+def test_bruteforce_recache(params):
+    """KV-recache: rewriting the resident window (oldest first, sink kept)
+    matches the streaming simulation that swaps its FIFO contents."""
+    T, C, nsc, R, H, D, seed = params
+    if R == 0:
+        R = 1
+    S, W = nsc * C, (R + 1) * C
+    g = CacheGeometry(T, C, S, W)
+    rng = np.random.default_rng(seed)
+    n_chunks = nsc + R + 4
+    ct = C * T
+    qs, ks, vs = _draw(rng, n_chunks, ct, H, D)
+    sw = nsc + R + 1                          # a chunk with a full window
+    pay = (rng.standard_normal((R * ct, H, D)), rng.standard_normal((R * ct, H, D)))
+    scale = 1.0 / math.sqrt(D)
+    want = _streaming_bruteforce(qs, ks, vs, T, C, S, W, scale, {sw: pay})
+    got = _oracle_stream(qs, ks, vs, g, scale, {sw: pay})
+    for (wo, wl), (go, gl) in zip(want, got):
+        np.testing.assert_allclose(go, wo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gl, wl, rtol=0, atol=1e-12)
+
+
+def test_bruteforce_tiny_fp32_config():
+    """P1 on the tiny fp32 workload: 1 head, D=64, 16 tokens/frame, chunk = 1
+    frame, sink 1 frame, window 2 frames, 8 chunks."""
+    from sink_short_window_amd import synth
+    T, C, S, W, H, D = 16, 1, 1, 2, 1, 64
+    g = CacheGeometry(T, C, S, W)
+    ct = C * T
+    qs = [synth.normal((ct, H, D), "f32", 0, 0, c, 0, synth.Q).astype(np.float64) for c in range(8)]
+    ks = [synth.normal((ct, H, D), "f32", 0, 0, c, 0, synth.K).astype(np.float64) for c in range(8)]
+    vs = [synth.normal((ct, H, D), "f32", 0, 0, c, 0, synth.V).astype(np.float64) for c in range(8)]
+    scale = 1.0 / math.sqrt(D)
+    want = _streaming_bruteforce(qs, ks, vs, T, C, S, W, scale)
+    got = _oracle_stream(qs, ks, vs, g, scale)
+    for (wo, wl), (go, gl) in zip(want, got):
+        np.testing.assert_allclose(go, wo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gl, wl, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# invariants against a library routine (torch SDPA, float64)
+# --------------------------------------------------------------------------
+
+def _sdpa(q, k, v, mask, scale):
+    """torch SDPA in float64; q [n,H,D], k/v [m,H,D], mask bool [n,m] or None."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+    tm = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("T,C,S,H,D,n_chunks", [(3, 2, 2, 2, 8, 5), (5, 1, 0, 1, 16, 6),
+                                                (2, 3, 3, 3, 4, 4)])
+def test_full_window_equals_block_causal(T, C, S, H, D, n_chunks):
+    """P2: when the window covers the whole history, sink+window attention is
+    full chunk-causal attention (every query sees all chunks <= its own)."""
+    W = C * n_chunks                     # window covers everything
+    g = CacheGeometry(T, C, S, W)
+    rng = np.random.default_rng(1)
+    ct = C * T
+    n = ct * n_chunks
+    q, k, v = (rng.standard_normal((n, H, D)) for _ in range(3))
+    chunk_of = np.arange(n) // ct
+    mask = chunk_of[None, :] <= chunk_of[:, None]
+    want = _sdpa(q, k, v, mask, 0.3)
+    for c in range(n_chunks):
+        sl = slice(c * ct, (c + 1) * ct)
+        got, _ = sink_window_attention(q[sl], k[:(c + 1) * ct], v[:(c + 1) * ct], c,
+                                       tokens_per_frame=T, frames_per_chunk=C,
+                                       sink_frames=S, window_frames=W, scale=0.3)
+        np.testing.assert_allclose(got, want[sl], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,C,S,R", [(4, 1, 1, 3), (2, 2, 2, 2), (3, 3, 3, 2)])
+def test_early_chunks_equal_block_causal(T, C, S, R):
+    """P8: before the window is full (c < sink chunks + R), nothing is evicted
+    and sink/window overlap is deduplicated: output = full chunk-causal."""
+    W = (R + 1) * C
+    nsc = S // C
+    rng = np.random.default_rng(2)
+    H, D = 2, 8
+    ct = C * T
+    n_chunks = nsc + R + 1
+    n = ct * n_chunks
+    q, k, v = (rng.standard_normal((n, H, D)) for _ in range(3))
+    chunk_of = np.arange(n) // ct
+    mask = chunk_of[None, :] <= chunk_of[:, None]
+    want = _sdpa(q, k, v, mask, 0.5)
+    for c in range(n_chunks):
+        sl = slice(c * ct, (c + 1) * ct)
+        got, _ = sink_window_attention(q[sl], k[:(c + 1) * ct], v[:(c + 1) * ct], c,
+                                       tokens_per_frame=T, frames_per_chunk=C,
+                                       sink_frames=S, window_frames=W, scale=0.5)
+        np.testing.assert_allclose(got, want[sl], rtol=0, atol=1e-12)
+
+
+def test_sink_only_equals_plain_attention_over_sink():
+    """P4: with no ring (W = C) and no current-chunk keys, a query chunk after
+    the sink attends exactly the sink: plain unmasked attention over it."""
+    T, C, S, H, D = 5, 2, 4, 3, 16
+    g = CacheGeometry(T, C, S, C)
+    rng = np.random.default_rng(3)
+    hist = LayerHistory(g)
+    for _ in range(5):
+        hist.append(rng.standard_normal((C * T, H, D)), rng.standard_normal((C * T, H, D)))
+    q = rng.standard_normal((C * T, H, D))
+    hk, hv = hist.keys()                           # no current chunk
+    got, lse = sink_window_attention(q, hk, hv, hist.chunks, tokens_per_frame=T,
+                                     frames_per_chunk=C, sink_frames=S,
+                                     window_frames=C, scale=0.25)
+    sink_k, sink_v = hk[:S * T], hv[:S * T]
+    want = _sdpa(q, sink_k, sink_v, None, 0.25)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # lse: log-sum-exp over the sink logits, via torch.logsumexp
+    lg = torch.einsum("ihd,jhd->hij", torch.from_numpy(q), torch.from_numpy(sink_k)) * 0.25
+    np.testing.assert_allclose(lse, torch.logsumexp(lg, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_cross_attention_matches_sdpa_and_single_key():
+    """P10: cross-attention is unmasked attention (SDPA); with one text token
+    the output is that token's value."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((7, 3, 8))
+    k = rng.standard_normal((5, 3, 8))
+    v = rng.standard_normal((5, 3, 8))
+    got, _ = cross_attention(q, k, v, 0.35)
+    np.testing.assert_allclose(got, _sdpa(q, k, v, None, 0.35), rtol=0, atol=1e-12)
+    got1, lse1 = cross_attention(q, k[:1], v[:1], 0.35)
+    np.testing.assert_allclose(got1, np.broadcast_to(v[:1], got1.shape), rtol=0, atol=1e-15)
+    want_lse = 0.35 * np.einsum("ihd,hd->hi", q, k[0])
+    np.testing.assert_allclose(lse1, want_lse, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# softmax rows, closed forms, order invariance
+# --------------------------------------------------------------------------
+
+def _probs_via_outputs(q, k, key_mask, scale):
+    """Recover the oracle's softmax rows by attending to one-hot values."""
+    n_k = k.shape[0]
+    H = q.shape[1]
+    eye = np.broadcast_to(np.eye(n_k)[:, None, :], (n_k, H, n_k)).copy()
+    p, _ = masked_attention(q, k, eye, key_mask, scale)
+    return p                                  # [n_q, H, n_k]
+
+
+def test_softmax_rows_sum_to_one_and_masked_are_zero():
+    """P3: every softmax row sums to 1, entries are >= 0 and masked keys get
+    exactly 0."""
+    T, C, S, W = 2, 2, 2, 4
+    rng = np.random.default_rng(5)
+    n_hist = 7 * C * T
+    q = rng.standard_normal((C * T, 2, 6)) * 3
+    k = rng.standard_normal((n_hist, 2, 6)) * 3
+    mask = frame_mask(n_hist, 6, tokens_per_frame=T, frames_per_chunk=C,
+                      sink_frames=S, window_frames=W)
+    p = _probs_via_outputs(q, k, mask, 0.7)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert (p >= 0).all()
+    assert (p[:, :, ~mask] == 0).all()
+    assert (p[:, :, mask] > 0).all()
+
+
+def test_closed_forms():
+    """P5: constant V gives that V; Q = 0 gives the mean of the allowed V and
+    lse = log(#allowed); one allowed key gives its V."""
+    T, C, S, W = 3, 1, 1, 2
+    H, D = 2, 8
+    rng = np.random.default_rng(6)
+    n_hist = 6 * T
+    c = 5
+    k = rng.standard_normal((n_hist, H, D))
+    q = rng.standard_normal((T, H, D))
+    kw = dict(tokens_per_frame=T, frames_per_chunk=C, sink_frames=S, window_frames=W, scale=0.4)
+    vconst = np.broadcast_to(rng.standard_normal((1, H, D)), (n_hist, H, D)).copy()
+    got, _ = sink_window_attention(q, k, vconst, c, **kw)
+    np.testing.assert_allclose(got, np.broadcast_to(vconst[:1], got.shape), rtol=0, atol=1e-12)
+
+    v = rng.standard_normal((n_hist, H, D))
+    got, lse = sink_window_attention(np.zeros_like(q), k, v, c, **kw)
+    allowed = [j for j in range(n_hist) if j // T in (0, 4, 5)]   # sink frame 0, window 4..5
+    np.testing.assert_allclose(got, np.broadcast_to(v[allowed].mean(0), got.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(len(allowed)), rtol=0, atol=1e-12)
+
+    # a single allowed key: T = 1, C = 1, no sink, window 1, first chunk
+    k1, v1 = rng.standard_normal((1, H, D)), rng.standard_normal((1, H, D))
+    q1 = rng.standard_normal((1, H, D))
+    got, _ = sink_window_attention(q1, k1, v1, 0, tokens_per_frame=1, frames_per_chunk=1,
+                                   sink_frames=0, window_frames=1, scale=1.0)
+    np.testing.assert_allclose(got, v1, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("segment", ["sink", "ring_old", "ring_new", "current", "evicted"])
+def test_planted_key_per_segment(segment):
+    """P5 planted key: a key aligned with a query (k = 40 q/|q|) dominates that
+    query's softmax when the key is attended (output ~ its value), and has no
+    effect when it lies in an evicted frame."""
+    T, C, S, W, H, D = 4, 1, 1, 3, 2, 16
+    rng = np.random.default_rng(7)
+    c = 6
+    n_hist = (c + 1) * T
+    k = rng.standard_normal((n_hist, H, D)) * 0.05
+    v = rng.standard_normal((n_hist, H, D))
+    q = rng.standard_normal((T, H, D))
+    frame = {"sink": 0, "ring_old": 4, "ring_new": 5, "current": 6, "evicted": 2}[segment]
+    j = frame * T + 1
+    i = 2
+    kw = dict(tokens_per_frame=T, frames_per_chunk=C, sink_frames=S, window_frames=W, scale=1.0)
+    base, _ = sink_window_attention(q, k, v, c, **kw)
+    k2 = k.copy()
+    k2[j] = 40.0 * q[i] / np.linalg.norm(q[i], axis=-1, keepdims=True)
+    got, _ = sink_window_attention(q, k2, v, c, **kw)
+    if segment == "evicted":
+        np.testing.assert_allclose(got, base, rtol=0, atol=1e-12)
+    else:
+        np.testing.assert_allclose(got[i], v[j], rtol=0, atol=1e-6)
+
+
+def test_key_order_invariance():
+    """P7: permuting the physical order of the keys (with their mask) does not
+    change the output: a ring may hold its chunks in any rotation."""
+    rng = np.random.default_rng(8)
+    n_k, H, D = 40, 2, 8
+    q = rng.standard_normal((6, H, D))
+    k = rng.standard_normal((n_k, H, D))
+    v = rng.standard_normal((n_k, H, D))
+    mask = rng.random(n_k) < 0.6
+    perm = rng.permutation(n_k)
+    a, la = masked_attention(q, k, v, mask, 0.3)
+    b, lb = masked_attention(q, k[perm], v[perm], mask[perm], 0.3)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-12)
+
+
+def test_empty_key_set_is_rejected():
+    with pytest.raises(ValueError):
+        masked_attention(np.zeros((1, 1, 2)), np.zeros((3, 1, 2)), np.zeros((3, 1, 2)),
+                         np.zeros(3, dtype=bool), 1.0)
+
+
+# --------------------------------------------------------------------------
+# INT8 quantiser
+# --------------------------------------------------------------------------
+
+def test_int8_quantiser_bounds_and_extremes():
+    """P9: |x - q s| <= s/2, |q| <= 127, the max-|x| element maps to +-127,
+    signs agree, a zero row maps to zero codes and a zero scale."""
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((200, 3, 64)) * rng.uniform(1e-3, 30, (200, 3, 1))).astype(np.float32)
+    x[5, 1] = 0.0
+    q, s = quantize_int8(x)
+    xh = dequantize_int8(q, s)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.abs(q.astype(int)).max() <= 127
+    err = np.abs(x.astype(np.float64) - xh)
+    assert (err <= s[..., None].astype(np.float64) * (0.5 + 1e-6)).all()
+    am = np.argmax(np.abs(x), axis=-1)
+    top = np.take_along_axis(q, am[..., None], -1)[..., 0].astype(int)
+    nz = s > 0
+    assert (np.abs(top[nz]) == 127).all()
+    assert (np.sign(q[q != 0]) == np.sign(x[q != 0])).all()
+    assert (q[5, 1] == 0).all() and s[5, 1] == 0
+
+
+def test_int8_quantiser_rounds_half_to_even():
+    """Round half to even at exact ties: a row with max 127 has scale 1.0, so
+    x/s is x itself; 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, 0.5 -> 0."""
+    x = np.zeros((1, 8), np.float32)
+    x[0, :6] = [127.0, 2.5, 3.5, -2.5, 0.5, -126.5]
+    q, s = quantize_int8(x)
+    assert s[0] == np.float32(1.0)
+    assert q[0, :6].tolist() == [127, 2, 4, -2, 0, -126]
+
+
+def test_int8_quantiser_power_of_two_scaling():
+    """Scaling a row by 2^k scales s by 2^k exactly and leaves q unchanged."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((50, 32)).astype(np.float32)
+    q1, s1 = quantize_int8(x)
+    q2, s2 = quantize_int8((x * np.float32(8.0)).astype(np.float32))
+    assert (q1 == q2).all()
+    assert (s2 == s1 * np.float32(8.0)).all()
+
+
+def test_int8_history_quantises_stored_chunks_only():
+    """The INT8 history holds dequantised stored K/V; the current chunk given
+    to keys() stays exact."""
+    g = CacheGeometry(2, 1, 1, 2)
+    rng = np.random.default_rng(11)
+    h = LayerHistory(g, int8=True)
+    k0 = rng.standard_normal((2, 1, 8)).astype(np.float32)
+    h.append(k0, k0)
+    q0, s0 = quantize_int8(k0)
+    np.testing.assert_array_equal(h.k[0], dequantize_int8(q0, s0))
+    cur = rng.standard_normal((2, 1, 8)).astype(np.float32)
+    hk, _ = h.keys(cur, cur)
+    np.testing.assert_array_equal(hk[2:], cur.astype(np.float64))
