@@ -1,0 +1,199 @@
+/*
+ * ll.h -- C ABI of the frame-sink + short-window KV-cache attention library
+ * (libll.so, HIP kernels for AMD Instinct MI355X / gfx950).
+ *
+ * What the library computes comes from the paper "LongLive: Real-time
+ * Interactive Long Video Generation":
+ *   - frame-level autoregressive generation conditioned on a per-layer KV
+ *     cache, causal across chunks of latent frames (Abstract; §3.2);
+ *   - short-window attention over the most recent frames plus a frame sink:
+ *     the first frame chunk's tokens are kept in the cache for good and are
+ *     concatenated to every layer's keys/values; the rest of the cache is a
+ *     short rolling window evicted in the usual way (§3.3 "Efficient long
+ *     inference"; §4 "Implementation");
+ *   - KV-recache at a prompt switch: the cache of the most recent window is
+ *     rebuilt (§3.1 "KV recache"; §3.3, last paragraph);
+ *   - text cross-attention injecting the prompt (§3.1).
+ *
+ * Notation.  T tokens per latent frame, C frames per chunk, S sink frames,
+ * W window frames (the window counts the chunk being generated), H heads,
+ * D head dimension.  C_tok = C*T tokens per chunk, R = (W-C)/C ring slots of
+ * one chunk each, n_sc = S/C sink chunks.  Chunk j's frames are [jC, (j+1)C).
+ *
+ * Conventions for every call.
+ *   - Pointers named q, k, v, k_cur, v_cur, k_txt, v_txt, out are DEVICE
+ *     pointers to token-major activations [n][H][D] (contiguous, element type
+ *     = the activation dtype, base 16-byte aligned).  lse is a nullable device
+ *     pointer to float [H][n_q].  Config, handle and query outputs are HOST
+ *     pointers.
+ *   - The library never allocates device memory and never frees the caller's.
+ *     The caller owns the cache's device buffer and every input/output, and
+ *     keeps them alive until the work enqueued on the stream has finished.
+ *   - All argument and state validation is synchronous and happens before
+ *     anything is enqueued.  On any error nothing is enqueued and no host
+ *     state changes; the status says why and ll_last_error() gives a
+ *     thread-local message.  A launch failure returns LL_ERR_HIP.  Device
+ *     faults surface at the caller's next synchronisation.  No C++ exception
+ *     crosses this ABI.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     All calls on one cache must be ordered on one stream (or otherwise
+ *     ordered by the caller): an append or recache overwrites ring slots that
+ *     an earlier attention call may still be reading.  Host state advances at
+ *     enqueue time.  A handle is not thread-safe.
+ */
+#ifndef LL_H
+#define LL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without pulling in the HIP headers (same underlying type). */
+typedef struct ihipStream_t* ll_stream_t;
+
+typedef struct ll_cache ll_cache; /* opaque host-side handle */
+
+typedef enum {
+  LL_OK = 0,
+  LL_ERR_INVALID_ARG = 1,      /* NULL/misaligned pointer, bad size or index */
+  LL_ERR_BAD_STATE = 2,        /* call not valid in the cache's current state */
+  LL_ERR_UNSUPPORTED = 3,      /* geometry or dtype combination not supported */
+  LL_ERR_BUFFER_TOO_SMALL = 4, /* device buffer smaller than required */
+  LL_ERR_HIP = 5,              /* a HIP launch/runtime call failed */
+  LL_ERR_INTERNAL = 6
+} ll_status;
+
+typedef enum { LL_F32 = 0, LL_BF16 = 1, LL_I8 = 2 } ll_dtype;
+
+/* Which cached tensor ll_cache_layout describes. */
+typedef enum { LL_WHICH_K = 0, LL_WHICH_V = 1, LL_WHICH_KSCALE = 2, LL_WHICH_VSCALE = 3 } ll_which;
+/* Which cache segment ll_cache_layout describes. */
+typedef enum { LL_SEG_SINK = 0, LL_SEG_RING = 1 } ll_segment;
+
+#define LL_MAX_RING_SLOTS 30
+
+/*
+ * Cache geometry.  Supported: head_dim in {64, 128}; sink_frames a multiple of
+ * frames_per_chunk (0 allowed: no sink); window_frames >= frames_per_chunk and
+ * window_frames - frames_per_chunk a multiple of frames_per_chunk with at most
+ * LL_MAX_RING_SLOTS ring slots; (act_dtype, kv_dtype) one of (F32, F32),
+ * (BF16, BF16), (BF16, I8).  With kv_dtype I8 the cache stores int8 K/V and an
+ * fp32 scale per (token, head): s = max|x|/127 (IEEE fp32 division),
+ * q = clamp(round_half_even(x/s), -127, 127), s = 0 and q = 0 for an all-zero
+ * vector.  (The paper mentions INT8 only for model weights; this per-token,
+ * per-head KV scheme is this library's own variant.)
+ */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t tokens_per_frame;
+  int32_t frames_per_chunk;
+  int32_t sink_frames;
+  int32_t window_frames; /* includes the chunk being generated */
+  int32_t act_dtype;     /* ll_dtype of q, k, v, k_cur, v_cur, out */
+  int32_t kv_dtype;      /* ll_dtype of the cached K/V */
+} ll_cache_config;
+
+/* Device bytes the cache needs for `cfg` (all layers), written to *bytes. */
+ll_status ll_cache_required_bytes(const ll_cache_config* cfg, size_t* bytes);
+
+/*
+ * Create a host handle over a caller-owned device buffer `dev_buf` of
+ * `dev_bytes` bytes (256-byte aligned, at least ll_cache_required_bytes).
+ * The buffer's contents need no initialisation: nothing is read before it is
+ * written.  The buffer must outlive the handle and all enqueued work.
+ */
+ll_status ll_cache_create(const ll_cache_config* cfg, void* dev_buf, size_t dev_bytes,
+                          ll_cache** out);
+
+/* Destroy the host handle (the device buffer is the caller's). NULL is a no-op. */
+ll_status ll_cache_destroy(ll_cache* cache);
+
+/* Forget every appended chunk in every layer (host-only; enqueues nothing). */
+ll_status ll_cache_reset(ll_cache* cache);
+
+/*
+ * Append the next chunk's keys/values to layer `layer` (paper §3.3: sink kept,
+ * rolling window evicted).  k, v: [C_tok][H][D] of act_dtype.  Appended chunk
+ * j goes to sink rows [j*C_tok, (j+1)*C_tok) while j < n_sc, else to ring slot
+ * (j - n_sc) mod R, overwriting (evicting) the oldest window chunk.  With
+ * R == 0 a non-sink chunk is counted but not stored.  With kv_dtype I8 the
+ * chunk is quantised on the way in.
+ */
+ll_status ll_cache_append_chunk(ll_cache* cache, int32_t layer, const void* k, const void* v,
+                                ll_stream_t stream);
+
+/*
+ * KV-recache (paper §3.1; §3.3: only the most recent window is rebuilt):
+ * rewrite every resident non-sink window chunk of layer `layer` in place,
+ * oldest to newest, from k, v: [n_tokens][H][D] of act_dtype, where n_tokens
+ * must equal (resident ring chunks) * C_tok.  layer == -1 rewrites all layers
+ * in one launch from k, v: [num_layers][n_tokens][H][D]; every layer must then
+ * hold the same number of resident ring chunks.  The sink is never rewritten.
+ * LL_ERR_BAD_STATE if no window chunk is resident.
+ */
+ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const void* v,
+                           int64_t n_tokens, ll_stream_t stream);
+
+/*
+ * Sink + short-window attention for the queries of the next chunk
+ * c = (chunks appended to `layer`) (paper §3.3).  Keys/values are, addressed
+ * in place without copies: the resident sink tokens, the resident ring chunks,
+ * and, when n_cur == C_tok, the caller's k_cur/v_cur [C_tok][H][D] of the
+ * current chunk (n_cur == 0: cache only).  One softmax runs over their union;
+ * there is no mask inside the set (causal across chunks only).
+ *   q, out: [n_q][H][D] act_dtype (n_q >= 0; 0 is a no-op).
+ *   scale:  logit scale, finite and > 0 (1/sqrt(D) in a standard DiT).
+ *   lse:    nullable float [H][n_q]: natural-log sum of exp(scale * q.k).
+ * Accumulation is fp32 (bf16 MFMA products for BF16 activations).
+ * LL_ERR_BAD_STATE if the key set is empty.
+ */
+ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                              const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                              void* out, float* lse, ll_stream_t stream);
+
+/*
+ * Text cross-attention (paper §3.1: cross-attention injects the prompt):
+ * unmasked softmax attention of q [n_q][H][D] to k_txt, v_txt [n_txt][H][D],
+ * all of `dtype` (F32 or BF16); out [n_q][H][D]; lse nullable [H][n_q];
+ * scale finite and > 0.
+ * head_dim in {64, 128}; n_txt >= 1.
+ */
+ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const void* v_txt,
+                        int64_t n_txt, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                        float scale, void* out, float* lse, ll_stream_t stream);
+
+/*
+ * Host state of one layer.  Any output pointer may be NULL.  slot_chunk, if
+ * given, receives R entries: the chunk index held by each ring slot, -1 if
+ * empty.  ring_next is the slot the next non-sink append writes.
+ */
+ll_status ll_cache_query(const ll_cache* cache, int32_t layer, int64_t* chunks_appended,
+                         int32_t* ring_valid, int32_t* ring_next, int64_t* slot_chunk);
+
+/*
+ * Where a cached tensor lives inside the device buffer, for snapshots and
+ * tests.  For (which, segment) it returns the byte offset (from dev_buf) of
+ * logical element [0][0][0] of a [H][rows][cols] view and its element strides;
+ * rows = S*T (sink) or R*C_tok (ring; slot s is rows [s*C_tok, (s+1)*C_tok));
+ * cols = D for K/V (element type kv_dtype) and 1 for the fp32 scales (I8
+ * only).  shape may be NULL.
+ */
+ll_status ll_cache_layout(const ll_cache* cache, int32_t layer, int32_t which, int32_t segment,
+                          size_t* byte_offset, int64_t* strides /*[3]*/, int64_t* shape /*[3]*/);
+
+/* Static text for a status code. */
+const char* ll_status_str(ll_status status);
+
+/* Thread-local message for the last error on this thread ("" if none). */
+const char* ll_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LL_H */

@@ -1,0 +1,98 @@
+// Host-side cache bookkeeping for the frame-sink + short-window KV cache.
+// No HIP in this translation unit: it is built into libll.so and, for CPU
+// tests, into a host-only shim.
+//
+// Policy (LongLive: Real-time Interactive Long Video Generation, §3.3
+// "Efficient long inference"): the first sink chunks are kept for good; the
+// remaining chunks go to a rolling window of R one-chunk slots, first in first
+// out.  A KV-recache (§3.1) rewrites the resident window chunks.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "ll.h"
+
+namespace ll {
+
+// Thread-local error text behind ll_last_error().
+void set_error(const std::string& msg);
+void clear_error();
+const char* last_error();
+ll_status fail(ll_status st, const std::string& msg);
+
+size_t dtype_bytes(int32_t dt);
+
+// Validated geometry with the derived sizes.
+struct Geometry {
+  int32_t L = 0, H = 0, D = 0, T = 0, C = 0, S = 0, W = 0;
+  int32_t act = 0, kv = 0;
+  int64_t ctok = 0;       // tokens per chunk, C*T
+  int32_t nsc = 0;        // sink chunks, S/C
+  int32_t R = 0;          // ring slots, (W-C)/C
+  int64_t sink_rows = 0;  // S*T
+  int64_t ring_rows = 0;  // R*ctok
+  int64_t rows = 0;       // sink_rows + ring_rows, per head
+};
+
+ll_status make_geometry(const ll_cache_config* cfg, Geometry* g);
+
+// Byte layout of the device buffer.  Per layer, in order, each region
+// 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype), and with I8
+// K scales [H][rows], V scales [H][rows] (fp32).  Rows [0, sink_rows) are the
+// sink; ring slot s is rows sink_rows + [s*ctok, (s+1)*ctok).
+struct Layout {
+  size_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0;  // within a layer
+  size_t layer_bytes = 0;
+  size_t total_bytes = 0;
+};
+Layout make_layout(const Geometry& g);
+
+struct LayerState {
+  int64_t appended = 0;
+  int32_t ring_valid = 0;
+  int32_t ring_next = 0;
+  std::vector<int64_t> slot_chunk;  // R entries, -1 = empty
+};
+
+// Where the next append of a layer goes.
+struct AppendPlan {
+  bool store = false;  // false: non-sink chunk with R == 0 (counted only)
+  bool sink = false;
+  int64_t row0 = 0;    // first row inside the per-head [rows] range
+  int32_t slot = -1;
+  int64_t chunk = 0;
+};
+
+class CacheState {
+ public:
+  CacheState(const Geometry& g, void* buf) : g_(g), lay_(make_layout(g)), buf_(buf), layers_(g.L) {
+    reset();
+  }
+  const Geometry& geom() const { return g_; }
+  const Layout& layout() const { return lay_; }
+  void* buffer() const { return buf_; }
+  const LayerState& layer(int l) const { return layers_[l]; }
+
+  void reset();
+  AppendPlan plan_append(int layer) const;
+  void commit_append(int layer, const AppendPlan& p);
+  // Ring slots of the resident window chunks, oldest chunk first.
+  std::vector<int32_t> resident_slots(int layer) const;
+  // Valid sink rows of a layer (the sink fills one chunk at a time).
+  int64_t sink_valid_rows(int layer) const;
+
+ private:
+  Geometry g_;
+  Layout lay_;
+  void* buf_;
+  std::vector<LayerState> layers_;
+};
+
+}  // namespace ll
+
+struct ll_cache {
+  ll::CacheState state;
+};

@@ -1,0 +1,73 @@
+// Launch interface between the C ABI layer (ll_api.cpp) and the HIP kernels
+// (kernels.hip).  Plain structs, no HIP types: a stream is passed as void*.
+#pragma once
+
+#include <cstdint>
+
+#include "ll.h"
+
+namespace ll {
+
+// One contiguous run of keys, addressed in place.  Element (head h, key i of
+// the run, dim d) of K lives at k + (h*head_stride + i*row_stride + d) elements
+// (and likewise V).  For int8 runs, its scale is at ks[h*sc_head_stride + i].
+struct KvSeg {
+  const void* k;
+  const void* v;
+  const float* ks;  // int8 runs only
+  const float* vs;
+  int64_t head_stride;     // elements
+  int64_t row_stride;      // elements
+  int64_t sc_head_stride;  // floats
+  int32_t key_start;       // first key index of the run in the joint key space
+  int32_t len;             // keys in the run
+  int32_t quant;           // 1: int8 with scales, 0: activation dtype
+  int32_t pad_;
+};
+
+constexpr int kMaxSeg = LL_MAX_RING_SLOTS + 2;
+
+struct AttnArgs {
+  KvSeg seg[kMaxSeg];
+  int32_t n_seg = 0;
+  int32_t n_keys = 0;
+  const void* q = nullptr;  // [n_q][H][D]
+  void* out = nullptr;      // [n_q][H][D]
+  float* lse = nullptr;     // [H][n_q] or null
+  int32_t n_q = 0;
+  int32_t H = 0;
+  int32_t D = 0;
+  int32_t act = LL_BF16;    // dtype of q/out and of non-quantised runs
+  int32_t kv = LL_BF16;     // LL_I8 when some runs are int8
+  float scale = 1.f;
+};
+
+// Copy (or quantise) whole chunks of token-major K/V into cache rows.
+// Source chunk i of layer z is src + (z*src_layer_stride + i*ctok*H*D) elements
+// (token-major [ctok][H][D]); it goes to rows dst_row0[i] .. + ctok of every
+// head in the destination layer z (cache base + z*dst_layer_bytes).
+constexpr int kMaxCopyChunks = LL_MAX_RING_SLOTS + 1;
+struct CopyArgs {
+  const void* src_k = nullptr;
+  const void* src_v = nullptr;
+  int64_t src_layer_elems = 0;  // elements between layers of the source
+  char* dst = nullptr;          // cache buffer base of layer 0
+  int64_t dst_layer_bytes = 0;
+  int64_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0;  // bytes within a layer
+  int64_t rows = 0;             // rows per head in the cache
+  int32_t n_chunks = 0;
+  int32_t n_layers = 1;
+  int32_t dst_row0[kMaxCopyChunks];
+  int32_t ctok = 0;
+  int32_t H = 0;
+  int32_t D = 0;
+  int32_t act = LL_BF16;
+  int32_t kv = LL_BF16;
+};
+
+// Each returns 0 on success or the hipError_t code of the failed launch.
+int launch_attention(const AttnArgs& a, void* stream);
+int launch_copy_chunks(const CopyArgs& a, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace ll

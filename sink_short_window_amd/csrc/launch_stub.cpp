@@ -1,0 +1,77 @@
+// Host-only stand-in for the kernel launchers, linked with the real C ABI
+// layer (ll_api.cpp) and bookkeeping (cache_state.cpp) into a CPU test
+// library.  It records what would have been launched instead of launching,
+// and can fail the next launch on request, so the ABI's validation, state
+// machine, segment tables and error guarantees run on a machine without a GPU.
+// Never part of libll.so.
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace ll {
+namespace {
+AttnArgs g_attn;
+CopyArgs g_copy;
+int g_attn_calls = 0;
+int g_copy_calls = 0;
+int g_fail_next = 0;
+}  // namespace
+
+int launch_attention(const AttnArgs& a, void*) {
+  if (g_fail_next) {
+    g_fail_next = 0;
+    return 1;
+  }
+  g_attn = a;
+  ++g_attn_calls;
+  return 0;
+}
+
+int launch_copy_chunks(const CopyArgs& a, void*) {
+  if (g_fail_next) {
+    g_fail_next = 0;
+    return 1;
+  }
+  g_copy = a;
+  ++g_copy_calls;
+  return 0;
+}
+
+const char* hip_error_string(int) { return "launch failure injected by the host test stub"; }
+
+}  // namespace ll
+
+extern "C" {
+
+void llh_fail_next_launch(void) { ll::g_fail_next = 1; }
+int llh_attn_calls(void) { return ll::g_attn_calls; }
+int llh_copy_calls(void) { return ll::g_copy_calls; }
+
+// Last attention launch: n_seg, n_keys, and per run [k, v, head_stride,
+// row_stride, key_start, len, quant] (pointers as integers).
+int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][7] */) {
+  const ll::AttnArgs& a = ll::g_attn;
+  *n_keys = a.n_keys;
+  for (int i = 0; i < a.n_seg; ++i) {
+    const ll::KvSeg& s = a.seg[i];
+    int64_t* r = runs + 7 * i;
+    r[0] = int64_t(reinterpret_cast<intptr_t>(s.k));
+    r[1] = int64_t(reinterpret_cast<intptr_t>(s.v));
+    r[2] = s.head_stride;
+    r[3] = s.row_stride;
+    r[4] = s.key_start;
+    r[5] = s.len;
+    r[6] = s.quant;
+  }
+  return a.n_seg;
+}
+
+// Last copy launch: n_chunks, n_layers and the destination row of each chunk.
+int llh_last_copy(int32_t* n_layers, int32_t* dst_row0 /* [n_chunks] */) {
+  const ll::CopyArgs& c = ll::g_copy;
+  *n_layers = c.n_layers;
+  for (int i = 0; i < c.n_chunks; ++i) dst_row0[i] = c.dst_row0[i];
+  return c.n_chunks;
+}
+
+}  // extern "C"

@@ -1,0 +1,330 @@
+// The C ABI declared in include/ll.h: validation, host state, launches.
+//
+// Every entry point validates its arguments and the cache state first and
+// returns before enqueuing anything on error (no state change).  Host state
+// advances only after a successful launch.
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <string>
+
+#include "cache_state.hpp"
+#include "launch.hpp"
+#include "ll.h"
+
+using ll::fail;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ll_status check_layer(const ll_cache* c, int32_t layer, bool allow_all) {
+  if (!c) return fail(LL_ERR_INVALID_ARG, "cache handle is NULL");
+  const int L = c->state.geom().L;
+  if (layer == -1 && allow_all) return LL_OK;
+  if (layer < 0 || layer >= L)
+    return fail(LL_ERR_INVALID_ARG, "layer " + std::to_string(layer) + " out of range [0, " +
+                                        std::to_string(L) + ")");
+  return LL_OK;
+}
+
+ll_status check_act_ptr(const void* p, const char* name) {
+  if (!p) return fail(LL_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p, 16)) return fail(LL_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return LL_OK;
+}
+
+ll_status launched(int err, const char* what) {
+  if (err != 0)
+    return fail(LL_ERR_HIP, std::string(what) + ": " + ll::hip_error_string(err));
+  return LL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ll_status_str(ll_status s) {
+  switch (s) {
+    case LL_OK: return "LL_OK";
+    case LL_ERR_INVALID_ARG: return "LL_ERR_INVALID_ARG";
+    case LL_ERR_BAD_STATE: return "LL_ERR_BAD_STATE";
+    case LL_ERR_UNSUPPORTED: return "LL_ERR_UNSUPPORTED";
+    case LL_ERR_BUFFER_TOO_SMALL: return "LL_ERR_BUFFER_TOO_SMALL";
+    case LL_ERR_HIP: return "LL_ERR_HIP";
+    case LL_ERR_INTERNAL: return "LL_ERR_INTERNAL";
+  }
+  return "unknown ll_status";
+}
+
+const char* ll_last_error(void) { return ll::last_error(); }
+
+ll_status ll_cache_required_bytes(const ll_cache_config* cfg, size_t* bytes) {
+  ll::clear_error();
+  if (!bytes) return fail(LL_ERR_INVALID_ARG, "bytes is NULL");
+  ll::Geometry g;
+  ll_status st = ll::make_geometry(cfg, &g);
+  if (st != LL_OK) return st;
+  *bytes = ll::make_layout(g).total_bytes;
+  return LL_OK;
+}
+
+ll_status ll_cache_create(const ll_cache_config* cfg, void* dev_buf, size_t dev_bytes,
+                          ll_cache** out) {
+  ll::clear_error();
+  if (!out) return fail(LL_ERR_INVALID_ARG, "out is NULL");
+  ll::Geometry g;
+  ll_status st = ll::make_geometry(cfg, &g);
+  if (st != LL_OK) return st;
+  if (!dev_buf) return fail(LL_ERR_INVALID_ARG, "dev_buf is NULL");
+  if (!aligned(dev_buf, 256)) return fail(LL_ERR_INVALID_ARG, "dev_buf is not 256-byte aligned");
+  const size_t need = ll::make_layout(g).total_bytes;
+  if (dev_bytes < need)
+    return fail(LL_ERR_BUFFER_TOO_SMALL, "device buffer has " + std::to_string(dev_bytes) +
+                                             " bytes, needs " + std::to_string(need));
+  ll_cache* c = new (std::nothrow) ll_cache{ll::CacheState(g, dev_buf)};
+  if (!c) return fail(LL_ERR_INTERNAL, "out of host memory");
+  *out = c;
+  return LL_OK;
+}
+
+ll_status ll_cache_destroy(ll_cache* cache) {
+  ll::clear_error();
+  delete cache;
+  return LL_OK;
+}
+
+ll_status ll_cache_reset(ll_cache* cache) {
+  ll::clear_error();
+  if (!cache) return fail(LL_ERR_INVALID_ARG, "cache handle is NULL");
+  cache->state.reset();
+  return LL_OK;
+}
+
+ll_status ll_cache_query(const ll_cache* cache, int32_t layer, int64_t* chunks_appended,
+                         int32_t* ring_valid, int32_t* ring_next, int64_t* slot_chunk) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::LayerState& L = cache->state.layer(layer);
+  if (chunks_appended) *chunks_appended = L.appended;
+  if (ring_valid) *ring_valid = L.ring_valid;
+  if (ring_next) *ring_next = L.ring_next;
+  if (slot_chunk)
+    for (size_t s = 0; s < L.slot_chunk.size(); ++s) slot_chunk[s] = L.slot_chunk[s];
+  return LL_OK;
+}
+
+ll_status ll_cache_layout(const ll_cache* cache, int32_t layer, int32_t which, int32_t segment,
+                          size_t* byte_offset, int64_t* strides, int64_t* shape) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  if (!byte_offset || !strides) return fail(LL_ERR_INVALID_ARG, "byte_offset and strides must be non-NULL");
+  if (which < LL_WHICH_K || which > LL_WHICH_VSCALE)
+    return fail(LL_ERR_INVALID_ARG, "which must be K, V, KSCALE or VSCALE");
+  if (segment != LL_SEG_SINK && segment != LL_SEG_RING)
+    return fail(LL_ERR_INVALID_ARG, "segment must be SINK or RING");
+  const ll::Geometry& g = cache->state.geom();
+  const ll::Layout& lay = cache->state.layout();
+  const bool scale = which >= LL_WHICH_KSCALE;
+  if (scale && g.kv != LL_I8) return fail(LL_ERR_INVALID_ARG, "scales exist only for an I8 cache");
+  size_t base = lay.layer_bytes * size_t(layer);
+  size_t region = which == LL_WHICH_K ? lay.k_off : which == LL_WHICH_V ? lay.v_off
+                : which == LL_WHICH_KSCALE ? lay.ks_off : lay.vs_off;
+  const int64_t cols = scale ? 1 : g.D;
+  const size_t elt = scale ? sizeof(float) : ll::dtype_bytes(g.kv);
+  const int64_t row0 = segment == LL_SEG_SINK ? 0 : g.sink_rows;
+  const int64_t nrows = segment == LL_SEG_SINK ? g.sink_rows : g.ring_rows;
+  *byte_offset = base + region + size_t(row0 * cols) * elt;
+  strides[0] = g.rows * cols;
+  strides[1] = cols;
+  strides[2] = 1;
+  if (shape) {
+    shape[0] = g.H;
+    shape[1] = nrows;
+    shape[2] = cols;
+  }
+  return LL_OK;
+}
+
+ll_status ll_cache_append_chunk(ll_cache* cache, int32_t layer, const void* k, const void* v,
+                                ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  if ((st = check_act_ptr(k, "k")) != LL_OK || (st = check_act_ptr(v, "v")) != LL_OK) return st;
+  ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  const ll::AppendPlan p = cs.plan_append(layer);
+  if (p.store) {
+    ll::CopyArgs a;
+    a.src_k = k;
+    a.src_v = v;
+    a.src_layer_elems = 0;
+    a.dst = static_cast<char*>(cs.buffer()) + cs.layout().layer_bytes * size_t(layer);
+    a.dst_layer_bytes = int64_t(cs.layout().layer_bytes);
+    a.k_off = cs.layout().k_off; a.v_off = cs.layout().v_off;
+    a.ks_off = cs.layout().ks_off; a.vs_off = cs.layout().vs_off;
+    a.rows = g.rows;
+    a.n_chunks = 1;
+    a.n_layers = 1;
+    a.dst_row0[0] = int32_t(p.row0);
+    a.ctok = int32_t(g.ctok);
+    a.H = g.H; a.D = g.D; a.act = g.act; a.kv = g.kv;
+    st = launched(ll::launch_copy_chunks(a, stream), "append launch");
+    if (st != LL_OK) return st;
+  }
+  cs.commit_append(layer, p);
+  return LL_OK;
+}
+
+ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const void* v,
+                           int64_t n_tokens, ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, true);
+  if (st != LL_OK) return st;
+  if ((st = check_act_ptr(k, "k")) != LL_OK || (st = check_act_ptr(v, "v")) != LL_OK) return st;
+  ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  const int l0 = layer == -1 ? 0 : layer;
+  const int nl = layer == -1 ? g.L : 1;
+  const std::vector<int32_t> slots = cs.resident_slots(l0);
+  if (slots.empty()) return fail(LL_ERR_BAD_STATE, "no window chunk is resident: nothing to recache");
+  for (int l = l0 + 1; l < l0 + nl; ++l)
+    if (cs.resident_slots(l) != slots)
+      return fail(LL_ERR_BAD_STATE, "layer -1 needs every layer to hold the same ring state");
+  const int64_t want = int64_t(slots.size()) * g.ctok;
+  if (n_tokens != want)
+    return fail(LL_ERR_INVALID_ARG, "n_tokens " + std::to_string(n_tokens) + " != resident window tokens " +
+                                        std::to_string(want));
+  ll::CopyArgs a;
+  a.src_k = k;
+  a.src_v = v;
+  a.src_layer_elems = want * g.H * g.D;
+  a.dst = static_cast<char*>(cs.buffer()) + cs.layout().layer_bytes * size_t(l0);
+  a.dst_layer_bytes = int64_t(cs.layout().layer_bytes);
+  a.k_off = cs.layout().k_off; a.v_off = cs.layout().v_off;
+  a.ks_off = cs.layout().ks_off; a.vs_off = cs.layout().vs_off;
+  a.rows = g.rows;
+  a.n_chunks = int32_t(slots.size());
+  a.n_layers = nl;
+  for (size_t i = 0; i < slots.size(); ++i) a.dst_row0[i] = int32_t(g.sink_rows + slots[i] * g.ctok);
+  a.ctok = int32_t(g.ctok);
+  a.H = g.H; a.D = g.D; a.act = g.act; a.kv = g.kv;
+  return launched(ll::launch_copy_chunks(a, stream), "recache launch");
+}
+
+ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                              const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                              void* out, float* lse, ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  if (n_q < 0 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
+  if (n_cur != 0 && n_cur != g.ctok)
+    return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (n_q > 0) {
+    if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK) return st;
+    if (lse && !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  }
+  if (n_cur > 0) {
+    if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK)
+      return st;
+  }
+  const ll::Layout& lay = cs.layout();
+  const char* base = static_cast<const char*>(cs.buffer()) + lay.layer_bytes * size_t(layer);
+  const size_t kelt = ll::dtype_bytes(g.kv);
+  const bool q8 = g.kv == LL_I8;
+  ll::AttnArgs a;
+  int32_t keys = 0;
+  auto add_cache_run = [&](int64_t row0, int64_t len) {
+    ll::KvSeg& s = a.seg[a.n_seg++];
+    s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
+    s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
+    s.ks = q8 ? reinterpret_cast<const float*>(base + lay.ks_off) + row0 : nullptr;
+    s.vs = q8 ? reinterpret_cast<const float*>(base + lay.vs_off) + row0 : nullptr;
+    s.head_stride = g.rows * g.D;
+    s.row_stride = g.D;
+    s.sc_head_stride = g.rows;
+    s.key_start = keys;
+    s.len = int32_t(len);
+    s.quant = q8 ? 1 : 0;
+    keys += int32_t(len);
+  };
+  const int64_t sink_rows = cs.sink_valid_rows(layer);
+  if (sink_rows > 0) add_cache_run(0, sink_rows);
+  for (int32_t slot : cs.resident_slots(layer)) add_cache_run(g.sink_rows + int64_t(slot) * g.ctok, g.ctok);
+  if (n_cur > 0) {
+    ll::KvSeg& s = a.seg[a.n_seg++];
+    s.k = k_cur;
+    s.v = v_cur;
+    s.ks = s.vs = nullptr;
+    s.head_stride = g.D;
+    s.row_stride = int64_t(g.H) * g.D;
+    s.sc_head_stride = 0;
+    s.key_start = keys;
+    s.len = int32_t(n_cur);
+    s.quant = 0;
+    keys += int32_t(n_cur);
+  }
+  if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
+  if (n_q == 0) return LL_OK;
+  a.n_keys = keys;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.n_q = int32_t(n_q);
+  a.H = g.H;
+  a.D = g.D;
+  a.act = g.act;
+  a.kv = g.kv;
+  a.scale = scale;
+  return launched(ll::launch_attention(a, stream), "attention launch");
+}
+
+ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const void* v_txt,
+                        int64_t n_txt, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                        float scale, void* out, float* lse, ll_stream_t stream) {
+  ll::clear_error();
+  if (num_heads < 1) return fail(LL_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != LL_F32 && dtype != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (n_txt < 1 || n_txt > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_txt must be in [1, 2^30)");
+  if (n_q < 0 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
+  ll_status st;
+  if ((st = check_act_ptr(k_txt, "k_txt")) != LL_OK || (st = check_act_ptr(v_txt, "v_txt")) != LL_OK)
+    return st;
+  if (n_q == 0) return LL_OK;
+  if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK) return st;
+  if (lse && !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  ll::AttnArgs a;
+  ll::KvSeg& s = a.seg[0];
+  s.k = k_txt;
+  s.v = v_txt;
+  s.ks = s.vs = nullptr;
+  s.head_stride = head_dim;
+  s.row_stride = int64_t(num_heads) * head_dim;
+  s.sc_head_stride = 0;
+  s.key_start = 0;
+  s.len = int32_t(n_txt);
+  s.quant = 0;
+  a.n_seg = 1;
+  a.n_keys = int32_t(n_txt);
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.n_q = int32_t(n_q);
+  a.H = num_heads;
+  a.D = head_dim;
+  a.act = dtype;
+  a.kv = dtype;
+  a.scale = scale;
+  return launched(ll::launch_attention(a, stream), "cross-attention launch");
+}
+
+}  // extern "C"

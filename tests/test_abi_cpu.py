@@ -1,0 +1,326 @@
+"""CPU tests of the C ABI (no GPU).
+
+* libll.so loads and exports every function include/ll.h declares.
+* The real ABI layer and bookkeeping (ll_api.cpp + cache_state.cpp), linked
+  against a launch stub that records launches, are driven through their error
+  paths and state machine, and checked against the oracle's cache model:
+  slot assignment after every append (P6), recache destination order, and the
+  key-run table an attention call would launch with.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import CacheGeometry, DequeCacheModel, slot_of_chunk, resident_window_chunks, allowed_frames
+from sink_short_window_amd import ll, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ll.h")
+
+FAKE_BUF = 1 << 20          # never dereferenced by the stub
+FAKE_ACT = 1 << 30
+
+
+@pytest.fixture(scope="module")
+def libs():
+    if not (os.path.exists(build.LIB_LL) and os.path.exists(build.LIB_HOSTSTUB)):
+        build.build_all()
+    stub = ctypes.CDLL(build.LIB_HOSTSTUB)
+    ll.bind(stub)
+    stub.llh_last_attn.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    stub.llh_last_copy.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    return stub
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:ll_status|const char\s*\*)\s*(ll_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(ll.EXPORTS)
+
+
+def test_libll_loads_and_exports_every_declared_symbol():
+    if not os.path.exists(build.LIB_LL):
+        build.build_ll()
+    lib = ctypes.CDLL(build.LIB_LL)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def cfg(L=2, H=3, D=64, T=4, C=2, S=2, W=6, act=ll.LL_BF16, kv=ll.LL_BF16):
+    return ll.make_config(L, H, D, T, C, S, W, act, kv)
+
+
+def create(stub, c, nbytes=None):
+    need = ll.ll_cache_required_bytes(c, lib=stub)
+    h = ctypes.c_void_p()
+    st = stub.ll_cache_create(ctypes.byref(c), FAKE_BUF, need if nbytes is None else nbytes, ctypes.byref(h))
+    assert st == 0, stub.ll_last_error()
+    return h.value
+
+
+def status(stub, st):
+    return ll.STATUS[st]
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(D=96), "LL_ERR_UNSUPPORTED"),
+    (dict(S=3), "LL_ERR_UNSUPPORTED"),
+    (dict(W=5), "LL_ERR_UNSUPPORTED"),
+    (dict(W=1), "LL_ERR_UNSUPPORTED"),
+    (dict(C=1, W=40), "LL_ERR_UNSUPPORTED"),
+    (dict(L=0), "LL_ERR_INVALID_ARG"),
+    (dict(H=0), "LL_ERR_INVALID_ARG"),
+    (dict(T=0), "LL_ERR_INVALID_ARG"),
+    (dict(S=-2), "LL_ERR_INVALID_ARG"),
+    (dict(act=ll.LL_F32, kv=ll.LL_BF16), "LL_ERR_UNSUPPORTED"),
+    (dict(act=ll.LL_I8, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
+    (dict(act=ll.LL_F32, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
+])
+def test_config_rejected(libs, bad, code):
+    n = ctypes.c_size_t(123)
+    st = libs.ll_cache_required_bytes(ctypes.byref(cfg(**bad)), ctypes.byref(n))
+    assert status(libs, st) == code
+    assert libs.ll_last_error()
+    assert n.value == 123
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(kv=ll.LL_I8), dict(act=ll.LL_F32, kv=ll.LL_F32, D=128),
+                                dict(S=0, W=2), dict(T=1560, C=3, S=3, W=9, H=12, D=128, L=30)])
+def test_required_bytes_matches_layout(libs, kw):
+    c = cfg(**kw)
+    L, H, D, T, C, S, W = (c.num_layers, c.num_heads, c.head_dim, c.tokens_per_frame,
+                           c.frames_per_chunk, c.sink_frames, c.window_frames)
+    rows = S * T + (W - C) // C * C * T
+    esz = {ll.LL_F32: 4, ll.LL_BF16: 2, ll.LL_I8: 1}[c.kv_dtype]
+    kvb = _align(H * rows * D * esz)
+    scb = _align(H * rows * 4) if c.kv_dtype == ll.LL_I8 else 0
+    assert ll.ll_cache_required_bytes(c, lib=libs) == L * max(2 * kvb + 2 * scb, 256)
+    if kw.get("L") == 30:     # the paper-shaped 30-layer bf16 cache
+        assert ll.ll_cache_required_bytes(c, lib=libs) == 30 * 2 * 12 * 14040 * 128 * 2
+
+
+def test_create_errors(libs):
+    c = cfg()
+    need = ll.ll_cache_required_bytes(c, lib=libs)
+    h = ctypes.c_void_p()
+    assert status(libs, libs.ll_cache_create(ctypes.byref(c), None, need, ctypes.byref(h))) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_create(ctypes.byref(c), FAKE_BUF + 16, need, ctypes.byref(h))) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_create(ctypes.byref(c), FAKE_BUF, need - 1, ctypes.byref(h))) == "LL_ERR_BUFFER_TOO_SMALL"
+    assert status(libs, libs.ll_cache_create(ctypes.byref(c), FAKE_BUF, need, None)) == "LL_ERR_INVALID_ARG"
+    assert libs.ll_cache_destroy(None) == 0
+    for s in range(7):
+        assert libs.ll_status_str(s).decode() == ll.STATUS[s]
+
+
+def query(stub, h, layer, R):
+    return ll.ll_cache_query(h, layer, R, lib=stub)
+
+
+def test_append_state_matches_fifo_model(libs):
+    """P6 on the C++ bookkeeping: after every append, ll_cache_query and the
+    destination row of the launched copy equal the oracle's FIFO model."""
+    for (T, C, S, W) in [(4, 2, 2, 6), (4, 1, 0, 3), (2, 2, 4, 2), (1560, 3, 3, 9), (3, 1, 2, 5)]:
+        c = cfg(T=T, C=C, S=S, W=W)
+        g = CacheGeometry(T, C, S, W)
+        h = create(libs, c)
+        sim = DequeCacheModel(g)
+        R = g.ring_slots
+        for j in range(3 * (g.sink_chunks + R) + 5):
+            calls = libs.llh_copy_calls()
+            assert libs.ll_cache_append_chunk(h, 1, FAKE_ACT, FAKE_ACT, None) == 0
+            where = sim.append()
+            assert where == slot_of_chunk(j, g)
+            if where[0] == "none":
+                assert libs.llh_copy_calls() == calls          # counted, not stored
+            else:
+                nl = ctypes.c_int32()
+                rows = (ctypes.c_int32 * 40)()
+                assert libs.llh_last_copy(ctypes.byref(nl), rows) == 1
+                want = where[1] * g.chunk_tokens if where[0] == "sink" else \
+                    g.sink_frames * T + where[1] * g.chunk_tokens
+                assert rows[0] == want
+            qd = query(libs, h, 1, R)
+            assert qd["chunks_appended"] == j + 1
+            assert qd["slot_chunk"] == sim.slot_chunk
+            assert qd["ring_valid"] == len(sim.fifo)
+            assert query(libs, h, 0, R)["chunks_appended"] == 0   # layers independent
+        libs.ll_cache_destroy(h)
+
+
+def test_append_errors_leave_state_unchanged(libs):
+    c = cfg()
+    h = create(libs, c)
+    R = 2
+    before = query(libs, h, 0, R)
+    assert status(libs, libs.ll_cache_append_chunk(h, 2, FAKE_ACT, FAKE_ACT, None)) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_append_chunk(h, -1, FAKE_ACT, FAKE_ACT, None)) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_append_chunk(h, 0, None, FAKE_ACT, None)) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_append_chunk(h, 0, FAKE_ACT + 8, FAKE_ACT, None)) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_append_chunk(None, 0, FAKE_ACT, FAKE_ACT, None)) == "LL_ERR_INVALID_ARG"
+    libs.llh_fail_next_launch()
+    assert status(libs, libs.ll_cache_append_chunk(h, 0, FAKE_ACT, FAKE_ACT, None)) == "LL_ERR_HIP"
+    assert "stub" in libs.ll_last_error().decode()
+    assert query(libs, h, 0, R) == before
+    assert libs.ll_cache_append_chunk(h, 0, FAKE_ACT, FAKE_ACT, None) == 0
+    assert libs.ll_last_error().decode() == ""
+    assert query(libs, h, 0, R)["chunks_appended"] == 1
+    assert libs.ll_cache_reset(h) == 0
+    assert query(libs, h, 0, R) == before
+    libs.ll_cache_destroy(h)
+
+
+def test_recache_targets_resident_window_oldest_first(libs):
+    T, C, S, W = 2, 1, 1, 4          # R = 3
+    c = cfg(L=3, T=T, C=C, S=S, W=W)
+    g = CacheGeometry(T, C, S, W)
+    h = create(libs, c)
+    ct = g.chunk_tokens
+    assert status(libs, libs.ll_cache_recache(h, 0, FAKE_ACT, FAKE_ACT, 0, None)) == "LL_ERR_BAD_STATE"
+    sim = DequeCacheModel(g)
+    for j in range(7):
+        for layer in range(3):
+            assert libs.ll_cache_append_chunk(h, layer, FAKE_ACT, FAKE_ACT, None) == 0
+        sim.append()
+        chunks = resident_window_chunks(j + 1, g)
+        if not chunks:
+            assert status(libs, libs.ll_cache_recache(h, 0, FAKE_ACT, FAKE_ACT, 0, None)) == "LL_ERR_BAD_STATE"
+            continue
+        n = len(chunks) * ct
+        assert status(libs, libs.ll_cache_recache(h, 0, FAKE_ACT, FAKE_ACT, n + ct, None)) == "LL_ERR_INVALID_ARG"
+        assert status(libs, libs.ll_cache_recache(h, 5, FAKE_ACT, FAKE_ACT, n, None)) == "LL_ERR_INVALID_ARG"
+        for layer in (1, -1):
+            assert libs.ll_cache_recache(h, layer, FAKE_ACT, FAKE_ACT, n, None) == 0
+            nl = ctypes.c_int32()
+            rows = (ctypes.c_int32 * 40)()
+            k = libs.llh_last_copy(ctypes.byref(nl), rows)
+            assert nl.value == (3 if layer == -1 else 1)
+            want = [S * T + sim.slot_chunk.index(ch) * ct for ch in chunks]
+            assert list(rows[:k]) == want
+    # layers out of step: layer -1 refused
+    assert libs.ll_cache_append_chunk(h, 0, FAKE_ACT, FAKE_ACT, None) == 0
+    n = len(resident_window_chunks(8, g)) * ct
+    assert status(libs, libs.ll_cache_recache(h, -1, FAKE_ACT, FAKE_ACT, n, None)) == "LL_ERR_BAD_STATE"
+    libs.ll_cache_destroy(h)
+
+
+def _layout(stub, h, layer, which, seg):
+    return ll.ll_cache_layout(h, layer, which, seg, lib=stub)
+
+
+def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
+    """The run table an attention call launches with covers exactly the sink
+    chunks and window chunks the frame definition allows (each once), points
+    at their rows, and ends with the current chunk."""
+    for (T, C, S, W) in [(4, 2, 2, 6), (4, 1, 0, 3), (2, 2, 4, 2), (1560, 3, 3, 9), (3, 1, 2, 5)]:
+        c = cfg(L=2, T=T, C=C, S=S, W=W, H=3, D=64)
+        g = CacheGeometry(T, C, S, W)
+        h = create(libs, c)
+        sim = DequeCacheModel(g)
+        ct = g.chunk_tokens
+        H, D = 3, 64
+        k_sink_off, st_sink, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
+        k_ring_off, st_ring, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_RING)
+        v_sink_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+        for chunk in range(3 * (g.sink_chunks + g.ring_slots) + 3):
+            for n_cur in (ct, 0):
+                st = libs.ll_sink_window_attn(h, 1, FAKE_ACT, 5, FAKE_ACT, FAKE_ACT, n_cur, 0.125,
+                                              FAKE_ACT, None, None)
+                if chunk == 0 and n_cur == 0:
+                    assert status(libs, st) == "LL_ERR_BAD_STATE"
+                    continue
+                assert st == 0, libs.ll_last_error()
+                nk = ctypes.c_int64()
+                runs = (ctypes.c_int64 * (7 * 40))()
+                n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+                covered = []
+                start = 0
+                for i in range(n_seg):
+                    kp, vp, hs, rs, ks, ln, q = runs[7 * i:7 * i + 7]
+                    assert ks == start and ln > 0 and q == 0
+                    start += ln
+                    if kp == FAKE_ACT:                 # current chunk, token-major
+                        assert i == n_seg - 1 and ln == ct and vp == FAKE_ACT
+                        assert (hs, rs) == (D, H * D)
+                        covered.append(chunk)
+                        continue
+                    assert (hs, rs) == (st_sink[0], D)
+                    row = (kp - FAKE_BUF - k_sink_off) // (2 * D)
+                    assert (vp - FAKE_BUF - v_sink_off) // (2 * D) == row
+                    assert ln % ct == 0
+                    for r0 in range(row, row + ln, ct):
+                        if r0 < S * T:
+                            covered.append(r0 // ct)               # sink chunk index
+                        else:
+                            covered.append(sim.slot_chunk[(r0 - S * T) // ct])
+                assert nk.value == start
+                ok = allowed_frames(chunk, frames_per_chunk=C, sink_frames=S, window_frames=W)
+                want = sorted({f // C for f in ok if n_cur or f // C != chunk})
+                assert sorted(covered) == want
+                assert len(covered) == len(set(covered))
+            assert libs.ll_cache_append_chunk(h, 1, FAKE_ACT, FAKE_ACT, None) == 0
+            sim.append()
+        libs.ll_cache_destroy(h)
+
+
+def test_attention_and_cross_attention_errors(libs):
+    c = cfg()
+    h = create(libs, c)
+    ct = 8
+    A = FAKE_ACT
+    ok = lambda st: status(libs, st)
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct - 1, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct, 0.0, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct, float("nan"), A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct, -1.0, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, None, 5, A, A, ct, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct, 0.1, A + 4, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, None, A, ct, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, 0, 0.1, A, None, None)) == "LL_ERR_BAD_STATE"
+    assert ok(libs.ll_sink_window_attn(h, 7, A, 5, A, A, ct, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_sink_window_attn(h, 0, A, -1, A, A, ct, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    calls = libs.llh_attn_calls()
+    assert libs.ll_sink_window_attn(h, 0, None, 0, A, A, ct, 0.1, None, None, None) == 0   # n_q = 0: no-op
+    assert libs.llh_attn_calls() == calls
+    libs.llh_fail_next_launch()
+    assert ok(libs.ll_sink_window_attn(h, 0, A, 5, A, A, ct, 0.1, A, None, None)) == "LL_ERR_HIP"
+    x = ok(libs.ll_cross_attn(A, 5, A, A, 0, 2, 64, ll.LL_BF16, 0.1, A, None, None))
+    assert x == "LL_ERR_INVALID_ARG"
+    assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 2, 80, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_UNSUPPORTED"
+    assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 2, 64, ll.LL_I8, 0.1, A, None, None)) == "LL_ERR_UNSUPPORTED"
+    assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 0, 64, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    assert libs.ll_cross_attn(A, 5, A, A, 3, 2, 64, ll.LL_BF16, 0.1, A, A, None) == 0
+    nk = ctypes.c_int64()
+    runs = (ctypes.c_int64 * (7 * 40))()
+    assert libs.llh_last_attn(ctypes.byref(nk), runs) == 1 and nk.value == 3
+    assert tuple(runs[2:4]) == (64, 128)
+    libs.ll_cache_destroy(h)
+
+
+def test_layout_queries(libs):
+    c = cfg(kv=ll.LL_I8, T=4, C=2, S=2, W=6, H=3, D=64)
+    h = create(libs, c)
+    rows = 2 * 4 + 2 * 8
+    off_k, st_k, sh_k = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
+    off_kr, st_kr, sh_kr = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_RING)
+    off_s, st_s, sh_s = _layout(libs, h, 1, ll.LL_WHICH_VSCALE, ll.LL_SEG_RING)
+    assert st_k == (rows * 64, 64, 1) and sh_k == (3, 8, 64)
+    assert sh_kr == (3, 16, 64) and off_kr == off_k + 8 * 64
+    assert st_s == (rows, 1, 1) and sh_s == (3, 16, 1)
+    assert off_k % 256 == 0
+    assert status(libs, libs.ll_cache_layout(h, 0, 9, 0, ctypes.byref(ctypes.c_size_t()),
+                                             (ctypes.c_int64 * 3)(), None)) == "LL_ERR_INVALID_ARG"
+    h2 = create(libs, cfg())
+    with pytest.raises(ll.LLError):
+        _layout(libs, h2, 0, ll.LL_WHICH_KSCALE, ll.LL_SEG_SINK)
+    libs.ll_cache_destroy(h)
+    libs.ll_cache_destroy(h2)

@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.
+
+Cache bytes (indexing, eviction order, recache placement, int8 codes and
+scales) must be bit-exact; outputs must be within 1e-4 max-abs (fp32) or
+2e-2 max-abs / 5e-3 mean-abs (bf16), plus the diagnostic relative-L2 and LSE
+gates.  Paper: LongLive: Real-time Interactive Long Video Generation, §3.1
+(KV recache), §3.3 (short window + frame sink).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (CacheGeometry, DequeCacheModel, LayerHistory, sink_window_attention,
+                    masked_attention, cross_attention, quantize_int8)
+from sink_short_window_amd import ll, synth
+from sink_short_window_amd.synth import Q, K, V, K_TXT, V_TXT, RK, RV
+from gpu_util import (need_gpu, say, dev, host, check_out, check_lse, act_code)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _expected_rows(chunks, payloads, ct):
+    """[H][n*ct][D] expected cache rows from token-major payloads."""
+    return np.concatenate([payloads[j].transpose(1, 0, 2) for j in chunks], axis=1)
+
+
+def _check_cache_bytes(cache, layer, g, sim, payloads, dtype, int8):
+    """Sink and ring rows equal the payloads the FIFO model says they hold."""
+    ct = g.chunk_tokens
+    segs = [(ll.LL_SEG_SINK, list(sim.sink))]
+    if g.ring_slots:
+        segs.append((ll.LL_SEG_RING, list(sim.slot_chunk)))
+    for which, tensor_payloads in ((ll.LL_WHICH_K, payloads[0]), (ll.LL_WHICH_V, payloads[1])):
+        for seg, chunks in segs:
+            got = cache.tensor(layer, which, seg)
+            for i, j in enumerate(chunks):
+                if j < 0:
+                    continue
+                rows = slice(i * ct, (i + 1) * ct)
+                x = tensor_payloads[j].transpose(1, 0, 2)          # [H][ct][D]
+                if int8:
+                    qw, sw = quantize_int8(np.ascontiguousarray(x, dtype=np.float32))
+                    gq = got[:, rows, :].cpu().numpy()
+                    assert np.array_equal(gq, qw), f"int8 codes differ (seg {seg}, chunk {j})"
+                    sc = cache.tensor(layer, ll.LL_WHICH_KSCALE if which == ll.LL_WHICH_K
+                                      else ll.LL_WHICH_VSCALE, seg)
+                    gs = sc[:, rows, 0].cpu().numpy()
+                    assert np.array_equal(gs.view(np.uint32), sw.view(np.uint32)), "scales differ"
+                elif dtype == "bf16":
+                    gb = got[:, rows, :].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                    assert np.array_equal(gb, synth.bf16_bits(x)), f"bytes differ (seg {seg}, chunk {j})"
+                else:
+                    gf = got[:, rows, :].cpu().numpy()
+                    assert np.array_equal(gf.view(np.uint32), x.astype(np.float32).view(np.uint32))
+
+
+def run_stream(cfg_id, T, C, S, W, H, D, dtype, n_chunks, int8=False, check_bytes=True,
+               n_cur_zero_at=()):
+    """Generate ``n_chunks`` chunks through the ABI and compare every attention
+    output with the oracle; check the cache bytes after every append."""
+    kv = ll.LL_I8 if int8 else act_code(dtype)
+    cfg = ll.make_config(1, H, D, T, C, S, W, act_code(dtype), kv)
+    cache = ll.Cache(cfg)
+    g = CacheGeometry(T, C, S, W)
+    hist = LayerHistory(g, int8=int8)
+    sim = DequeCacheModel(g)
+    ct = g.chunk_tokens
+    scale = 1.0 / math.sqrt(D)
+    payloads = ({}, {})
+    for c in range(n_chunks):
+        q = synth.normal((ct, H, D), dtype, cfg_id, 0, c, 0, Q)
+        k = synth.normal((ct, H, D), dtype, cfg_id, 0, c, 0, K)
+        v = synth.normal((ct, H, D), dtype, cfg_id, 0, c, 0, V)
+        dq, dk, dv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+        out = torch.empty_like(dq)
+        lse = torch.empty((H, ct), dtype=torch.float32, device="cuda")
+        use_cur = c not in n_cur_zero_at
+        if not use_cur and c == 0:
+            use_cur = True
+        say(f"[stream cfg={cfg_id} T={T} C={C} S={S} W={W} H={H} D={D} {dtype}{' i8' if int8 else ''}] chunk {c}")
+        cache.attn(0, dq, dk if use_cur else None, dv if use_cur else None, scale, out, lse)
+        torch.cuda.synchronize()
+        hk, hv = hist.keys(k, v) if use_cur else hist.keys()
+        want, wlse = sink_window_attention(q, hk, hv, c, tokens_per_frame=T, frames_per_chunk=C,
+                                           sink_frames=S, window_frames=W, scale=scale)
+        check_out(out, want, dtype, f"chunk {c}")
+        check_lse(lse, wlse, dtype, f"chunk {c}")
+        cache.append_chunk(0, dk, dv)
+        hist.append(k, v)
+        sim.append()
+        payloads[0][c], payloads[1][c] = k, v
+        if check_bytes:
+            torch.cuda.synchronize()
+            _check_cache_bytes(cache, 0, g, sim, payloads, dtype, int8)
+        q_state = cache.query(0)
+        assert q_state["chunks_appended"] == c + 1
+        assert q_state["slot_chunk"] == sim.slot_chunk
+    return cache
+
+
+def test_tiny_fp32_stream():
+    """Tiny fp32 workload: 1 head x 64, 16 tokens/frame, chunk = 1 frame,
+    sink 1 frame, window 2 frames, 8 chunks with append + evict."""
+    run_stream(0, 16, 1, 1, 2, 1, 64, "f32", 8)
+
+
+def test_fp32_d128_ragged():
+    run_stream(101, 37, 2, 2, 6, 2, 128, "f32", 6)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_stream_ragged_tiles(D):
+    """Several key tiles with ragged tails (chunk of 100 tokens, 400 keys
+    at steady state) and a ragged query tile."""
+    run_stream(102 + D, 50, 2, 2, 6, 2, D, "bf16", 7)
+
+
+def test_bf16_stream_two_sink_chunks_no_sink():
+    run_stream(110, 24, 1, 2, 3, 3, 128, "bf16", 7)      # sink = 2 chunks
+    run_stream(111, 24, 1, 0, 3, 3, 128, "bf16", 6)      # no sink (window only)
+
+
+def test_bf16_sink_only_cache_only():
+    """W = C (no ring) and n_cur = 0: a query chunk attends the sink alone."""
+    run_stream(112, 40, 2, 2, 2, 2, 128, "bf16", 5, n_cur_zero_at=(2, 3, 4))
+
+
+def test_bf16_max_ring_slots():
+    """The largest window: 30 ring slots (32 key runs per call)."""
+    run_stream(113, 8, 1, 1, 31, 2, 128, "bf16", 34, check_bytes=False)
+
+
+def test_int8_stream_bitexact_and_parity():
+    """INT8 KV: codes and scales bit-exact vs the oracle quantiser; attention
+    vs the oracle on the identically dequantised values."""
+    run_stream(120, 50, 2, 2, 6, 2, 128, "bf16", 6, int8=True)
+    run_stream(121, 33, 1, 1, 3, 3, 64, "bf16", 5, int8=True)
+
+
+def _config1_inputs(c, tensor):
+    return synth.normal((4680, 12, 128), "bf16", 1, 0, c, 0, tensor)
+
+
+def test_config1_snapshot_sampled():
+    """Single layer at full size: 12 heads x 128, 1560 tokens/frame, chunk = 3
+    frames (4680 tokens), sink 3 frames, window 9 frames.  Chunks 0..3 are
+    appended, then chunk 4 attends sink (chunk 0) + ring (chunks 3, 2) +
+    itself: 18720 keys.  Sampled query rows are checked against the oracle;
+    the cache bytes are checked in full."""
+    T, C, S, W, H, D = 1560, 3, 3, 9, 12, 128
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    ks, vs = {}, {}
+    for c in range(4):
+        ks[c], vs[c] = _config1_inputs(c, K), _config1_inputs(c, V)
+        cache.append_chunk(0, dev(ks[c], "bf16"), dev(vs[c], "bf16"))
+    q = _config1_inputs(4, Q)
+    k4, v4 = _config1_inputs(4, K), _config1_inputs(4, V)
+    out = torch.empty((4680, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, 4680), dtype=torch.float32, device="cuda")
+    say("[config1 snapshot] attention chunk 4 (18720 keys)")
+    cache.attn(0, dev(q, "bf16"), dev(k4, "bf16"), dev(v4, "bf16"), 1 / math.sqrt(D), out, lse)
+    torch.cuda.synchronize()
+    st = cache.query(0)
+    assert st["slot_chunk"] == [3, 2] and st["ring_valid"] == 2
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 4607, 4608, 4678, 4679],
+                                     rng.choice(4680, 246, replace=False)]))
+    hk = np.concatenate([ks[0], ks[2], ks[3], k4])
+    hv = np.concatenate([vs[0], vs[2], vs[3], v4])
+    want, wlse = masked_attention(q[rows], hk, hv, None, 1 / math.sqrt(D))
+    check_out(out[rows], want, "bf16", "config1 sampled rows")
+    check_lse(lse[:, rows], wlse, "bf16", "config1 sampled rows")
+    assert torch.isfinite(out.float()).all()
+    # cache bytes: sink = chunk 0, slot 0 = chunk 3, slot 1 = chunk 2
+    for which, src in ((ll.LL_WHICH_K, ks), (ll.LL_WHICH_V, vs)):
+        sink = cache.tensor(0, which, ll.LL_SEG_SINK).contiguous().view(torch.int16).cpu().numpy()
+        ring = cache.tensor(0, which, ll.LL_SEG_RING).contiguous().view(torch.int16).cpu().numpy()
+        assert np.array_equal(sink.view(np.uint16), synth.bf16_bits(src[0].transpose(1, 0, 2)))
+        want_ring = np.concatenate([src[3], src[2]]).transpose(1, 0, 2)
+        assert np.array_equal(ring.view(np.uint16), synth.bf16_bits(want_ring))
+
+
+def test_recache_all_layers_and_order_invariance():
+    """KV-recache of every layer (layer = -1): resident window chunks are
+    rewritten oldest first, bit-exact, the sink is kept, and attention equals
+    the oracle on the recached history.  Two caches holding the same logical
+    window in different physical slot orders give the same output (P7)."""
+    T, C, S, W, H, D, L = 40, 2, 2, 6, 2, 128, 3
+    g = CacheGeometry(T, C, S, W)
+    ct = g.chunk_tokens
+    scale = 1 / math.sqrt(D)
+    outs = []
+    for n_pre in (4, 5):                       # ring rotations differ
+        cfg = ll.make_config(L, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+        cache = ll.Cache(cfg)
+        hists = [LayerHistory(g) for _ in range(L)]
+        sims = [DequeCacheModel(g) for _ in range(L)]
+        for c in range(n_pre):
+            for layer in range(L):
+                k = synth.normal((ct, H, D), "bf16", 130, layer, c, 0, K)
+                v = synth.normal((ct, H, D), "bf16", 130, layer, c, 0, V)
+                cache.append_chunk(layer, dev(k, "bf16"), dev(v, "bf16"))
+                hists[layer].append(k, v)
+                sims[layer].append()
+        n = 2 * ct
+        pk = synth.normal((L, n, H, D), "bf16", 130, 0, 99, 0, RK)
+        pv = synth.normal((L, n, H, D), "bf16", 130, 0, 99, 0, RV)
+        say(f"[recache] n_pre={n_pre} layer=-1")
+        cache.recache(-1, dev(pk, "bf16"), dev(pv, "bf16"), n)
+        torch.cuda.synchronize()
+        q = synth.normal((ct, H, D), "bf16", 130, 0, 50, 0, Q)
+        kc = synth.normal((ct, H, D), "bf16", 130, 0, 50, 0, K)
+        vc = synth.normal((ct, H, D), "bf16", 130, 0, 50, 0, V)
+        for layer in range(L):
+            hists[layer].recache(pk[layer], pv[layer])
+            # bytes: oldest resident chunk's slot holds the payload's first chunk
+            sim = sims[layer]
+            for which, p in ((ll.LL_WHICH_K, pk[layer]), (ll.LL_WHICH_V, pv[layer])):
+                ring = cache.tensor(layer, which, ll.LL_SEG_RING)
+                for i, ch in enumerate(sim.resident_ring_chunks()):
+                    s = sim.slot_chunk.index(ch)
+                    got = ring[:, s * ct:(s + 1) * ct].contiguous().view(torch.int16).cpu().numpy()
+                    want = synth.bf16_bits(p[i * ct:(i + 1) * ct].transpose(1, 0, 2))
+                    assert np.array_equal(got.view(np.uint16), want)
+            out = torch.empty((ct, H, D), dtype=torch.bfloat16, device="cuda")
+            cache.attn(layer, dev(q, "bf16"), dev(kc, "bf16"), dev(vc, "bf16"), scale, out)
+            torch.cuda.synchronize()
+            hk, hv = hists[layer].keys(kc, vc)
+            want, _ = sink_window_attention(q, hk, hv, n_pre, tokens_per_frame=T, frames_per_chunk=C,
+                                            sink_frames=S, window_frames=W, scale=scale)
+            check_out(out, want, "bf16", f"recache n_pre={n_pre} layer {layer}")
+            if layer == 0:
+                outs.append(host(out))
+    # Same logical key set {sink = chunk 0, payload chunks, current} in both.
+    assert np.abs(outs[0] - outs[1]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("segment", ["sink", "ring_old", "ring_new", "current"])
+def test_planted_key_per_segment(segment):
+    """A key aligned with query i (k = 40 q_i/|q_i|) in each key run in turn:
+    the output row i is that key's value (detects a dropped run)."""
+    T, C, S, W, H, D = 64, 1, 1, 3, 2, 128
+    ct = T
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    c_now = 6
+    frame = {"sink": 0, "ring_old": 4, "ring_new": 5, "current": 6}[segment]
+    i, j = 9, 17
+    q = synth.normal((ct, H, D), "bf16", 140, 0, c_now, 0, Q)
+    plant = 40.0 * q[i] / np.linalg.norm(q[i], axis=-1, keepdims=True)
+    plant = synth.bf16_to_f32(synth.bf16_bits(plant.astype(np.float32)))
+    vals = {}
+    for c in range(c_now + 1):
+        k = synth.normal((ct, H, D), "bf16", 140, 0, c, 0, K) * np.float32(0.0625)
+        v = synth.normal((ct, H, D), "bf16", 140, 0, c, 0, V)
+        if c == frame:
+            k[j] = plant
+        vals[c] = (k, v)
+        if c < c_now:
+            cache.append_chunk(0, dev(k, "bf16"), dev(v, "bf16"))
+    k, v = vals[c_now]
+    out = torch.empty((ct, H, D), dtype=torch.bfloat16, device="cuda")
+    cache.attn(0, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), 1 / math.sqrt(D), out)
+    torch.cuda.synchronize()
+    got = host(out)[i]
+    want = vals[frame][1][j]
+    say(f"[planted {segment}] max diff {np.abs(got - want).max():.3e}")
+    assert np.abs(got - want).max() <= 2e-2
+
+
+def test_single_query_and_zero_queries():
+    T, C, S, W, H, D = 30, 1, 1, 2, 2, 128
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    k = synth.normal((T, H, D), "bf16", 150, 0, 0, 0, K)
+    v = synth.normal((T, H, D), "bf16", 150, 0, 0, 0, V)
+    q = synth.normal((1, H, D), "bf16", 150, 0, 0, 0, Q)
+    out = torch.empty((1, H, D), dtype=torch.bfloat16, device="cuda")
+    cache.attn(0, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), 0.1, out)
+    torch.cuda.synchronize()
+    want, _ = masked_attention(q, k, v, None, 0.1)
+    check_out(out, want, "bf16", "single query")
+    empty = torch.empty((0, H, D), dtype=torch.bfloat16, device="cuda")
+    cache.attn(0, empty, dev(k, "bf16"), dev(v, "bf16"), 0.1, empty)
+
+
+@pytest.mark.parametrize("dtype,D,n_q,n_txt", [("bf16", 128, 300, 512), ("bf16", 128, 4680, 512),
+                                               ("bf16", 64, 77, 33), ("f32", 64, 50, 77),
+                                               ("f32", 128, 20, 1)])
+def test_cross_attention(dtype, D, n_q, n_txt):
+    H = 12 if D == 128 and dtype == "bf16" else 3
+    q = synth.normal((n_q, H, D), dtype, 160, 0, n_q, 0, Q)
+    kt = synth.normal((n_txt, H, D), dtype, 160, 0, n_txt, 0, K_TXT)
+    vt = synth.normal((n_txt, H, D), dtype, 160, 0, n_txt, 0, V_TXT)
+    out = torch.empty((n_q, H, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device="cuda")
+    lse = torch.empty((H, n_q), dtype=torch.float32, device="cuda")
+    say(f"[cross-attn {dtype} D={D} n_q={n_q} n_txt={n_txt}]")
+    ll.ll_cross_attn(dev(q, dtype), dev(kt, dtype), dev(vt, dtype), 1 / math.sqrt(D), out,
+                     act_code(dtype), lse)
+    torch.cuda.synchronize()
+    rows = np.arange(n_q) if n_q <= 512 else np.unique(np.r_[0, 127, 128, n_q - 1,
+                                                              np.random.default_rng(0).choice(n_q, 200)])
+    want, wlse = cross_attention(q[rows], kt, vt, 1 / math.sqrt(D))
+    check_out(out[rows], want, dtype, "cross")
+    check_lse(lse[:, rows], wlse, dtype, "cross")
+    if n_txt == 1:
+        assert np.abs(host(out) - vt[0][None]).max() <= (1e-6 if dtype == "f32" else 1e-2)
