@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark: streaming 30-layer sink + short-window KV-cache step on one MI355X.
+
+Workload (LongLive: Real-time Interactive Long Video Generation, §3.1 KV
+recache, §3.3 short window + frame sink, §4 implementation; shapes of a 1.3B
+video DiT): 30 layers with independent caches, 12 heads x 128, 1560 tokens per
+latent frame, chunks of 3 latent frames (4680 tokens), sink = the first chunk
+(3 frames), window = 9 frames including the current chunk.
+
+One step = one generated chunk:
+  * before chunks 20, 30, ..., 70 (prompt switch): KV-recache of all 30
+    layers' resident window (fresh seeded N(0,1) bf16 K/V, sink kept) and a
+    new prompt's text K/V;
+  * 4 denoising passes x 30 layers of sink+window attention (queries of the
+    chunk over sink + ring + current chunk) and text cross-attention to 512
+    text tokens;
+  * one cache-append pass: 30 appends (the oldest window chunk is evicted).
+Warmup steps generate chunks 0.. W-1 untimed; the K timed steps continue the
+same stream.  ``--workload stream`` drops cross-attention and recache (the
+30-layer cache step alone); ``--kv int8`` stores K/V as int8 with per-token,
+per-head scales, dequantised inside the attention kernel.
+
+All inputs are seeded synthetic N(0,1) values (bf16) drawn on the host from
+pools and copied to the device once before timing.
+
+Prints ONE JSON line.  ``value`` is latent frames per second over the timed
+steps (3 latent frames per step); the attention kernel's roofline figures
+are measured live with HIP events around each attention launch.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + latent frames/sec (30-layer cache step) on 1 MI355X; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+# geometry
+L, H, D = 30, 12, 128
+T, C, S, W = 1560, 3, 3, 9
+CT = C * T                    # 4680 tokens per chunk
+N_TXT = 512
+PASSES = 4
+SWITCH_FIRST, SWITCH_EVERY = 20, 10
+POOL = 8                      # Q/K/V pool size
+TXT_POOL = 16
+RECACHE_POOL = 8
+CFG_ID = {"switch": 3, "stream": 2}
+
+
+def pool_index(layer, chunk, pass_):
+    """Which pooled Q/K/V tensor a (layer, chunk, pass) uses; pass 4 = append."""
+    return (7 * layer + 3 * chunk + pass_) % POOL
+
+
+def switches_before(chunk):
+    """Number of prompt switches that happen at or before ``chunk``."""
+    if chunk < SWITCH_FIRST:
+        return 0
+    return 1 + (chunk - SWITCH_FIRST) // SWITCH_EVERY
+
+
+def is_switch(chunk):
+    return chunk >= SWITCH_FIRST and (chunk - SWITCH_FIRST) % SWITCH_EVERY == 0
+
+
+def txt_index(prompt, layer):
+    return (prompt * L + layer) % TXT_POOL
+
+
+def recache_index(switch, layer):
+    return (3 * layer + switch) % RECACHE_POOL
+
+
+class Workload:
+    """Pools, caches and the per-chunk step, shared with the full-size test."""
+
+    def __init__(self, workload="switch", kv="bf16", device="cuda", n_chunks=80):
+        import torch
+        from sink_short_window_amd import ll, synth
+        self.torch, self.ll, self.synth = torch, ll, synth
+        self.workload, self.kv = workload, kv
+        self.cfg_id = CFG_ID[workload] + (10 if kv == "int8" else 0)
+        self.device = device
+        self.scale = 1.0 / math.sqrt(D)
+        gen = lambda shape, chunk, tensor: synth.to_torch(
+            synth.normal(shape, "bf16", self.cfg_id, 0, chunk, 0, tensor), "bf16", device)
+        # disjoint pools (different tensor ids) so no query equals a resident key
+        self.q = [gen((CT, H, D), i, synth.Q) for i in range(POOL)]
+        self.k = [gen((CT, H, D), i, synth.K) for i in range(POOL)]
+        self.v = [gen((CT, H, D), i, synth.V) for i in range(POOL)]
+        self.with_text = workload == "switch"
+        if self.with_text:
+            self.ktxt = [gen((N_TXT, H, D), i, synth.K_TXT) for i in range(TXT_POOL)]
+            self.vtxt = [gen((N_TXT, H, D), i, synth.V_TXT) for i in range(TXT_POOL)]
+            self.rk = [gen((2 * CT, H, D), i, synth.RK) for i in range(RECACHE_POOL)]
+            self.rv = [gen((2 * CT, H, D), i, synth.RV) for i in range(RECACHE_POOL)]
+        self.payload = {}
+        kvcode = ll.LL_I8 if kv == "int8" else ll.LL_BF16
+        cfg = ll.make_config(L, H, D, T, C, S, W, ll.LL_BF16, kvcode)
+        self.cache = ll.Cache(cfg, device)
+        self.out = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
+        self.xout = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
+        self.chunk = 0
+        self.timers = None
+
+    def recache_payload(self, switch):
+        """[L][2*CT][H][D] K and V for the ``switch``-th prompt switch."""
+        if switch not in self.payload:
+            t = self.torch
+            self.payload[switch] = (
+                t.stack([self.rk[recache_index(switch, l)] for l in range(L)]).contiguous(),
+                t.stack([self.rv[recache_index(switch, l)] for l in range(L)]).contiguous())
+        return self.payload[switch]
+
+    def prepare(self, chunks):
+        """Build every recache payload the given chunks need (before timing)."""
+        if self.with_text:
+            for c in chunks:
+                if is_switch(c):
+                    self.recache_payload(switches_before(c))
+
+    def _timed(self, kind, fn, work=0.0):
+        """Run ``fn``; with timers on, bracket it with HIP events recorded on
+        the stream the library launches on (torch's current stream)."""
+        if self.timers is None:
+            return fn()
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.timers.setdefault(kind, []).append((a, b, work))
+
+    def step(self, capture=None):
+        """Generate one chunk.  ``capture``: set of (pass, layer) whose
+        attention (and cross-attention) outputs are copied out and returned."""
+        ll, c = self.ll, self.chunk
+        cache = self.cache
+        got = {}
+        prompt = switches_before(c)
+        if self.with_text and is_switch(c):
+            pk, pv = self.recache_payload(prompt)
+            self._timed("recache", lambda: cache.recache(-1, pk, pv, 2 * CT))
+        for p in range(PASSES):
+            for layer in range(L):
+                i = pool_index(layer, c, p)
+                self._timed("attn", lambda: cache.attn(layer, self.q[i], self.k[i], self.v[i],
+                                                       self.scale, self.out),
+                            attn_flops(keys_at(c)))
+                if capture and (p, layer) in capture:
+                    got[(p, layer, "attn")] = self.out.clone()
+                if self.with_text:
+                    j = txt_index(prompt, layer)
+                    self._timed("cross", lambda: ll.ll_cross_attn(
+                        self.q[i], self.ktxt[j], self.vtxt[j], self.scale, self.xout, ll.LL_BF16))
+                    if capture and (p, layer) in capture:
+                        got[(p, layer, "cross")] = self.xout.clone()
+        for layer in range(L):
+            i = pool_index(layer, c, PASSES)
+            self._timed("append", lambda: cache.append_chunk(layer, self.k[i], self.v[i]))
+        self.chunk += 1
+        return got
+
+
+def kernel_stats(timers, kind):
+    """(average ms per launch, total work, total ms) of one kernel kind."""
+    ev = timers.get(kind, [])
+    if not ev:
+        return None, 0.0, 0.0
+    ms = [a.elapsed_time(b) for a, b, _ in ev]
+    return sum(ms) / len(ms), sum(w for _, _, w in ev), sum(ms)
+
+
+def keys_at(chunk):
+    """Keys attended by chunk ``chunk``: sink + resident ring chunks + itself."""
+    return CT * min(chunk + 1, 1 + (W - C) // C + 1)
+
+
+def attn_flops(n_keys):
+    """Algorithmic flop of one attention call: 4 * L_q * L_k * D * H."""
+    return 4.0 * CT * n_keys * D * H
+
+
+def cpu_baseline(k_steps, warmup, budget_s=20.0):
+    """Time the oracle (float64 numpy, as it stands) on a bounded sample of the
+    same workload and scale it to latent frames/s.
+
+    Sample: one steady-state attention call (chunk 4: sink + 2 ring chunks +
+    current chunk, 18720 allowed keys out of a 23400-key history), whole heads
+    at a time until ``budget_s`` is spent."""
+    import oracle
+    from sink_short_window_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    g = oracle.CacheGeometry(T, C, S, W)
+    hist = oracle.LayerHistory(g)
+    ks = [synth.normal((CT, H, D), "bf16", 90, 0, j, 0, synth.K) for j in range(5)]
+    vs = [synth.normal((CT, H, D), "bf16", 90, 0, j, 0, synth.V) for j in range(5)]
+    for j in range(4):
+        hist.append(ks[j], vs[j])
+    hk, hv = hist.keys(ks[4], vs[4])
+    q = synth.normal((CT, H, D), "bf16", 90, 0, 4, 0, synth.Q)
+    heads, spent = 0, 0.0
+    t0 = time.perf_counter()
+    while heads < H and spent < budget_s:
+        h = slice(heads, heads + 1)
+        oracle.sink_window_attention(q[:, h], hk[:, h], hv[:, h], 4, tokens_per_frame=T,
+                                     frames_per_chunk=C, sink_frames=S, window_frames=W,
+                                     scale=1 / math.sqrt(D))
+        heads += 1
+        spent = time.perf_counter() - t0
+    per_call = spent / heads * H             # one full call at a 5-chunk history
+    # The oracle masks the whole history, so its cost grows with the chunk
+    # index; scale each timed chunk's calls by its history length.
+    total = sum(PASSES * L * per_call * (c + 1) / 5.0 for c in range(warmup, warmup + k_steps))
+    return {"value": 3.0 * k_steps / total, "unit": "latent frames/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"oracle sink+window attention, {heads} of {H} heads x {CT} queries of one "
+                      f"call at chunk 4 (23400-key history, 18720 allowed) in {spent:.1f} s "
+                      f"({per_call:.1f} s per call); extrapolated to {PASSES}x{L} calls per chunk "
+                      f"for chunks {warmup}..{warmup + k_steps - 1} with cost scaled by history "
+                      f"length; cross-attention, append and recache not counted"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=36)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", choices=["switch", "stream"], default="switch")
+    ap.add_argument("--kv", choices=["bf16", "int8"], default="bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(each interactive stream is independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+    if args.warmup + args.steps > 80:
+        print("warmup + steps must be <= 80 chunks (240 latent frames)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+    wl = Workload(args.workload, args.kv)
+    wl.prepare(range(args.warmup + args.steps))
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps.  HIP events bracket every kernel launch on
+    # the launch stream, so per-kernel durations come from the same run.
+    wl.timers = {}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    first = wl.chunk
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        wl.step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timers, wl.timers = wl.timers, None
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = gpu_ms / args.steps
+    frames_per_s = 3.0 * args.steps / (gpu_ms / 1e3)
+
+    attn_ms, attn_work, attn_total_ms = kernel_stats(timers, "attn")
+    tflops = attn_work / (attn_total_ms * 1e-3) / 1e12 if attn_ms else None
+    keys = keys_at(first)
+    extra = {"attention_ms_per_call": attn_ms, "attention_tflops": tflops,
+             "attention_flop_per_call_steady": attn_flops(keys_at(10)),
+             "attention_calls": len(timers.get("attn", [])),
+             "attention_share_of_step": attn_total_ms / gpu_ms,
+             "timed_chunks": [first, first + args.steps - 1], "wall_s": wall}
+    app_ms, _, _ = kernel_stats(timers, "append")
+    if app_ms:
+        elt = 1 if args.kv == "int8" else 2
+        by = CT * H * D * 2 * 2 + CT * H * D * elt * 2 + (CT * H * 4 * 2 if args.kv == "int8" else 0)
+        extra["append_ms"] = app_ms
+        extra["append_GBps"] = by / (app_ms * 1e-3) / 1e9
+    x_ms, _, _ = kernel_stats(timers, "cross")
+    if x_ms:
+        xf = 4.0 * CT * N_TXT * D * H
+        extra["cross_attn_ms"] = x_ms
+        extra["cross_attn_tflops"] = xf / (x_ms * 1e-3) / 1e12
+    rc_ms, _, _ = kernel_stats(timers, "recache")
+    if rc_ms:
+        elt = 1 if args.kv == "int8" else 2
+        rc_bytes = L * 2 * (2 * CT * H * D) * (2 + elt) + (L * 2 * 2 * CT * H * 4 if args.kv == "int8" else 0)
+        extra["recache_ms"] = rc_ms
+        extra["recache_GBps"] = rc_bytes / (rc_ms * 1e-3) / 1e9
+
+    roofline = None
+    if tflops:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.steps, args.warmup, args.cpu_budget)
+
+    name = {"switch": "30-layer streaming step with prompt switches (KV-recache) and text cross-attention",
+            "stream": "30-layer streaming cache step"}[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": round(frames_per_s, 3),
+        "unit": "latent frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name + (" (int8 KV cache)" if args.kv == "int8" else ""),
+                   "layers": L, "heads": H, "head_dim": D, "tokens_per_frame": T,
+                   "chunk_frames": C, "sink_frames": S, "window_frames": W,
+                   "chunk_tokens": CT, "keys_per_call": keys, "denoise_passes": PASSES,
+                   "text_tokens": N_TXT if args.workload == "switch" else 0,
+                   "kv_cache": args.kv, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
