@@ -43,8 +43,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
 typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned))));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -57,15 +59,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
-// Combine a per-lane value with the one held by lane l^32 (the other half of
-// the wave, which owns the same query column).
-__device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32); }
+// Value held by lane l^32 (the other half of the wave, which owns the same
+// query column), via v_permlane32_swap: with operands (x, x) the first result
+// holds, in lanes 32..63, lanes 0..31 of x and the second result holds, in
+// lanes 0..31, lanes 32..63 of x.  Picking "second" in the low half and
+// "first" in the high half gives the partner's value whether or not both
+// operands share a register.
+__device__ __forceinline__ float partner_half(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, lane < 32 ? p[1] : p[0]);
+}
+__device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, partner_half(x)); }
+__device__ __forceinline__ float swap_halves_sum(float x) { return x + partner_half(x); }
 
 // gfx950 LDS transpose read of 4 bf16.  Within each group of 16 lanes, lane
 // i receives element (i & 3) of the 8 bytes addressed by lane 4*e + (i >> 2),
@@ -110,68 +123,180 @@ __device__ __forceinline__ int count_tiles(const AttnArgs& a) {
 // ---------------------------------------------------------------------------
 // bf16 activations (bf16 or int8 cache)
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// bf16 ping-pong kernel: 8 waves per workgroup in two groups of 4 (wave i and
+// wave i+4 share a SIMD), each wave owning 32 queries of one head, 256 queries
+// per workgroup.  Per key tile t a group runs
+//   M(t): S(t) = K(t) Q^T and O += V(t-1) P(t-1)^T   (MFMA phase)
+//   V(t): online softmax of S(t) -> P(t)             (VALU phase)
+// separated by workgroup barriers, with group B one barrier interval behind
+// group A: while one wave of a SIMD issues MFMAs the other runs its softmax.
+//
+// K/V tiles live in a 4-stage LDS ring, rows unpadded, with the 16-byte
+// granules of row r XOR-swizzled by (r mod granules-per-row) so the MFMA
+// operand reads of 32 consecutive rows spread over the banks.  bf16 tiles are
+// loaded straight from memory into LDS (buffer_load ... lds): group A loads
+// K(t+2) during its V(t), group B loads V(t+1) during its M(t), and each waits
+// for those loads two barrier intervals later, just before the barrier that
+// precedes their first use.  The int8 kernel stages through registers instead
+// (load tile t+3, convert and store tile t+2 during V(t)).
+// ---------------------------------------------------------------------------
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPBM = 32 * kPPWaves;  // queries per workgroup
+constexpr int kPPStages = 4;
+
 template <int D>
-struct Bf16Stage {
-  static constexpr int KS = D + 8;   // K row stride (elements): rows shift by 4 banks
-  static constexpr int VS = D + 32;  // V row stride (elements): rows shift by 16 banks
-  __bf16 k[kBN * KS];
-  __bf16 v[kBN * VS];
+struct SwzStage {
+  static constexpr int kRowB = D * 2;                // bytes per row
+  static constexpr int kGran = kRowB / 16;           // 16-byte granules per row
+  static constexpr int kRowsPerLoad = 1024 / kRowB;  // rows one 64-lane 16-byte load covers
+  __bf16 k[kBN * D];
+  __bf16 v[kBN * D];
   float ksc[kBN];
   float vsc[kBN];
 };
 
-// Per-thread share of one tile: kItems 16-byte vectors of K and of V.
+// Byte offset of logical granule g of row r inside a swizzled tile.  The two
+// operands are read differently, so they get different swizzles (both
+// measured bank-conflict-free on gfx950): K rows are read 16 bytes per lane
+// down 32 consecutive rows (XOR the granule with r mod G); V rows are read by
+// ds_read_b64_tr_b16, 4 rows x 32 bytes per 16 lanes (XOR with 2 (r mod G/2)).
 template <int D>
-struct Bf16Regs {
-  static constexpr int kVec = D / 8;                   // 8 bf16 per vector
-  static constexpr int kItems = kBN * kVec / kThreads; // per thread
-  u32x4 k[kItems];  // bf16 rows, or raw int8 bytes in the low 8 bytes
-  u32x4 v[kItems];
-  float ks, vs;
-  bool q8;          // the staged tile comes from an int8 run
+__device__ __forceinline__ int k_swz_gran(int r, int g) {
+  return g ^ (r & (SwzStage<D>::kGran - 1));
+}
+template <int D>
+__device__ __forceinline__ int v_swz_gran(int r, int g) {
+  return g ^ ((r & (SwzStage<D>::kGran / 2 - 1)) << 1);
+}
+template <int D>
+__device__ __forceinline__ int k_swz(int r, int g) {
+  return r * SwzStage<D>::kRowB + (k_swz_gran<D>(r, g) << 4);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r, int g) {
+  return r * SwzStage<D>::kRowB + (v_swz_gran<D>(r, g) << 4);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations; global
+// and LDS-DMA loads stay in flight (callers wait for them explicitly).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) (N <= 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Walks the 64-key tiles of the key runs, keeping the current run's buffer
+// resources (for one head) in scalar registers; the run table is read only
+// when the run changes.
+struct RunCursor {
+  int run;
+  int tile;
+  int len;
+  int quant;
+  uint32_t rs;  // row stride in bytes
+  __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
+
+  // Every field is uniform across the workgroup; readfirstlane says so to the
+  // compiler, which keeps the descriptors in scalar registers (a descriptor
+  // it believed divergent would turn each buffer load into a loop).
+  static __device__ __forceinline__ const char* uni(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+  }
+  __device__ void open(const AttnArgs& a, int head, int r) {
+    r = __builtin_amdgcn_readfirstlane(r);
+    run = r;
+    tile = 0;
+    if (r >= a.n_seg) return;
+    const KvSeg& s = a.seg[r];
+    quant = __builtin_amdgcn_readfirstlane(s.quant);
+    len = __builtin_amdgcn_readfirstlane(s.len);
+    const int elt = quant ? 1 : 2;
+    rs = __builtin_amdgcn_readfirstlane(uint32_t(s.row_stride) * elt);
+    const int64_t hoff = int64_t(head) * s.head_stride * elt;
+    rk = make_rsrc(uni(static_cast<const char*>(s.k) + hoff), uint32_t(len) * rs);
+    rv = make_rsrc(uni(static_cast<const char*>(s.v) + hoff), uint32_t(len) * rs);
+    if (quant) {
+      rks = make_rsrc(uni(s.ks + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
+      rvs = make_rsrc(uni(s.vs + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
+    }
+  }
+  __device__ void advance(const AttnArgs& a, int head) {
+    ++tile;
+    if (tile * kBN >= len) open(a, head, run + 1);
+  }
 };
 
-template <int D, bool kQ8>
-__device__ __forceinline__ void load_tile_bf16(const AttnArgs& a, int head, TileCursor cur,
-                                               Bf16Regs<D>& r) {
-  using R = Bf16Regs<D>;
-  const KvSeg& s = a.seg[cur.run];
+// LDS-DMA load of rows [row_lo, row_lo + 16) of a tile (bf16 runs).
+template <int D>
+__device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16* tile_base, int row_lo,
+                                         int lane) {
+  using S = SwzStage<D>;
+  const int row0 = c.tile * kBN;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += S::kRowsPerLoad) {
+    const int row = row_lo + r0 + lane / S::kGran;
+    const int pg = lane % S::kGran;
+    const int lg = v_side ? v_swz_gran<D>(row, pg) : k_swz_gran<D>(row, pg);  // XOR: its own inverse
+    const uint32_t voff = uint32_t(row0 + row) * c.rs + uint32_t(lg) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(v_side ? c.rv : c.rk,
+                                             (__attribute__((address_space(3))) void*)(tile_base + (row_lo + r0) * D),
+                                             16, voff, 0, 0, 0);
+  }
+}
+
+// Register staging for the int8 kernel: each thread owns kItems 16-byte
+// (bf16) or 8-byte (int8) vectors of K and of V.
+template <int D>
+struct PPRegs {
+  static constexpr int kVec = D / 8;
+  static constexpr int kItems = kBN * kVec / kPPThreads;
+  u32x4 k[kItems];
+  u32x4 v[kItems];
+  float ks, vs;
+  bool q8;
+};
+
+template <int D>
+__device__ __forceinline__ void pp_load(const RunCursor& c, PPRegs<D>& r) {
+  using R = PPRegs<D>;
   const int tid = threadIdx.x;
-  const int row0 = cur.tile * kBN;
-  const bool q8 = kQ8 && s.quant;
-  const int elt = q8 ? 1 : 2;
-  const uint32_t rs = uint32_t(s.row_stride) * elt;
-  const char* kb = static_cast<const char*>(s.k) + int64_t(head) * s.head_stride * elt;
-  const char* vb = static_cast<const char*>(s.v) + int64_t(head) * s.head_stride * elt;
-  const uint32_t bytes = uint32_t(s.len) * rs;
-  const auto rk = make_rsrc(kb, bytes);
-  const auto rv = make_rsrc(vb, bytes);
+  const int row0 = c.tile * kBN;
+  const bool q8 = c.quant;
 #pragma unroll
   for (int it = 0; it < R::kItems; ++it) {
-    const int item = tid + it * kThreads;
+    const int item = tid + it * kPPThreads;
     const int row = item / R::kVec, vec = item % R::kVec;
-    const uint32_t off = uint32_t(row0 + row) * rs;
+    const uint32_t off = uint32_t(row0 + row) * c.rs;
     if (q8) {
-      // converted when staged into LDS, so the loads stay in flight
-      const u32x2 kq = __builtin_amdgcn_raw_buffer_load_b64(rk, off + vec * 8, 0, 0);
-      const u32x2 vq = __builtin_amdgcn_raw_buffer_load_b64(rv, off + vec * 8, 0, 0);
+      const u32x2 kq = __builtin_amdgcn_raw_buffer_load_b64(c.rk, off + vec * 8, 0, 0);
+      const u32x2 vq = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off + vec * 8, 0, 0);
       r.k[it] = u32x4{kq[0], kq[1], 0, 0};
       r.v[it] = u32x4{vq[0], vq[1], 0, 0};
     } else {
-      r.k[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + vec * 16, 0, 0);
-      r.v[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + vec * 16, 0, 0);
+      r.k[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rk, off + vec * 16, 0, 0);
+      r.v[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rv, off + vec * 16, 0, 0);
     }
   }
   r.q8 = q8;
-  if constexpr (kQ8) {
-    // one scale per key row: threads 0..63 load the K and V scales
-    const int row = tid & (kBN - 1);
+  if (tid < kBN) {
     if (q8) {
-      const uint32_t sb = uint32_t(s.len) * 4;
-      const auto rks = make_rsrc(s.ks + int64_t(head) * s.sc_head_stride, sb);
-      const auto rvs = make_rsrc(s.vs + int64_t(head) * s.sc_head_stride, sb);
-      r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, uint32_t(row0 + row) * 4, 0, 0));
-      r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, uint32_t(row0 + row) * 4, 0, 0));
+      r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rks, uint32_t(row0 + tid) * 4, 0, 0));
+      r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rvs, uint32_t(row0 + tid) * 4, 0, 0));
     } else {
       r.ks = 1.f;
       r.vs = 1.f;
@@ -179,195 +304,307 @@ __device__ __forceinline__ void load_tile_bf16(const AttnArgs& a, int head, Tile
   }
 }
 
-template <int D, bool kQ8>
-__device__ __forceinline__ void store_tile_bf16(Bf16Stage<D>& st, const Bf16Regs<D>& r) {
-  using R = Bf16Regs<D>;
-  using S = Bf16Stage<D>;
+template <int D>
+__device__ __forceinline__ void pp_store(SwzStage<D>& st, const PPRegs<D>& r) {
+  using R = PPRegs<D>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int it = 0; it < R::kItems; ++it) {
-    const int item = tid + it * kThreads;
+    const int item = tid + it * kPPThreads;
     const int row = item / R::kVec, vec = item % R::kVec;
     u32x4 kw = r.k[it], vw = r.v[it];
-    if (kQ8 && r.q8) {
+    if (r.q8) {
       kw = int8x8_to_bf16x8(u32x2{kw[0], kw[1]});
       vw = int8x8_to_bf16x8(u32x2{vw[0], vw[1]});
     }
-    *reinterpret_cast<u32x4*>(&st.k[row * S::KS + vec * 8]) = kw;
-    *reinterpret_cast<u32x4*>(&st.v[row * S::VS + vec * 8]) = vw;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.k) + k_swz<D>(row, vec)) = kw;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.v) + v_swz<D>(row, vec)) = vw;
   }
-  if constexpr (kQ8) {
-    if (tid < kBN) {
-      st.ksc[tid] = r.ks;
-      st.vsc[tid] = r.vs;
-    }
+  if (tid < kBN) {
+    st.ksc[tid] = r.ks;
+    st.vsc[tid] = r.vs;
   }
 }
 
 template <int D, bool kQ8, bool kOneRun>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  using S = Bf16Stage<D>;
-  __shared__ __attribute__((aligned(16))) S stage[2];
+__global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
+  using S = SwzStage<D>;
+  constexpr int kLoads = 16 / S::kRowsPerLoad;  // DMA loads per wave per tile side
+  __shared__ __attribute__((aligned(16))) S stage[kPPStages];
 
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // group's branches and the buffer descriptors scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;
+  const int wq = wave & 3;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  const int qi = blockIdx.x * kBM + wave * 32 + r32;
+  const int qi = blockIdx.x * kPPBM + wave * 32 + r32;
   const bool q_ok = qi < a.n_q;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds Q[q][16j + 8*half + 0..7].
+  // Q fragment with the logit scale folded in: Q' = bf16(Q * scale * log2 e),
+  // so the MFMA yields scores in log2 units.
   bf16x8 qf[D / 16];
   {
     const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
       const u32x4 w = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
-      qf[j] = __builtin_bit_cast(bf16x8, w);
+      f32x8 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_bit_cast(float, w[i] << 16) * c;
+        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u) * c;
+      }
+      qf[j] = __builtin_convertvector(f, bf16x8);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -INFINITY;
+  // Running reference max in log2 units; the S accumulators start at -m_run
+  // (cinit), so the MFMA output is already c*q.k - m_run.
+  float m_run = 0.f;
+  f32x16 cinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cinit[r] = 0.f;
   float l_run = 0.f;
+  bf16x8 pb[4];  // P of the last softmaxed tile, one bf16x8 per 16-key step
 
-  // Lane-constant LDS offsets (elements).
-  // K A-operand: row = kb*32 + r32, cols 16j + 8*half.
-  const int k_off = r32 * S::KS + 8 * half;
-  // V transpose read: 16-lane group g, lane j in group.  The group reads rows
-  // 4*(g>>1) + (j>>2) (+ 16*step + 8*a) at cols 16*(g&1) + 4*(j&3) (+ 32*db);
-  // lane receives V[4 consecutive keys][d = 32*db + (lane & 31)].
+  // Byte offsets of this lane's operand reads.
+  // K (A of S^T): row kb*32 + r32, logical granule 2j + half, i.e. physical
+  // granule (2j ^ (r32 & ~1 & mask)) | (half ^ (r32 & 1)), formed per j.
+  const int k_row = r32 * S::kRowB + ((half ^ (r32 & 1)) << 4);
+  const int k_x = r32 & (S::kGran - 2);
+  // V (transpose reads): 16-lane group g16, lane j16 reads 4 elements of row
+  // 16*step + 8*a + 4*(g16 >> 1) + (j16 >> 2) at column
+  // 32*db + 16*(g16 & 1) + 4*(j16 & 3); the lane then holds V[4 keys][d].
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int v_off = (4 * (g16 >> 1) + (j16 >> 2)) * S::VS + 16 * (g16 & 1) + 4 * (j16 & 3);
+  int voff[2][D / 32];
+#pragma unroll
+  for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
+      const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+      voff[aa][db] = v_swz<D>(row, col >> 3) + ((col & 7) << 1);
+    }
 
-  const int n_tiles = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a);
-  TileCursor ld{0, 0};       // next tile to load
-  TileCursor cu{0, 0};       // tile being computed
-  Bf16Regs<D> regs;
-  load_tile_bf16<D, kQ8>(a, head, ld, regs);
-  ld.advance(a);
-  store_tile_bf16<D, kQ8>(stage[0], regs);
-  if (n_tiles > 1) {
-    load_tile_bf16<D, kQ8>(a, head, ld, regs);
-    ld.advance(a);
+  const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a);
+  RunCursor cu;  // tile being softmaxed (masking)
+  cu.open(a, head, 0);
+  RunCursor ld;  // int8 kernel: next tile to stage; bf16: next K tile (group A) / V tile (group B)
+  ld.open(a, head, 0);
+  PPRegs<D> regs;
+
+  // Prologue.
+  if constexpr (kQ8) {
+    // tiles 0, 1 into stages 0, 1; tile 2 into registers
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p < n) {
+        pp_load<D>(ld, regs);
+        ld.advance(a, head);
+        pp_store<D>(stage[p], regs);
+      }
+    }
+    if (n > 2) {
+      pp_load<D>(ld, regs);
+      ld.advance(a, head);
+    }
+  } else {
+    // group A: K(0), K(1); group B: V(0).  Afterwards A's cursor points at
+    // K(2) and B's at V(1).
+    if (group == 0) {
+      dma_rows<D>(ld, false, stage[0].k, 16 * wq, lane);
+      ld.advance(a, head);
+      if (n > 1) {
+        dma_rows<D>(ld, false, stage[1].k, 16 * wq, lane);
+        ld.advance(a, head);
+      }
+    } else {
+      dma_rows<D>(ld, true, stage[0].v, 16 * wq, lane);
+      ld.advance(a, head);
+    }
+    wait_vmcnt<0>();
   }
-  __syncthreads();
+  wg_barrier();
+  if (group == 1) wg_barrier();  // group B runs one interval behind
 
-  for (int g = 0; g < n_tiles; ++g) {
-    S& st = stage[g & 1];
-    // Stage tile g+1 (already in registers) and start loading tile g+2.
-    if (g + 1 < n_tiles) {
-      store_tile_bf16<D, kQ8>(stage[(g + 1) & 1], regs);
-      if (g + 2 < n_tiles) {
-        load_tile_bf16<D, kQ8>(a, head, ld, regs);
-        ld.advance(a);
+  f32x16 s[2];
+  for (int t = 0; t <= n; ++t) {
+    // ---------------- M(t): MFMA phase ----------------
+    __builtin_amdgcn_s_setprio(1);
+    bool issued = false;
+    if constexpr (!kQ8) {
+      if (group == 1 && t + 1 < n) {  // V(t+1) straight into LDS
+        dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
+        ld.advance(a, head);
+        issued = true;
       }
     }
-    const int valid = min(kBN, a.seg[cu.run].len - cu.tile * kBN);
-    cu.advance(a);
-
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 s[2];
+    if (t < n) {
+      const char* kt = reinterpret_cast<const char*>(stage[t % kPPStages].k);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < D / 16; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&st.k[k_off + kb * 32 * S::KS + 16 * j]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s[kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_row + (((2 * j) ^ k_x) << 4) + kb * 32 * S::kRowB);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], j == 0 ? cinit : s[kb], 0, 0, 0);
+        }
       }
     }
+    if (t >= 1) {
+      const __bf16* vt = stage[(t - 1) % kPPStages].v;
+#pragma unroll
+      for (int step = 0; step < 4; ++step) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const char* base = reinterpret_cast<const char*>(vt) + 16 * step * S::kRowB;
+          const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base + voff[0][db]));
+          const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + voff[1][db]));
+          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[step], o[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!kQ8) {
+      // group B: V(t) (issued one M phase ago) must be in LDS before A's M(t+1)
+      if (group == 1) {
+        if (issued) wait_vmcnt<kLoads>();
+        else wait_vmcnt<0>();
+      }
+    }
+    wg_barrier();
 
-    // Lane (q = r32, half) holds keys kb*32 + 8*(r/4) + 4*half + r%4.
-    if constexpr (kQ8) {
+    // ---------------- V(t): softmax phase ----------------
+    if (t < n) {
+      bool k_issued = false;
+      if constexpr (!kQ8) {
+        if (group == 0 && t + 2 < n) {  // K(t+2) straight into LDS
+          dma_rows<D>(ld, false, stage[(t + 2) % kPPStages].k, 16 * wq, lane);
+          ld.advance(a, head);
+          k_issued = true;
+        }
+      } else {
+        // stage tile t+2 (in registers since V(t-1)) and start loading tile t+3
+        if (t + 2 < n) {
+          pp_store<D>(stage[(t + 2) % kPPStages], regs);
+          if (t + 3 < n) {
+            pp_load<D>(ld, regs);
+            ld.advance(a, head);
+          }
+        }
+      }
+      const S& st = stage[t % kPPStages];
+      const int valid = min(kBN, cu.len - cu.tile * kBN);
+      cu.advance(a, head);
+      if constexpr (kQ8) {
+        // int8 runs: score = ksc * (q'.k_int); cinit is 0 for this kernel
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const float4 sc = *reinterpret_cast<const float4*>(&st.ksc[kb * 32 + 8 * gq + 4 * half]);
+            s[kb][4 * gq + 0] = fmaf(s[kb][4 * gq + 0], sc.x, -m_run);
+            s[kb][4 * gq + 1] = fmaf(s[kb][4 * gq + 1], sc.y, -m_run);
+            s[kb][4 * gq + 2] = fmaf(s[kb][4 * gq + 2], sc.z, -m_run);
+            s[kb][4 * gq + 3] = fmaf(s[kb][4 * gq + 3], sc.w, -m_run);
+          }
+      }
+      if (valid < kBN) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= valid) s[kb][r] = -INFINITY;
+          }
+      }
+      // tile max relative to m_run: four partial maxima, then the other half
+      float mp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
+      const float mx = swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+      // The first tile sets the reference; later tiles move it only when a
+      // score exceeds it by more than 2^8 (P stays <= 256).
+      if (t == 0 || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2)) {
+        const float sh = t == 0 ? mx : fmaxf(mx, 0.f);
+        if (t != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-sh);
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        }
+        m_run += sh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
+        if constexpr (!kQ8) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 sc = *reinterpret_cast<const float4*>(&st.ksc[kb * 32 + 8 * gq + 4 * half]);
-          s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
-          s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
-        }
-    }
-    if (valid < kBN) {
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
+      if constexpr (kQ8) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= valid) s[kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (log2 domain) ----
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = swap_halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kRescaleLog2)) {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = m_run * c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
-        l_run += p;
-        s[kb][r] = p;
+          for (int gq = 0; gq < 4; ++gq) {
+            const float4 sc = *reinterpret_cast<const float4*>(&st.vsc[kb * 32 + 8 * gq + 4 * half]);
+            // row sum uses the unscaled P; the V scale goes into P for PV
+            l_run += (s[kb][4 * gq + 0] + s[kb][4 * gq + 1]) + (s[kb][4 * gq + 2] + s[kb][4 * gq + 3]);
+            s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
+            s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
+          }
       }
-    if constexpr (kQ8) {
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int step = 0; step < 4; ++step) {
+        // P as bf16 pairs (one 32-bit word each) for the PV operand; the row
+        // sum adds exactly these rounded values, two per dot2.
+        u32x4 pw;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 sc = *reinterpret_cast<const float4*>(&st.vsc[kb * 32 + 8 * gq + 4 * half]);
-          s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
-          s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
+        for (int i = 0; i < 4; ++i) {
+          const f32x2 f = {s[step >> 1][8 * (step & 1) + 2 * i], s[step >> 1][8 * (step & 1) + 2 * i + 1]};
+          const bf16x2 b = __builtin_convertvector(f, bf16x2);
+          pw[i] = __builtin_bit_cast(unsigned, b);
+          if constexpr (!kQ8) ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
         }
-    }
-
-    // ---- O^T += V^T P^T: 4 steps of 16 keys ----
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const f32x16& sv = s[step >> 1];
-      const int t8 = 8 * (step & 1);
-      f32x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = sv[t8 + i];
-      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int base = v_off + 16 * step * S::VS + 32 * db;
-        const bf16x4 lo = tr_read(&st.v[base]);
-        const bf16x4 hi = tr_read(&st.v[base + 8 * S::VS]);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+        pb[step] = __builtin_bit_cast(bf16x8, pw);
+      }
+      l_run += ls[0] + ls[1];
+      if constexpr (!kQ8) {
+        // group A: K(t+1) (issued one V phase ago) must be in LDS before M(t+1)
+        if (group == 0) {
+          if (k_issued) wait_vmcnt<kLoads>();
+          else wait_vmcnt<0>();
+        }
       }
     }
-    __syncthreads();
+    wg_barrier();
   }
+  if (group == 0) wg_barrier();
 
-  // ---- epilogue: O = O^T / l, optional LSE ----
   const float l_tot = swap_halves_sum(l_run);
   if (!q_ok) return;
   const float inv = 1.f / l_tot;
@@ -381,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       const bf16x4 b = __builtin_convertvector(*reinterpret_cast<float __attribute__((__vector_size__(16)))*>(&f), bf16x4);
       *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + qrow + d0) = b;
     }
-  if (a.lse && half == 0) a.lse[int64_t(head) * a.n_q + qi] = (m_run * c + __log2f(l_tot)) * kLn2;
+  if (a.lse && half == 0) a.lse[int64_t(head) * a.n_q + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -596,20 +833,23 @@ int launch(K kernel, dim3 grid, dim3 block, const void* arg, void* stream) {
 }
 
 template <int D>
-int launch_attention_d(const AttnArgs& a, dim3 grid, void* stream) {
-  const dim3 block(kThreads);
-  if (a.act == LL_F32) return launch(attn_f32_kernel<D>, grid, block, &a, stream);
-  if (a.kv == LL_I8) return launch(attn_bf16_kernel<D, true, false>, grid, block, &a, stream);
-  if (a.n_seg == 1) return launch(attn_bf16_kernel<D, false, true>, grid, block, &a, stream);
-  return launch(attn_bf16_kernel<D, false, false>, grid, block, &a, stream);
+int launch_attention_d(const AttnArgs& a, void* stream) {
+  if (a.act == LL_F32) {
+    const dim3 grid((a.n_q + kBM - 1) / kBM, a.H);
+    return launch(attn_f32_kernel<D>, grid, dim3(kThreads), &a, stream);
+  }
+  const dim3 grid((a.n_q + kPPBM - 1) / kPPBM, a.H);
+  const dim3 block(kPPThreads);
+  if (a.kv == LL_I8) return launch(attn_pp_kernel<D, true, false>, grid, block, &a, stream);
+  if (a.n_seg == 1) return launch(attn_pp_kernel<D, false, true>, grid, block, &a, stream);
+  return launch(attn_pp_kernel<D, false, false>, grid, block, &a, stream);
 }
 
 }  // namespace
 
 int launch_attention(const AttnArgs& a, void* stream) {
   if (a.n_q <= 0) return 0;
-  const dim3 grid((a.n_q + kBM - 1) / kBM, a.H);
-  return a.D == 64 ? launch_attention_d<64>(a, grid, stream) : launch_attention_d<128>(a, grid, stream);
+  return a.D == 64 ? launch_attention_d<64>(a, stream) : launch_attention_d<128>(a, stream);
 }
 
 int launch_copy_chunks(const CopyArgs& a, void* stream) {
