@@ -326,13 +326,31 @@ __device__ __forceinline__ void pp_store(SwzStage<D>& st, const PPRegs<D>& r) {
   }
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  Give XCD x a contiguous range of (head, query-tile)
+// units, head-major, so the query tiles that share a head's K/V run on the
+// same XCD at the same time and fetch each K/V tile from memory once.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
+  const int nq = gridDim.x;
+  const int total = nq * gridDim.y;
+  const int lin = blockIdx.y * nq + blockIdx.x;
+  const int xcd = lin % kXcds;
+  const int slot = lin / kXcds;
+  const int per = total / kXcds, extra = total % kXcds;  // XCDs < extra get per + 1
+  const int unit = xcd * per + min(xcd, extra) + slot;
+  head = unit / nq;
+  qtile = unit % nq;
+}
+
 template <int D, bool kQ8, bool kOneRun>
 __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   using S = SwzStage<D>;
   constexpr int kLoads = 16 / S::kRowsPerLoad;  // DMA loads per wave per tile side
   __shared__ __attribute__((aligned(16))) S stage[kPPStages];
 
-  const int head = blockIdx.y;
+  int head, qtile;
+  xcd_unit(head, qtile);
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // group's branches and the buffer descriptors scalar
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int wq = wave & 3;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  const int qi = blockIdx.x * kPPBM + wave * 32 + r32;
+  const int qi = qtile * kPPBM + wave * 32 + r32;
   const bool q_ok = qi < a.n_q;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
@@ -444,13 +462,6 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     // ---------------- M(t): MFMA phase ----------------
     __builtin_amdgcn_s_setprio(1);
     bool issued = false;
-    if constexpr (!kQ8) {
-      if (group == 1 && t + 1 < n) {  // V(t+1) straight into LDS
-        dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
-        ld.advance(a, head);
-        issued = true;
-      }
-    }
     if (t < n) {
       const char* kt = reinterpret_cast<const char*>(stage[t % kPPStages].k);
 #pragma unroll
@@ -478,6 +489,14 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (!kQ8) {
+      // V(t+1) straight into LDS, issued after this phase's V^T reads: the
+      // compiler waits for every outstanding LDS-DMA load before a transpose
+      // read, so loads issued earlier in the phase would stall it.
+      if (group == 1 && t + 1 < n) {
+        dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
+        ld.advance(a, head);
+        issued = true;
+      }
       // group B: V(t) (issued one M phase ago) must be in LDS before A's M(t+1)
       if (group == 1) {
         if (issued) wait_vmcnt<kLoads>();
