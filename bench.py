@@ -29,9 +29,11 @@ are measured live with HIP events around each attention launch.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,6 +58,8 @@ POOL = 8                      # Q/K/V pool size
 TXT_POOL = 16
 RECACHE_POOL = 8
 CFG_ID = {"switch": 3, "stream": 2}
+KERNEL_SOURCE = os.path.join(ROOT, "sink_short_window_amd", "csrc", "kernels.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_bf16_sink3_win9_hbm_counters.txt")
 
 
 def pool_index(layer, chunk, pass_):
@@ -83,13 +87,13 @@ def recache_index(switch, layer):
 
 
 class Workload:
-    """Pools, caches and the per-chunk step, shared with the full-size test."""
+    """Input pools, the 30-layer cache and the per-chunk step."""
 
-    def __init__(self, workload="switch", kv="bf16", device="cuda", n_chunks=80):
+    def __init__(self, workload="switch", kv="bf16", device="cuda", n_chunks=80, passes=PASSES):
         import torch
         from sink_short_window_amd import ll, synth
         self.torch, self.ll, self.synth = torch, ll, synth
-        self.workload, self.kv = workload, kv
+        self.workload, self.kv, self.passes = workload, kv, passes
         self.cfg_id = CFG_ID[workload] + (10 if kv == "int8" else 0)
         self.device = device
         self.scale = 1.0 / math.sqrt(D)
@@ -152,7 +156,7 @@ class Workload:
         if self.with_text and is_switch(c):
             pk, pv = self.recache_payload(prompt)
             self._timed("recache", lambda: cache.recache(-1, pk, pv, 2 * CT))
-        for p in range(PASSES):
+        for p in range(self.passes):
             for layer in range(L):
                 i = pool_index(layer, c, p)
                 self._timed("attn", lambda: cache.attn(layer, self.q[i], self.k[i], self.v[i],
@@ -167,7 +171,7 @@ class Workload:
                     if capture and (p, layer) in capture:
                         got[(p, layer, "cross")] = self.xout.clone()
         for layer in range(L):
-            i = pool_index(layer, c, PASSES)
+            i = pool_index(layer, c, self.passes)
             self._timed("append", lambda: cache.append_chunk(layer, self.k[i], self.v[i]))
         self.chunk += 1
         return got
@@ -192,7 +196,7 @@ def attn_flops(n_keys):
     return 4.0 * CT * n_keys * D * H
 
 
-def cpu_baseline(k_steps, warmup, budget_s=20.0):
+def cpu_baseline(k_steps, warmup, budget_s=20.0, passes=PASSES):
     """Time the oracle (float64 numpy, as it stands) on a bounded sample of the
     same workload and scale it to latent frames/s.
 
@@ -226,29 +230,76 @@ def cpu_baseline(k_steps, warmup, budget_s=20.0):
     per_call = spent / heads * H             # one full call at a 5-chunk history
     # The oracle masks the whole history, so its cost grows with the chunk
     # index; scale each timed chunk's calls by its history length.
-    total = sum(PASSES * L * per_call * (c + 1) / 5.0 for c in range(warmup, warmup + k_steps))
+    total = sum(passes * L * per_call * (c + 1) / 5.0 for c in range(warmup, warmup + k_steps))
     return {"value": 3.0 * k_steps / total, "unit": "latent frames/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"oracle sink+window attention, {heads} of {H} heads x {CT} queries of one "
                       f"call at chunk 4 (23400-key history, 18720 allowed) in {spent:.1f} s "
-                      f"({per_call:.1f} s per call); extrapolated to {PASSES}x{L} calls per chunk "
+                      f"({per_call:.1f} s per call); extrapolated to {passes}x{L} calls per chunk "
                       f"for chunks {warmup}..{warmup + k_steps - 1} with cost scaled by history "
                       f"length; cross-attention, append and recache not counted"}
+
+
+def kernel_source_digest():
+    """sha256 of the kernel source with comments and whitespace removed, so
+    that the counter record survives edits that cannot change the code."""
+    src = open(KERNEL_SOURCE).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed FETCH_SIZE/WRITE_SIZE
+    record, or None when the kernel source changed since it was taken."""
+    try:
+        rec = dict(line.split(":", 1) for line in open(TRAFFIC_RECORD)
+                   if line.startswith(("kernel_source_sha256:", "traffic_bytes_per_launch:")))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256", "").strip() != kernel_source_digest():
+        return None
+    return int(rec["traffic_bytes_per_launch"].strip())
+
+
+def copy_calibration():
+    """A plain device copy of a known size (2 GiB read + 2 GiB written), run
+    three times: the FETCH_SIZE / WRITE_SIZE counters of its kernel give the
+    factor that turns those counters into bytes on this chip."""
+    import torch
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
+                                           "launches": 3}}))
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=36)
+    ap.add_argument("--steps", type=int, default=76)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", choices=["switch", "stream"], default="switch")
     ap.add_argument("--kv", choices=["bf16", "int8"], default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--passes", type=int, default=PASSES,
+                    help="attention passes per chunk (4 denoising; 5 adds the append pass's own attention)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 2 GiB device copy (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
-              "(each interactive stream is independent; see the sharding notes).", file=sys.stderr)
+              "(each interactive stream is independent and runs on one GPU).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.passes < 1:
+        print("--passes must be >= 1", file=sys.stderr)
         sys.exit(2)
     if args.warmup + args.steps > 80:
         print("warmup + steps must be <= 80 chunks (240 latent frames)", file=sys.stderr)
@@ -256,7 +307,7 @@ def main():
 
     import torch
     torch.cuda.init()
-    wl = Workload(args.workload, args.kv)
+    wl = Workload(args.workload, args.kv, passes=args.passes)
     wl.prepare(range(args.warmup + args.steps))
     for _ in range(args.warmup):
         wl.step()
@@ -309,11 +360,12 @@ def main():
     roofline = None
     if tflops:
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                    "traffic": recorded_traffic() if args.kv == "bf16" else None}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.steps, args.warmup, args.cpu_budget)
+        cpu = cpu_baseline(args.steps, args.warmup, args.cpu_budget, args.passes)
 
     name = {"switch": "30-layer streaming step with prompt switches (KV-recache) and text cross-attention",
             "stream": "30-layer streaming cache step"}[args.workload]
@@ -333,7 +385,7 @@ def main():
         "config": {"workload": name + (" (int8 KV cache)" if args.kv == "int8" else ""),
                    "layers": L, "heads": H, "head_dim": D, "tokens_per_frame": T,
                    "chunk_frames": C, "sink_frames": S, "window_frames": W,
-                   "chunk_tokens": CT, "keys_per_call": keys, "denoise_passes": PASSES,
+                   "chunk_tokens": CT, "keys_per_call": keys, "attention_passes": args.passes,
                    "text_tokens": N_TXT if args.workload == "switch" else 0,
                    "kv_cache": args.kv, "parallelism": "none (1 GPU)"},
         "roofline": roofline,

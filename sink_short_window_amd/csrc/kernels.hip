@@ -12,7 +12,8 @@
 // buffer resource plus a per-lane 32-bit offset, and rows past the run's end
 // read as zero.
 //
-// bf16 kernel, per workgroup: 4 waves x 32 queries of one head.  Per tile:
+// bf16 kernel (attn_pp_kernel), per workgroup: 8 waves x 32 queries of one
+// head.  Per 64-key tile:
 //   S^T[key][q] = K Q^T      bf16 MFMA 32x32x16, A = K rows from LDS, B = the
 //                            wave's Q fragment kept in registers.  Each lane
 //                            owns one query and 16 keys per 32-key block, so
@@ -25,12 +26,13 @@
 //                            accumulators; A = V^T produced from row-major V
 //                            in LDS by the gfx950 transpose read
 //                            (ds_read_b64_tr_b16).
-// K/V tiles are staged through registers into a double-buffered LDS: the next
-// tile's global loads are in flight while the current tile is computed, with
-// one barrier per tile.
-// INT8 runs are converted exactly to bf16 (|q| <= 127) while staged; the K
-// scale multiplies the score and the V scale multiplies P before its bf16
-// cast.  fp32 activations use a plainer kernel with the fp32 MFMA 32x32x2.
+// The two halves of the workgroup alternate between an MFMA phase and a
+// softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
+// direct-to-LDS buffer loads, or, for int8 runs, through registers where they
+// are converted exactly to bf16 (|q| <= 127); the K scale then multiplies the
+// score and the V scale multiplies P before its bf16 cast.
+// fp32 activations use a plainer kernel with the fp32 MFMA 32x32x2.
+
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
