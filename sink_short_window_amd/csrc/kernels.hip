@@ -345,6 +345,56 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
   qtile = unit % nq;
 }
 
+// One MFMA phase of a wave: S(t) = K(t) Q^T (kQK) and O += V(t-1)^T P(t-1)^T
+// (kPV), as 16 + 16 MFMAs 32x32x16.  The operand reads are software
+// pipelined by hand: kAhead LDS reads are in flight ahead of the MFMA that
+// consumes them, and sched_barrier keeps the compiler from regrouping them
+// (left alone it waits for every pair of reads before each pair of MFMAs).
+constexpr int kAhead = 6;
+
+template <int D, bool kQK, bool kPV>
+__device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k_row, int k_x,
+                                           const int (&voff)[2][D / 32], const bf16x8 (&qf)[D / 16],
+                                           const f32x16& cinit, f32x16 (&s)[2], f32x16 (&o)[D / 32],
+                                           const bf16x8 (&pb)[4]) {
+  using S = SwzStage<D>;
+  constexpr int NK = kQK ? D / 8 : 0;          // K operand reads / QK MFMAs
+  constexpr int NV = kPV ? 4 * (D / 32) : 0;   // V^T operand reads / PV MFMAs
+  constexpr int N = NK + NV;
+  static_assert(N >= kAhead, "phase shorter than the read-ahead");
+  // operand i: K rows (j = i/2, 32-key block kb = i%2), then V^T for the
+  // 16-key step and 32-dim block of the PV MFMA
+  auto rd = [&](int i) -> bf16x8 {
+    if (i < NK) {
+      const int j = i >> 1, kb = i & 1;
+      return *reinterpret_cast<const bf16x8*>(kt + k_row + (((2 * j) ^ k_x) << 4) + kb * 32 * S::kRowB);
+    }
+    const int ii = i - NK;
+    const int step = ii / (D / 32), db = ii % (D / 32);
+    const char* base = vt + 16 * step * S::kRowB;
+    const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base + voff[0][db]));
+    const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + voff[1][db]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  bf16x8 rb[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) rb[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < NK) {
+      const int j = i >> 1, kb = i & 1;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i % kAhead], qf[j], j == 0 ? cinit : s[kb], 0, 0, 0);
+    } else {
+      const int ii = i - NK;
+      const int step = ii / (D / 32), db = ii % (D / 32);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i % kAhead], pb[step], o[db], 0, 0, 0);
+    }
+    if (i + kAhead < N) rb[i % kAhead] = rd(i + kAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, bool kQ8, bool kOneRun>
 __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   using S = SwzStage<D>;
@@ -418,7 +468,9 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       voff[aa][db] = v_swz<D>(row, col >> 3) + ((col & 7) << 1);
     }
 
+  // Tiles in the key set; the host never launches an empty one.
   const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a);
+  if (n == 0) return;
   RunCursor cu;  // tile being softmaxed (masking)
   cu.open(a, head, 0);
   RunCursor ld;  // int8 kernel: next tile to stage; bf16: next K tile (group A) / V tile (group B)
@@ -460,170 +512,170 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   if (group == 1) wg_barrier();  // group B runs one interval behind
 
   f32x16 s[2];
-  for (int t = 0; t <= n; ++t) {
-    // ---------------- M(t): MFMA phase ----------------
-    __builtin_amdgcn_s_setprio(1);
-    bool issued = false;
-    if (t < n) {
-      const char* kt = reinterpret_cast<const char*>(stage[t % kPPStages].k);
-#pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_row + (((2 * j) ^ k_x) << 4) + kb * 32 * S::kRowB);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], j == 0 ? cinit : s[kb], 0, 0, 0);
-        }
-      }
-    }
-    if (t >= 1) {
-      const __bf16* vt = stage[(t - 1) % kPPStages].v;
-#pragma unroll
-      for (int step = 0; step < 4; ++step) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const char* base = reinterpret_cast<const char*>(vt) + 16 * step * S::kRowB;
-          const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base + voff[0][db]));
-          const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + voff[1][db]));
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[step], o[db], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if constexpr (!kQ8) {
-      // V(t+1) straight into LDS, issued after this phase's V^T reads: the
-      // compiler waits for every outstanding LDS-DMA load before a transpose
-      // read, so loads issued earlier in the phase would stall it.
-      if (group == 1 && t + 1 < n) {
-        dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
-        ld.advance(a, head);
-        issued = true;
-      }
-      // group B: V(t) (issued one M phase ago) must be in LDS before A's M(t+1)
-      if (group == 1) {
-        if (issued) wait_vmcnt<kLoads>();
-        else wait_vmcnt<0>();
-      }
-    }
-    wg_barrier();
 
-    // ---------------- V(t): softmax phase ----------------
-    if (t < n) {
-      bool k_issued = false;
-      if constexpr (!kQ8) {
-        if (group == 0 && t + 2 < n) {  // K(t+2) straight into LDS
-          dma_rows<D>(ld, false, stage[(t + 2) % kPPStages].k, 16 * wq, lane);
+  // After the MFMA phase t (its transpose reads done; the compiler waits for
+  // every outstanding LDS-DMA load before a transpose read, so loads issued
+  // earlier in the phase would stall it): group B loads V(t+1) straight into
+  // LDS and makes sure V(t), issued one MFMA phase ago, has landed before
+  // group A's MFMA phase t+1.
+  auto after_mfma = [&](int t) {
+    if constexpr (!kQ8) {
+      if (group == 1) {
+        if (t + 1 < n) {
+          dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
           ld.advance(a, head);
-          k_issued = true;
-        }
-      } else {
-        // stage tile t+2 (in registers since V(t-1)) and start loading tile t+3
-        if (t + 2 < n) {
-          pp_store<D>(stage[(t + 2) % kPPStages], regs);
-          if (t + 3 < n) {
-            pp_load<D>(ld, regs);
-            ld.advance(a, head);
-          }
+          wait_vmcnt<kLoads>();
+        } else {
+          wait_vmcnt<0>();
         }
       }
-      const S& st = stage[t % kPPStages];
-      const int valid = min(kBN, cu.len - cu.tile * kBN);
-      cu.advance(a, head);
-      if constexpr (kQ8) {
-        // int8 runs: score = ksc * (q'.k_int); cinit is 0 for this kernel
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const float4 sc = *reinterpret_cast<const float4*>(&st.ksc[kb * 32 + 8 * gq + 4 * half]);
-            s[kb][4 * gq + 0] = fmaf(s[kb][4 * gq + 0], sc.x, -m_run);
-            s[kb][4 * gq + 1] = fmaf(s[kb][4 * gq + 1], sc.y, -m_run);
-            s[kb][4 * gq + 2] = fmaf(s[kb][4 * gq + 2], sc.z, -m_run);
-            s[kb][4 * gq + 3] = fmaf(s[kb][4 * gq + 3], sc.w, -m_run);
-          }
+    }
+  };
+
+  // Softmax phase t: online softmax of S(t) -> P(t).
+  auto softmax_phase = [&](int t) {
+    bool k_issued = false;
+    if constexpr (!kQ8) {
+      if (group == 0 && t + 2 < n) {  // K(t+2) straight into LDS
+        dma_rows<D>(ld, false, stage[(t + 2) % kPPStages].k, 16 * wq, lane);
+        ld.advance(a, head);
+        k_issued = true;
       }
-      if (valid < kBN) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= valid) s[kb][r] = -INFINITY;
-          }
-      }
-      // tile max relative to m_run: four partial maxima, then the other half
-      float mp[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
-      const float mx = swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-      // The first tile sets the reference; later tiles move it only when a
-      // score exceeds it by more than 2^8 (P stays <= 256).
-      if (t == 0 || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2)) {
-        const float sh = t == 0 ? mx : fmaxf(mx, 0.f);
-        if (t != 0) {
-          const float alpha = __builtin_amdgcn_exp2f(-sh);
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-        }
-        m_run += sh;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
-        if constexpr (!kQ8) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
+    } else {
+      // stage tile t+2 (in registers since V(t-1)) and start loading tile t+3
+      if (t + 2 < n) {
+        pp_store<D>(stage[(t + 2) % kPPStages], regs);
+        if (t + 3 < n) {
+          pp_load<D>(ld, regs);
+          ld.advance(a, head);
         }
       }
+    }
+    const S& st = stage[t % kPPStages];
+    const int valid = min(kBN, cu.len - cu.tile * kBN);
+    cu.advance(a, head);
+    if constexpr (kQ8) {
+      // int8 runs: score = ksc * (q'.k_int); cinit is 0 for this kernel
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
-      if constexpr (kQ8) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const float4 sc = *reinterpret_cast<const float4*>(&st.vsc[kb * 32 + 8 * gq + 4 * half]);
-            // row sum uses the unscaled P; the V scale goes into P for PV
-            l_run += (s[kb][4 * gq + 0] + s[kb][4 * gq + 1]) + (s[kb][4 * gq + 2] + s[kb][4 * gq + 3]);
-            s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
-            s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
-          }
-      }
-      float ls[2] = {0.f, 0.f};
-#pragma unroll
-      for (int step = 0; step < 4; ++step) {
-        // P as bf16 pairs (one 32-bit word each) for the PV operand; the row
-        // sum adds exactly these rounded values, two per dot2.
-        u32x4 pw;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x2 f = {s[step >> 1][8 * (step & 1) + 2 * i], s[step >> 1][8 * (step & 1) + 2 * i + 1]};
-          const bf16x2 b = __builtin_convertvector(f, bf16x2);
-          pw[i] = __builtin_bit_cast(unsigned, b);
-          if constexpr (!kQ8) ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 sc = *reinterpret_cast<const float4*>(&st.ksc[kb * 32 + 8 * gq + 4 * half]);
+          s[kb][4 * gq + 0] = fmaf(s[kb][4 * gq + 0], sc.x, -m_run);
+          s[kb][4 * gq + 1] = fmaf(s[kb][4 * gq + 1], sc.y, -m_run);
+          s[kb][4 * gq + 2] = fmaf(s[kb][4 * gq + 2], sc.z, -m_run);
+          s[kb][4 * gq + 3] = fmaf(s[kb][4 * gq + 3], sc.w, -m_run);
         }
-        pb[step] = __builtin_bit_cast(bf16x8, pw);
+    }
+    if (valid < kBN) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= valid) s[kb][r] = -INFINITY;
+        }
+    }
+    // tile max relative to m_run: four partial maxima, then the other half
+    float mp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
+    const float mx = swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    // The first tile sets the reference; later tiles move it only when a
+    // score exceeds it by more than 2^8 (P stays <= 256).
+    if (t == 0 || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2)) {
+      const float sh = t == 0 ? mx : fmaxf(mx, 0.f);
+      if (t != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       }
-      l_run += ls[0] + ls[1];
+      m_run += sh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
       if constexpr (!kQ8) {
-        // group A: K(t+1) (issued one V phase ago) must be in LDS before M(t+1)
-        if (group == 0) {
-          if (k_issued) wait_vmcnt<kLoads>();
-          else wait_vmcnt<0>();
-        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
+    if constexpr (kQ8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 sc = *reinterpret_cast<const float4*>(&st.vsc[kb * 32 + 8 * gq + 4 * half]);
+          // row sum uses the unscaled P; the V scale goes into P for PV
+          l_run += (s[kb][4 * gq + 0] + s[kb][4 * gq + 1]) + (s[kb][4 * gq + 2] + s[kb][4 * gq + 3]);
+          s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
+          s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
+        }
+    }
+    float ls[2] = {0.f, 0.f};
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      // P as bf16 pairs (one 32-bit word each) for the PV operand; the row
+      // sum adds exactly these rounded values, two per dot2.
+      u32x4 pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 f = {s[step >> 1][8 * (step & 1) + 2 * i], s[step >> 1][8 * (step & 1) + 2 * i + 1]};
+        const bf16x2 b = __builtin_convertvector(f, bf16x2);
+        pw[i] = __builtin_bit_cast(unsigned, b);
+        if constexpr (!kQ8) ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+      }
+      pb[step] = __builtin_bit_cast(bf16x8, pw);
+    }
+    l_run += ls[0] + ls[1];
+    if constexpr (!kQ8) {
+      // group A: K(t+1) (issued one softmax phase ago) must be in LDS before M(t+1)
+      if (group == 0) {
+        if (k_issued) wait_vmcnt<kLoads>();
+        else wait_vmcnt<0>();
+      }
+    }
+  };
+
+  auto kt = [&](int t) { return reinterpret_cast<const char*>(stage[t % kPPStages].k); };
+  auto vt = [&](int t) { return reinterpret_cast<const char*>(stage[t % kPPStages].v); };
+
+  // Per key tile t a group runs MFMA phase t (QK of tile t, PV of tile t-1)
+  // and softmax phase t, each closed by a workgroup barrier; the first and
+  // last MFMA phases are peeled so the steady one is one straight-line block.
+  __builtin_amdgcn_s_setprio(1);
+  mfma_phase<D, true, false>(kt(0), vt(0), k_row, k_x, voff, qf, cinit, s, o, pb);
+  __builtin_amdgcn_s_setprio(0);
+  after_mfma(0);
+  wg_barrier();
+  softmax_phase(0);
+  wg_barrier();
+  for (int t = 1; t < n; ++t) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<D, true, true>(kt(t), vt(t - 1), k_row, k_x, voff, qf, cinit, s, o, pb);
+    __builtin_amdgcn_s_setprio(0);
+    after_mfma(t);
+    wg_barrier();
+    softmax_phase(t);
     wg_barrier();
   }
+  __builtin_amdgcn_s_setprio(1);
+  mfma_phase<D, false, true>(kt(n), vt(n - 1), k_row, k_x, voff, qf, cinit, s, o, pb);
+  __builtin_amdgcn_s_setprio(0);
+  after_mfma(n);
+  wg_barrier();
+  wg_barrier();  // the softmax phase n does not exist; keep the two groups' barrier counts equal
   if (group == 0) wg_barrier();
 
   const float l_tot = swap_halves_sum(l_run);
