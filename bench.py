@@ -277,6 +277,38 @@ def copy_calibration():
                                            "launches": 3}}))
 
 
+def gemm_ceiling():
+    """Reference point for the MFMA roofline: the vendor bf16 GEMM (torch.matmul,
+    8192^3) on N(0,1) operands and on all-zero operands.  MI355X holds a lower
+    clock under MFMA load with real data, so the first figure is the practical
+    ceiling a bf16 contraction reaches on this chip."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    res = {}
+    for name in ("normal", "zeros"):
+        if name == "normal":
+            a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        else:
+            a = torch.zeros(n, n, device="cuda", dtype=torch.bfloat16)
+            b = torch.zeros(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del c
+    print(json.dumps({"gemm_ceiling_tflops": res, "shape": [n, n, n], "dtype": "bf16"}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +322,8 @@ def main():
                     help="attention passes per chunk (4 denoising; 5 adds the append pass's own attention)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 2 GiB device copy (HBM counter calibration) and exit")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor bf16 GEMM on random and on zero operands and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
@@ -297,6 +331,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
     if args.passes < 1:
         print("--passes must be >= 1", file=sys.stderr)
