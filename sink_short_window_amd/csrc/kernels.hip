@@ -254,7 +254,9 @@ __device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16
     const int row = row_lo + r0 + lane / S::kGran;
     const int pg = lane % S::kGran;
     const int lg = v_side ? v_swz_gran<D>(row, pg) : k_swz_gran<D>(row, pg);  // XOR: its own inverse
-    const uint32_t voff = uint32_t(row0 + row) * c.rs + uint32_t(lg) * 16;
+    // row stride is a multiple of the (power-of-two) row size, so OR-ing in
+    // the granule offset is exact and keeps the address a 32-bit value
+    const uint32_t voff = (uint32_t(row0 + row) * c.rs) | (uint32_t(lg) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(v_side ? c.rv : c.rk,
                                              (__attribute__((address_space(3))) void*)(tile_base + (row_lo + r0) * D),
                                              16, voff, 0, 0, 0);
@@ -350,7 +352,8 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
 // pipelined by hand: kAhead LDS reads are in flight ahead of the MFMA that
 // consumes them, and sched_barrier keeps the compiler from regrouping them
 // (left alone it waits for every pair of reads before each pair of MFMAs).
-constexpr int kAhead = 6;
+// Five reads ahead measured as fast as six with fewer registers spilled.
+constexpr int kAhead = 5;
 
 template <int D, bool kQK, bool kPV>
 __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k_row, int k_x,
