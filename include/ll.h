@@ -83,8 +83,10 @@ typedef enum { LL_SEG_SINK = 0, LL_SEG_RING = 1 } ll_segment;
  * (BF16, BF16), (BF16, I8).  With kv_dtype I8 the cache stores int8 K/V and an
  * fp32 scale per (token, head): s = max|x|/127 (IEEE fp32 division),
  * q = clamp(round_half_even(x/s), -127, 127), s = 0 and q = 0 for an all-zero
- * vector.  (The paper mentions INT8 only for model weights; this per-token,
- * per-head KV scheme is this library's own variant.)
+ * vector.  (The paper reports INT8 inference without giving a scheme; this
+ * per-token, per-head KV scheme is this library's own.)  With kv_dtype BF16
+ * every sink chunk and ring slot is its own key run: at most 39 of them.  One
+ * chunk of activations ([C_tok][H][D]) must be smaller than 4 GiB.
  */
 typedef struct {
   int32_t num_layers;
@@ -178,13 +180,19 @@ ll_status ll_cache_query(const ll_cache* cache, int32_t layer, int64_t* chunks_a
 /*
  * Where a cached tensor lives inside the device buffer, for snapshots and
  * tests.  For (which, segment) it returns the byte offset (from dev_buf) of
- * logical element [0][0][0] of a [H][rows][cols] view and its element strides;
- * rows = S*T (sink) or R*C_tok (ring; slot s is rows [s*C_tok, (s+1)*C_tok));
- * cols = D for K/V (element type kv_dtype) and 1 for the fp32 scales (I8
- * only).  shape may be NULL.
+ * element [0][0][0][0] of a 4-D view, its element strides and its shape
+ * (shape may be NULL).
+ *   - K, and V of an F32 or I8 cache: [H][rows][cols][1]; rows = S*T (sink)
+ *     or R*C_tok (ring; slot s is rows [s*C_tok, (s+1)*C_tok)); cols = D
+ *     (element type kv_dtype), or 1 for the fp32 scales (I8 only).
+ *   - V of a BF16 cache: [H][tiles][D][64], V transposed in tiles of 64 keys,
+ *     C_tok rounded up to whole tiles per chunk slot (the sink's chunks, then
+ *     the ring's slots), zeros after a chunk's last key.  Key i of slot s is in
+ *     tile s*ceil(C_tok/64) + i/64, column p = i%64 with bits 2 and 3 swapped
+ *     (the key order in which the attention kernel's PV operand wants it).
  */
 ll_status ll_cache_layout(const ll_cache* cache, int32_t layer, int32_t which, int32_t segment,
-                          size_t* byte_offset, int64_t* strides /*[3]*/, int64_t* shape /*[3]*/);
+                          size_t* byte_offset, int64_t* strides /*[4]*/, int64_t* shape /*[4]*/);
 
 /* Static text for a status code. */
 const char* ll_status_str(ll_status status);

@@ -62,6 +62,18 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g) {
   const int64_t lim = std::numeric_limits<int32_t>::max() / 2;
   if (r.ctok > lim || r.rows > lim || r.rows * r.D > lim)
     return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit row indexing");
+  r.vt = r.kv == LL_BF16;
+  r.nslots = r.nsc + r.R;
+  r.tps = int32_t((r.ctok + kVtTileKeys - 1) / kVtTileKeys);
+  r.vt_head_elems = int64_t(r.nslots) * r.tps * kVtTileKeys * r.D;
+  if (r.vt && r.nslots + 1 > kMaxKeyRuns)
+    return fail(LL_ERR_UNSUPPORTED, "a BF16 cache walks each sink chunk and ring slot as its own key run: "
+                                    "sink chunks + ring slots must be <= " + std::to_string(kMaxKeyRuns - 1));
+  if (r.vt && r.vt_head_elems > lim) return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit indexing");
+  // The kernels address a token-major chunk ([ctok][H][D] activations) with
+  // one 32-bit buffer range.
+  if (r.ctok * r.H * r.D * int64_t(dtype_bytes(r.act)) >= (int64_t(1) << 32))
+    return fail(LL_ERR_UNSUPPORTED, "a chunk of activations must be smaller than 4 GiB");
   *g = r;
   return LL_OK;
 }
@@ -69,10 +81,11 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g) {
 Layout make_layout(const Geometry& g) {
   Layout l;
   const size_t kv_bytes = size_t(g.H) * g.rows * g.D * dtype_bytes(g.kv);
+  const size_t v_bytes = g.vt ? size_t(g.H) * size_t(g.vt_head_elems) * dtype_bytes(g.kv) : kv_bytes;
   const size_t sc_bytes = (g.kv == LL_I8) ? size_t(g.H) * g.rows * sizeof(float) : 0;
   size_t off = 0;
   l.k_off = off; off = align256(off + kv_bytes);
-  l.v_off = off; off = align256(off + kv_bytes);
+  l.v_off = off; off = align256(off + v_bytes);
   l.ks_off = off; off = align256(off + sc_bytes);
   l.vs_off = off; off = align256(off + sc_bytes);
   l.layer_bytes = std::max<size_t>(off, 256);
@@ -123,6 +136,11 @@ std::vector<int32_t> CacheState::resident_slots(int layer) const {
   std::sort(slots.begin(), slots.end(),
             [&](int a, int b) { return L.slot_chunk[a] < L.slot_chunk[b]; });
   return slots;
+}
+
+int32_t slot_of_row(const Geometry& g, int64_t row0) {
+  if (row0 < g.sink_rows) return int32_t(row0 / g.ctok);
+  return g.nsc + int32_t((row0 - g.sink_rows) / g.ctok);
 }
 
 int64_t CacheState::sink_valid_rows(int layer) const {

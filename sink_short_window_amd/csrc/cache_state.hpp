@@ -35,12 +35,25 @@ struct Geometry {
   int64_t sink_rows = 0;  // S*T
   int64_t ring_rows = 0;  // R*ctok
   int64_t rows = 0;       // sink_rows + ring_rows, per head
+  // A BF16 cache keeps V transposed in 64-key tiles (the layout the attention
+  // kernel's PV operand wants): per head, nslots chunk slots (sink chunks,
+  // then ring slots) of tps tiles, each tile [D][64] with zero padding after
+  // the chunk's last key.
+  bool vt = false;
+  int32_t tps = 0;            // tiles per chunk slot, ceil(ctok / 64)
+  int32_t nslots = 0;         // nsc + R
+  int64_t vt_head_elems = 0;  // nslots * tps * 64 * D
 };
+
+// Key runs an attention call may walk (sink chunks, ring slots, current chunk).
+constexpr int kMaxKeyRuns = 40;
+constexpr int kVtTileKeys = 64;
 
 ll_status make_geometry(const ll_cache_config* cfg, Geometry* g);
 
 // Byte layout of the device buffer.  Per layer, in order, each region
-// 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype), and with I8
+// 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype; for a BF16
+// cache V is [H][nslots*tps][D][64] instead, see Geometry), and with I8
 // K scales [H][rows], V scales [H][rows] (fp32).  Rows [0, sink_rows) are the
 // sink; ring slot s is rows sink_rows + [s*ctok, (s+1)*ctok).
 struct Layout {
@@ -65,6 +78,9 @@ struct AppendPlan {
   int32_t slot = -1;
   int64_t chunk = 0;
 };
+
+// Chunk slot (sink chunks first, then ring slots) of the chunk stored at row0.
+int32_t slot_of_row(const Geometry& g, int64_t row0);
 
 class CacheState {
  public:

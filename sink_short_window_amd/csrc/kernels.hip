@@ -23,9 +23,11 @@
 //   max grows by more than 2^8 (exact: any reference max works, the bound
 //   keeps P within bf16/fp32 range).
 //   O^T[d][q] += V^T P^T     bf16 MFMA; B = P straight from the S^T
-//                            accumulators; A = V^T produced from row-major V
-//                            in LDS by the gfx950 transpose read
-//                            (ds_read_b64_tr_b16).
+//                            accumulators; A = V^T: for the bf16 cache, whose
+//                            V is stored transposed in 64-key tiles, a plain
+//                            16-byte LDS read; for row-major V (the caller's
+//                            current chunk, text K/V, the int8 cache) the
+//                            gfx950 transpose read (ds_read_b64_tr_b16).
 // The two halves of the workgroup alternate between an MFMA phase and a
 // softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
 // direct-to-LDS buffer loads, or, for int8 runs, through registers where they
@@ -138,11 +140,10 @@ __device__ __forceinline__ int count_tiles(const AttnArgs& a) {
 // K/V tiles live in a 4-stage LDS ring, rows unpadded, with the 16-byte
 // granules of row r XOR-swizzled by (r mod granules-per-row) so the MFMA
 // operand reads of 32 consecutive rows spread over the banks.  bf16 tiles are
-// loaded straight from memory into LDS (buffer_load ... lds): group A loads
-// K(t+2) during its V(t), group B loads V(t+1) during its M(t), and each waits
-// for those loads two barrier intervals later, just before the barrier that
-// precedes their first use.  The int8 kernel stages through registers instead
-// (load tile t+3, convert and store tile t+2 during V(t)).
+// loaded straight from memory into LDS (buffer_load ... lds): at the start of
+// its softmax phase t group A loads K(t+3) and group B V(t+3), three tiles
+// ahead.  The int8 kernel stages through registers instead (load tile t+3,
+// convert and store tile t+2 during V(t)).
 // ---------------------------------------------------------------------------
 constexpr int kPPWaves = 8;
 constexpr int kPPThreads = 64 * kPPWaves;
@@ -207,6 +208,7 @@ struct RunCursor {
   int tile;
   int len;
   int quant;
+  int vt;       // V of this run in transposed 64-key tiles
   uint32_t rs;  // row stride in bytes
   __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
 
@@ -231,7 +233,14 @@ struct RunCursor {
     rs = __builtin_amdgcn_readfirstlane(uint32_t(s.row_stride) * elt);
     const int64_t hoff = int64_t(head) * s.head_stride * elt;
     rk = make_rsrc(uni(static_cast<const char*>(s.k) + hoff), uint32_t(len) * rs);
-    rv = make_rsrc(uni(static_cast<const char*>(s.v) + hoff), uint32_t(len) * rs);
+    vt = __builtin_amdgcn_readfirstlane(s.v_tiled);
+    if (vt) {
+      // whole zero-padded tiles; a tile is 64 rows of the cache's K row size
+      const uint32_t tiles = uint32_t(len + kBN - 1) / kBN;
+      rv = make_rsrc(uni(static_cast<const char*>(s.v) + int64_t(head) * s.v_head_stride * elt), tiles * kBN * rs);
+    } else {
+      rv = make_rsrc(uni(static_cast<const char*>(s.v) + hoff), uint32_t(len) * rs);
+    }
     if (quant) {
       rks = make_rsrc(uni(s.ks + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
       rvs = make_rsrc(uni(s.vs + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
@@ -260,6 +269,26 @@ __device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16
     __builtin_amdgcn_raw_ptr_buffer_load_lds(v_side ? c.rv : c.rk,
                                              (__attribute__((address_space(3))) void*)(tile_base + (row_lo + r0) * D),
                                              16, voff, 0, 0, 0);
+  }
+}
+
+// LDS-DMA load of this wave's quarter of a transposed V tile ([D][64] bf16,
+// 128-byte rows).  LDS granule g of row d holds logical granule
+// g ^ ((d >> 1) & 7), which keeps the PV operand reads (32 rows, one granule
+// each per 16 lanes) free of bank conflicts.
+template <int D>
+__device__ __forceinline__ void dma_vt(const RunCursor& c, __bf16* tile_base, int wq, int lane) {
+  constexpr int kPer = D / 32;  // 1 KB loads per wave: D rows x 128 B over 4 waves
+  const uint32_t tile0 = uint32_t(c.tile) * uint32_t(kBN * D * 2);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ins = wq * kPer + i;
+    const int d = ins * 8 + (lane >> 3);
+    const int lg = (lane & 7) ^ ((d >> 1) & 7);
+    const uint32_t voff = tile0 + uint32_t(d * 128 + lg * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c.rv, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(tile_base) + ins * 1024), 16, voff,
+        0, 0, 0);
   }
 }
 
@@ -355,11 +384,11 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
 // Five reads ahead measured as fast as six with fewer registers spilled.
 constexpr int kAhead = 5;
 
-template <int D, bool kQK, bool kPV>
+template <int D, bool kQK, bool kPV, bool kVT>
 __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k_row, int k_x,
-                                           const int (&voff)[2][D / 32], const bf16x8 (&qf)[D / 16],
-                                           const f32x16& cinit, f32x16 (&s)[2], f32x16 (&o)[D / 32],
-                                           const bf16x8 (&pb)[4]) {
+                                           const int (&voff)[2][D / 32], const int (&vb)[4],
+                                           const bf16x8 (&qf)[D / 16], const f32x16& cinit, f32x16 (&s)[2],
+                                           f32x16 (&o)[D / 32], const bf16x8 (&pb)[4]) {
   using S = SwzStage<D>;
   constexpr int NK = kQK ? D / 8 : 0;          // K operand reads / QK MFMAs
   constexpr int NV = kPV ? 4 * (D / 32) : 0;   // V^T operand reads / PV MFMAs
@@ -374,10 +403,14 @@ __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k
     }
     const int ii = i - NK;
     const int step = ii / (D / 32), db = ii % (D / 32);
-    const char* base = vt + 16 * step * S::kRowB;
-    const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base + voff[0][db]));
-    const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + voff[1][db]));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (kVT) {  // transposed tile: one 16-byte read of row 32*db + r32
+      return *reinterpret_cast<const bf16x8*>(vt + vb[step] + db * 32 * 128);
+    } else {
+      const char* base = vt + 16 * step * S::kRowB;
+      const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base + voff[0][db]));
+      const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + voff[1][db]));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   };
   bf16x8 rb[kAhead];
 #pragma unroll
@@ -470,10 +503,26 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
       voff[aa][db] = v_swz<D>(row, col >> 3) + ((col & 7) << 1);
     }
+  // V^T tiles (128-byte rows, see dma_vt): lane (r32, half) reads row
+  // 32*db + r32 at logical granule 2*step + half, stored at granule
+  // (2*step + half) ^ ((r32 >> 1) & 7).
+  int vb[4];
+  {
+    const int f = (r32 >> 1) & 7;
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+      vb[step] = r32 * 128 + ((((2 * step) ^ (f & 6)) | (half ^ (f & 1))) << 4);
+  }
 
   // Tiles in the key set; the host never launches an empty one.
   const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a);
   if (n == 0) return;
+  // tiles of the leading runs whose V is in transposed tiles
+  int n_vt = 0;
+  if constexpr (!kQ8) {
+    for (int r = 0; r < a.n_seg && a.seg[r].v_tiled; ++r) n_vt += (a.seg[r].len + kBN - 1) / kBN;
+    n_vt = __builtin_amdgcn_readfirstlane(n_vt);
+  }
   RunCursor cu;  // tile being softmaxed (masking)
   cu.open(a, head, 0);
   RunCursor ld;  // int8 kernel: next tile to stage; bf16: next K tile (group A) / V tile (group B)
@@ -496,53 +545,50 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       ld.advance(a, head);
     }
   } else {
-    // group A: K(0), K(1); group B: V(0).  Afterwards A's cursor points at
-    // K(2) and B's at V(1).
-    if (group == 0) {
-      dma_rows<D>(ld, false, stage[0].k, 16 * wq, lane);
-      ld.advance(a, head);
-      if (n > 1) {
-        dma_rows<D>(ld, false, stage[1].k, 16 * wq, lane);
-        ld.advance(a, head);
-      }
-    } else {
-      dma_rows<D>(ld, true, stage[0].v, 16 * wq, lane);
+    // group A loads K(0..2), group B V(0..2); A waits for K(0) (B waits for
+    // V(0) after its first MFMA phase)
+    const int pre = min(n, 3);
+    for (int j = 0; j < pre; ++j) {
+      if (group == 0) dma_rows<D>(ld, false, stage[j].k, 16 * wq, lane);
+      else if (ld.vt) dma_vt<D>(ld, stage[j].v, wq, lane);
+      else dma_rows<D>(ld, true, stage[j].v, 16 * wq, lane);
       ld.advance(a, head);
     }
-    wait_vmcnt<0>();
+    if (group == 0) {
+      if (pre == 3) wait_vmcnt<2 * kLoads>();
+      else if (pre == 2) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+    }
   }
   wg_barrier();
   if (group == 1) wg_barrier();  // group B runs one interval behind
 
   f32x16 s[2];
 
-  // After the MFMA phase t (its transpose reads done; the compiler waits for
-  // every outstanding LDS-DMA load before a transpose read, so loads issued
-  // earlier in the phase would stall it): group B loads V(t+1) straight into
-  // LDS and makes sure V(t), issued one MFMA phase ago, has landed before
-  // group A's MFMA phase t+1.
+  // Each group keeps three tiles of its side (A: K, B: V) in flight, issuing
+  // tile t+3 at the start of its softmax phase t.  Group B makes sure V(t)
+  // has landed at the end of its MFMA phase t, before group A's MFMA phase
+  // t+1 multiplies with it.  (A wave's LDS reads wait behind its own
+  // outstanding LDS-DMA loads, and the compiler puts a full wait before each
+  // transpose read, so loads issued any earlier would only stall the reads.)
   auto after_mfma = [&](int t) {
     if constexpr (!kQ8) {
       if (group == 1) {
-        if (t + 1 < n) {
-          dma_rows<D>(ld, true, stage[(t + 1) % kPPStages].v, 16 * wq, lane);
-          ld.advance(a, head);
-          wait_vmcnt<kLoads>();
-        } else {
-          wait_vmcnt<0>();
-        }
+        if (t + 2 < n) wait_vmcnt<2 * kLoads>();
+        else if (t + 1 < n) wait_vmcnt<kLoads>();
+        else wait_vmcnt<0>();
       }
     }
   };
 
   // Softmax phase t: online softmax of S(t) -> P(t).
   auto softmax_phase = [&](int t) {
-    bool k_issued = false;
     if constexpr (!kQ8) {
-      if (group == 0 && t + 2 < n) {  // K(t+2) straight into LDS
-        dma_rows<D>(ld, false, stage[(t + 2) % kPPStages].k, 16 * wq, lane);
+      if (t + 3 < n) {  // A: K(t+3), B: V(t+3), straight into LDS
+        if (group == 0) dma_rows<D>(ld, false, stage[(t + 3) % kPPStages].k, 16 * wq, lane);
+        else if (ld.vt) dma_vt<D>(ld, stage[(t + 3) % kPPStages].v, wq, lane);
+        else dma_rows<D>(ld, true, stage[(t + 3) % kPPStages].v, 16 * wq, lane);
         ld.advance(a, head);
-        k_issued = true;
       }
     } else {
       // stage tile t+2 (in registers since V(t-1)) and start loading tile t+3
@@ -643,9 +689,10 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     }
     l_run += ls[0] + ls[1];
     if constexpr (!kQ8) {
-      // group A: K(t+1) (issued one softmax phase ago) must be in LDS before M(t+1)
+      // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
       if (group == 0) {
-        if (k_issued) wait_vmcnt<kLoads>();
+        if (t + 3 < n) wait_vmcnt<2 * kLoads>();
+        else if (t + 2 < n) wait_vmcnt<kLoads>();
         else wait_vmcnt<0>();
       }
     }
@@ -658,15 +705,29 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // and softmax phase t, each closed by a workgroup barrier; the first and
   // last MFMA phases are peeled so the steady one is one straight-line block.
   __builtin_amdgcn_s_setprio(1);
-  mfma_phase<D, true, false>(kt(0), vt(0), k_row, k_x, voff, qf, cinit, s, o, pb);
+  mfma_phase<D, true, false, false>(kt(0), vt(0), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(0);
   wg_barrier();
   softmax_phase(0);
   wg_barrier();
-  for (int t = 1; t < n; ++t) {
+  // Runs with transposed V tiles (cache runs) come before the others (the
+  // caller's current chunk), so the steady loop splits in two, each with one
+  // straight-line MFMA phase (one loop holding both variants spills the
+  // accumulators).
+  const int t1 = min(n_vt + 1, n);
+  for (int t = 1; t < t1; ++t) {  // PV of tile t-1 < n_vt: transposed V
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase<D, true, true>(kt(t), vt(t - 1), k_row, k_x, voff, qf, cinit, s, o, pb);
+    mfma_phase<D, true, true, !kQ8>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+    __builtin_amdgcn_s_setprio(0);
+    after_mfma(t);
+    wg_barrier();
+    softmax_phase(t);
+    wg_barrier();
+  }
+  for (int t = t1; t < n; ++t) {  // row-major V: transpose reads
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<D, true, true, false>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -674,7 +735,8 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     wg_barrier();
   }
   __builtin_amdgcn_s_setprio(1);
-  mfma_phase<D, false, true>(kt(n), vt(n - 1), k_row, k_x, voff, qf, cinit, s, o, pb);
+  if (n - 1 < n_vt) mfma_phase<D, false, true, !kQ8>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+  else mfma_phase<D, false, true, false>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(n);
   wg_barrier();
@@ -840,8 +902,10 @@ __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = int64_t(a.ctok) * a.H * vpr;
   if (e >= total) return;
-  const int chunk = blockIdx.y >> 1;
-  const int isv = blockIdx.y & 1;
+  // y = chunk * parts + part; with the transposed V layout this kernel copies K only
+  const int parts = a.vt ? 1 : 2;
+  const int chunk = blockIdx.y / parts;
+  const int isv = blockIdx.y % parts;
   const int z = blockIdx.z;
   const int vec = int(e % vpr);
   const int64_t rh = e / vpr;
@@ -853,6 +917,47 @@ __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
   char* dst = a.dst + int64_t(z) * a.dst_layer_bytes + (isv ? a.v_off : a.k_off) +
               ((int64_t(h) * a.rows + a.dst_row0[chunk] + row) * a.D) * kElt + vec * 16;
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
+// V writer for the transposed tile layout: one workgroup per (head, 64-key
+// tile) of a chunk.  The tile is staged key-major in LDS and written as
+// [D][64] (16 KB contiguous for D = 128), physical column p holding key p with
+// bits 2 and 3 swapped (the key order of the PV operand); keys past the
+// chunk's end are written as zeros.
+template <int D>
+__global__ __launch_bounds__(256) void copy_vt_kernel(CopyArgs a) {
+  constexpr int kG = D / 8;  // 16-byte granules per key row
+  __shared__ __attribute__((aligned(16))) __bf16 t[kBN][D + 8];
+  const int h = blockIdx.x / a.tps;
+  const int tile = blockIdx.x % a.tps;
+  const int chunk = blockIdx.y;
+  const int z = blockIdx.z;
+  const int tid = threadIdx.x;
+  const __bf16* src = static_cast<const __bf16*>(a.src_v) + int64_t(z) * a.src_layer_elems +
+                      int64_t(chunk) * a.ctok * a.H * D + int64_t(h) * D;
+#pragma unroll
+  for (int it = tid; it < kBN * kG; it += 256) {
+    const int key = it / kG, g = it % kG;
+    const int row = tile * kBN + key;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row < a.ctok) w = *reinterpret_cast<const uint4*>(src + int64_t(row) * a.H * D + g * 8);
+    *reinterpret_cast<uint4*>(&t[key][g * 8]) = w;
+  }
+  __syncthreads();
+  __bf16* dst = reinterpret_cast<__bf16*>(a.dst + int64_t(z) * a.dst_layer_bytes + a.v_off) +
+                int64_t(h) * a.vt_head_elems + (int64_t(a.dst_slot[chunk]) * a.tps + tile) * (kBN * D);
+#pragma unroll
+  for (int it = tid; it < D * (kBN / 8); it += 256) {
+    const int d = it / (kBN / 8), p0 = (it % (kBN / 8)) * 8;
+    bf16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j;
+      const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+      o[j] = t[key][d];
+    }
+    *reinterpret_cast<bf16x8*>(dst + d * kBN + p0) = o;
+  }
 }
 
 // INT8 writer: one group of D/8 lanes per (head, row); each lane quantises
@@ -937,9 +1042,13 @@ int launch_copy_chunks(const CopyArgs& a, void* stream) {
   }
   const int elt = a.act == LL_F32 ? 4 : 2;
   const int64_t threads = int64_t(a.ctok) * a.H * (a.D * elt / 16);
-  const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * 2, a.n_layers);
+  const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * (a.vt ? 1 : 2), a.n_layers);
   if (elt == 4) return launch(copy_chunks_kernel<4>, grid, dim3(256), &a, stream);
-  return launch(copy_chunks_kernel<2>, grid, dim3(256), &a, stream);
+  int err = launch(copy_chunks_kernel<2>, grid, dim3(256), &a, stream);
+  if (err != 0 || !a.vt) return err;
+  const dim3 vgrid(unsigned(a.H * a.tps), a.n_chunks, a.n_layers);
+  return a.D == 64 ? launch(copy_vt_kernel<64>, vgrid, dim3(256), &a, stream)
+                   : launch(copy_vt_kernel<128>, vgrid, dim3(256), &a, stream);
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }

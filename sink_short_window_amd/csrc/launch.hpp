@@ -9,8 +9,12 @@
 namespace ll {
 
 // One contiguous run of keys, addressed in place.  Element (head h, key i of
-// the run, dim d) of K lives at k + (h*head_stride + i*row_stride + d) elements
-// (and likewise V).  For int8 runs, its scale is at ks[h*sc_head_stride + i].
+// the run, dim d) of K lives at k + (h*head_stride + i*row_stride + d)
+// elements, and likewise V unless v_tiled.  A v_tiled run (bf16 cache) keeps
+// V transposed in 64-key tiles: element (h, i, d) at
+// v + h*v_head_stride + (i/64)*64*D + d*64 + p, where p is i%64 with bits 2
+// and 3 swapped (the key order of the PV operand).  For int8 runs, the scale
+// of key i is at ks[h*sc_head_stride + i].
 struct KvSeg {
   const void* k;
   const void* v;
@@ -19,13 +23,14 @@ struct KvSeg {
   int64_t head_stride;     // elements
   int64_t row_stride;      // elements
   int64_t sc_head_stride;  // floats
+  int64_t v_head_stride;   // elements, v_tiled runs
   int32_t key_start;       // first key index of the run in the joint key space
   int32_t len;             // keys in the run
   int32_t quant;           // 1: int8 with scales, 0: activation dtype
-  int32_t pad_;
+  int32_t v_tiled;         // 1: V in transposed 64-key tiles (see above)
 };
 
-constexpr int kMaxSeg = LL_MAX_RING_SLOTS + 2;
+constexpr int kMaxSeg = 40;
 
 struct AttnArgs {
   KvSeg seg[kMaxSeg];
@@ -45,7 +50,9 @@ struct AttnArgs {
 // Copy (or quantise) whole chunks of token-major K/V into cache rows.
 // Source chunk i of layer z is src + (z*src_layer_stride + i*ctok*H*D) elements
 // (token-major [ctok][H][D]); it goes to rows dst_row0[i] .. + ctok of every
-// head in the destination layer z (cache base + z*dst_layer_bytes).
+// head in the destination layer z (cache base + z*dst_layer_bytes).  With vt,
+// V goes instead to chunk slot dst_slot[i] of the transposed tile layout
+// (tps tiles of [D][64] per slot, vt_head_elems per head, zero padding).
 constexpr int kMaxCopyChunks = LL_MAX_RING_SLOTS + 1;
 struct CopyArgs {
   const void* src_k = nullptr;
@@ -58,6 +65,10 @@ struct CopyArgs {
   int32_t n_chunks = 0;
   int32_t n_layers = 1;
   int32_t dst_row0[kMaxCopyChunks];
+  int32_t dst_slot[kMaxCopyChunks];
+  int32_t vt = 0;
+  int32_t tps = 0;
+  int64_t vt_head_elems = 0;
   int32_t ctok = 0;
   int32_t H = 0;
   int32_t D = 0;

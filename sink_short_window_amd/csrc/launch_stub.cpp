@@ -48,13 +48,14 @@ int llh_attn_calls(void) { return ll::g_attn_calls; }
 int llh_copy_calls(void) { return ll::g_copy_calls; }
 
 // Last attention launch: n_seg, n_keys, and per run [k, v, head_stride,
-// row_stride, key_start, len, quant] (pointers as integers).
-int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][7] */) {
+// row_stride, key_start, len, quant, v_head_stride, v_tiled] (pointers as
+// integers).
+int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][9] */) {
   const ll::AttnArgs& a = ll::g_attn;
   *n_keys = a.n_keys;
   for (int i = 0; i < a.n_seg; ++i) {
     const ll::KvSeg& s = a.seg[i];
-    int64_t* r = runs + 7 * i;
+    int64_t* r = runs + 9 * i;
     r[0] = int64_t(reinterpret_cast<intptr_t>(s.k));
     r[1] = int64_t(reinterpret_cast<intptr_t>(s.v));
     r[2] = s.head_stride;
@@ -62,6 +63,8 @@ int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][7] */) {
     r[4] = s.key_start;
     r[5] = s.len;
     r[6] = s.quant;
+    r[7] = s.v_head_stride;
+    r[8] = s.v_tiled;
   }
   return a.n_seg;
 }
@@ -72,6 +75,15 @@ int llh_last_copy(int32_t* n_layers, int32_t* dst_row0 /* [n_chunks] */) {
   *n_layers = c.n_layers;
   for (int i = 0; i < c.n_chunks; ++i) dst_row0[i] = c.dst_row0[i];
   return c.n_chunks;
+}
+
+// Last copy launch, transposed-V part: returns vt; dst_slot receives the
+// chunk slot of each chunk, tps the tiles per slot.
+int llh_last_copy_vt(int32_t* tps, int32_t* dst_slot /* [n_chunks] */) {
+  const ll::CopyArgs& c = ll::g_copy;
+  *tps = c.tps;
+  for (int i = 0; i < c.n_chunks; ++i) dst_slot[i] = c.dst_slot[i];
+  return c.vt;
 }
 
 }  // extern "C"

@@ -14,6 +14,8 @@
 
 using ll::fail;
 
+static_assert(ll::kMaxSeg == ll::kMaxKeyRuns, "run table size");
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -132,18 +134,38 @@ ll_status ll_cache_layout(const ll_cache* cache, int32_t layer, int32_t which, i
   size_t base = lay.layer_bytes * size_t(layer);
   size_t region = which == LL_WHICH_K ? lay.k_off : which == LL_WHICH_V ? lay.v_off
                 : which == LL_WHICH_KSCALE ? lay.ks_off : lay.vs_off;
-  const int64_t cols = scale ? 1 : g.D;
   const size_t elt = scale ? sizeof(float) : ll::dtype_bytes(g.kv);
+  if (which == LL_WHICH_V && g.vt) {
+    // [H][tiles][D][64]: the segment's chunk slots, tps tiles each
+    const int64_t slot0 = segment == LL_SEG_SINK ? 0 : g.nsc;
+    const int64_t nslot = segment == LL_SEG_SINK ? g.nsc : g.R;
+    const int64_t tile = int64_t(ll::kVtTileKeys) * g.D;
+    *byte_offset = base + region + size_t(slot0 * g.tps * tile) * elt;
+    strides[0] = g.vt_head_elems;
+    strides[1] = tile;
+    strides[2] = ll::kVtTileKeys;
+    strides[3] = 1;
+    if (shape) {
+      shape[0] = g.H;
+      shape[1] = nslot * g.tps;
+      shape[2] = g.D;
+      shape[3] = ll::kVtTileKeys;
+    }
+    return LL_OK;
+  }
+  const int64_t cols = scale ? 1 : g.D;
   const int64_t row0 = segment == LL_SEG_SINK ? 0 : g.sink_rows;
   const int64_t nrows = segment == LL_SEG_SINK ? g.sink_rows : g.ring_rows;
   *byte_offset = base + region + size_t(row0 * cols) * elt;
   strides[0] = g.rows * cols;
   strides[1] = cols;
   strides[2] = 1;
+  strides[3] = 1;
   if (shape) {
     shape[0] = g.H;
     shape[1] = nrows;
     shape[2] = cols;
+    shape[3] = 1;
   }
   return LL_OK;
 }
@@ -170,6 +192,10 @@ ll_status ll_cache_append_chunk(ll_cache* cache, int32_t layer, const void* k, c
     a.n_chunks = 1;
     a.n_layers = 1;
     a.dst_row0[0] = int32_t(p.row0);
+    a.dst_slot[0] = ll::slot_of_row(g, p.row0);
+    a.vt = g.vt ? 1 : 0;
+    a.tps = g.tps;
+    a.vt_head_elems = g.vt_head_elems;
     a.ctok = int32_t(g.ctok);
     a.H = g.H; a.D = g.D; a.act = g.act; a.kv = g.kv;
     st = launched(ll::launch_copy_chunks(a, stream), "append launch");
@@ -209,7 +235,13 @@ ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const 
   a.rows = g.rows;
   a.n_chunks = int32_t(slots.size());
   a.n_layers = nl;
-  for (size_t i = 0; i < slots.size(); ++i) a.dst_row0[i] = int32_t(g.sink_rows + slots[i] * g.ctok);
+  for (size_t i = 0; i < slots.size(); ++i) {
+    a.dst_row0[i] = int32_t(g.sink_rows + slots[i] * g.ctok);
+    a.dst_slot[i] = g.nsc + slots[i];
+  }
+  a.vt = g.vt ? 1 : 0;
+  a.tps = g.tps;
+  a.vt_head_elems = g.vt_head_elems;
   a.ctok = int32_t(g.ctok);
   a.H = g.H; a.D = g.D; a.act = g.act; a.kv = g.kv;
   return launched(ll::launch_copy_chunks(a, stream), "recache launch");
@@ -244,19 +276,32 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   auto add_cache_run = [&](int64_t row0, int64_t len) {
     ll::KvSeg& s = a.seg[a.n_seg++];
     s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
-    s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
     s.ks = q8 ? reinterpret_cast<const float*>(base + lay.ks_off) + row0 : nullptr;
     s.vs = q8 ? reinterpret_cast<const float*>(base + lay.vs_off) + row0 : nullptr;
     s.head_stride = g.rows * g.D;
     s.row_stride = g.D;
     s.sc_head_stride = g.rows;
+    if (g.vt) {  // one chunk slot of the transposed tile layout
+      const int64_t slot = ll::slot_of_row(g, row0);
+      s.v = base + lay.v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * kelt;
+      s.v_head_stride = g.vt_head_elems;
+      s.v_tiled = 1;
+    } else {
+      s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
+      s.v_head_stride = 0;
+      s.v_tiled = 0;
+    }
     s.key_start = keys;
     s.len = int32_t(len);
     s.quant = q8 ? 1 : 0;
     keys += int32_t(len);
   };
   const int64_t sink_rows = cs.sink_valid_rows(layer);
-  if (sink_rows > 0) add_cache_run(0, sink_rows);
+  if (g.vt) {  // each sink chunk is its own run (its own slot of V tiles)
+    for (int64_t r0 = 0; r0 < sink_rows; r0 += g.ctok) add_cache_run(r0, g.ctok);
+  } else if (sink_rows > 0) {
+    add_cache_run(0, sink_rows);
+  }
   for (int32_t slot : cs.resident_slots(layer)) add_cache_run(g.sink_rows + int64_t(slot) * g.ctok, g.ctok);
   if (n_cur > 0) {
     ll::KvSeg& s = a.seg[a.n_seg++];
@@ -266,6 +311,8 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
     s.head_stride = g.D;
     s.row_stride = int64_t(g.H) * g.D;
     s.sc_head_stride = 0;
+    s.v_head_stride = 0;
+    s.v_tiled = 0;
     s.key_start = keys;
     s.len = int32_t(n_cur);
     s.quant = 0;
@@ -294,6 +341,8 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (dtype != LL_F32 && dtype != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
   if (n_txt < 1 || n_txt > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_txt must be in [1, 2^30)");
+  if (n_txt * num_heads * int64_t(head_dim) * ll::dtype_bytes(dtype) >= (int64_t(1) << 32))
+    return fail(LL_ERR_UNSUPPORTED, "text K/V must be smaller than 4 GiB each");
   if (n_q < 0 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
   ll_status st;
@@ -310,6 +359,8 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   s.head_stride = head_dim;
   s.row_stride = int64_t(num_heads) * head_dim;
   s.sc_head_stride = 0;
+  s.v_head_stride = 0;
+  s.v_tiled = 0;
   s.key_start = 0;
   s.len = int32_t(n_txt);
   s.quant = 0;

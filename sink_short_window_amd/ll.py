@@ -216,12 +216,21 @@ def ll_cache_query(handle, layer, ring_slots, lib=None):
 
 
 def ll_cache_layout(handle, layer, which, segment, lib=None):
+    """(byte offset, strides[4], shape[4]) of a cached tensor (see ll.h)."""
     lib = lib or load()
     off = _sz()
-    strides = (_i64 * 3)()
-    shape = (_i64 * 3)()
+    strides = (_i64 * 4)()
+    shape = (_i64 * 4)()
     _check(lib, lib.ll_cache_layout(handle, layer, which, segment, ctypes.byref(off), strides, shape))
     return off.value, tuple(strides), tuple(shape)
+
+
+# key held by physical column p of a transposed V tile (bits 2 and 3 of p swapped)
+def vt_column_key(p):
+    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)
+
+
+VT_TILE_KEYS = 64
 
 
 def ll_status_str(status, lib=None):
@@ -279,8 +288,17 @@ class Cache:
     def query(self, layer):
         return ll_cache_query(self.handle, layer, self.ring_slots)
 
+    @property
+    def chunk_tokens(self):
+        return self.cfg.tokens_per_frame * self.cfg.frames_per_chunk
+
+    def v_tiled(self):
+        """True when V is stored transposed in 64-key tiles (BF16 cache)."""
+        return self.cfg.kv_dtype == LL_BF16
+
     def tensor(self, layer, which, segment):
-        """A strided view of a cached tensor inside the device buffer."""
+        """A strided view of a cached tensor inside the device buffer:
+        [H][rows][cols], or [H][tiles][D][64] for the tiled V of a BF16 cache."""
         torch = _torch()
         off, strides, shape = ll_cache_layout(self.handle, layer, which, segment)
         if which in (LL_WHICH_KSCALE, LL_WHICH_VSCALE):
@@ -290,4 +308,32 @@ class Cache:
                        LL_I8: (torch.int8, 1)}[self.cfg.kv_dtype]
         assert off % esz == 0
         flat = self.buf.view(dt) if esz > 1 else self.buf.view(torch.int8)
-        return flat.as_strided(shape, strides, off // esz)
+        view = flat.as_strided(shape, strides, off // esz)
+        return view if (which == LL_WHICH_V and self.v_tiled()) else view[..., 0]
+
+    def rows(self, layer, which, segment):
+        """A cached tensor in logical order [H][rows][cols] (a copy for tiled V):
+        row r of the segment is token r % C_tok of its chunk slot r // C_tok."""
+        torch = _torch()
+        t = self.tensor(layer, which, segment)
+        if not (which == LL_WHICH_V and self.v_tiled()):
+            return t
+        ct = self.chunk_tokens
+        tps = (ct + VT_TILE_KEYS - 1) // VT_TILE_KEYS
+        nslots = t.shape[1] // tps
+        i = torch.arange(ct, device=t.device)
+        col = torch.tensor([vt_column_key(p) for p in range(VT_TILE_KEYS)], device=t.device)
+        tiles = (torch.arange(nslots, device=t.device)[:, None] * tps + (i // VT_TILE_KEYS)[None, :]).reshape(-1)
+        cols = col[i % VT_TILE_KEYS].repeat(nslots)
+        # advanced indices in dims 1 and 3 (separated by a slice) come out first: [R][H][D]
+        return t[:, tiles, :, cols].permute(1, 0, 2)
+
+    def v_padding(self, layer, segment):
+        """The zero padding after each chunk slot's last key in the tiled V."""
+        t = self.tensor(layer, LL_WHICH_V, segment)
+        ct = self.chunk_tokens
+        tps = (ct + VT_TILE_KEYS - 1) // VT_TILE_KEYS
+        last = t[:, tps - 1::tps]
+        keys = [vt_column_key(p) for p in range(VT_TILE_KEYS)]
+        pad_cols = [p for p, k in enumerate(keys) if (tps - 1) * VT_TILE_KEYS + k >= ct]
+        return last[..., pad_cols]

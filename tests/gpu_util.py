@@ -67,7 +67,7 @@ def check_lse(got, want, dtype, what=""):
 
 def cache_rows(cache, layer, which, segment):
     """A cached tensor as a host array [H][rows][cols] (exact values)."""
-    t = cache.tensor(layer, which, segment)
+    t = cache.rows(layer, which, segment)
     return t.cpu().numpy() if t.dtype.is_floating_point is False else host(t)
 
 

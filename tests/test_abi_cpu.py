@@ -32,7 +32,16 @@ def libs():
     ll.bind(stub)
     stub.llh_last_attn.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     stub.llh_last_copy.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    stub.llh_last_copy_vt.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     return stub
+
+
+RUN_FIELDS = 9   # llh_last_attn: k, v, head_stride, row_stride, key_start, len, quant, v_head_stride, v_tiled
+VT_KEYS = 64
+
+
+def tiles_per_slot(ct):
+    return (ct + VT_KEYS - 1) // VT_KEYS
 
 
 def header_functions():
@@ -81,6 +90,7 @@ def status(stub, st):
     (dict(act=ll.LL_F32, kv=ll.LL_BF16), "LL_ERR_UNSUPPORTED"),
     (dict(act=ll.LL_I8, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
     (dict(act=ll.LL_F32, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
+    (dict(C=1, S=10, W=31), "LL_ERR_UNSUPPORTED"),   # bf16: 10 sink chunks + 30 slots + current > 40 runs
 ])
 def test_config_rejected(libs, bad, code):
     n = ctypes.c_size_t(123)
@@ -88,6 +98,13 @@ def test_config_rejected(libs, bad, code):
     assert status(libs, st) == code
     assert libs.ll_last_error()
     assert n.value == 123
+
+
+def test_many_runs_fine_for_int8_cache(libs):
+    """Only the BF16 cache walks each sink chunk as its own run."""
+    n = ctypes.c_size_t(0)
+    assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=10, W=31, kv=ll.LL_I8)), ctypes.byref(n)) == 0
+    assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=9, W=31)), ctypes.byref(n)) == 0
 
 
 def _align(x):
@@ -102,11 +119,16 @@ def test_required_bytes_matches_layout(libs, kw):
                            c.frames_per_chunk, c.sink_frames, c.window_frames)
     rows = S * T + (W - C) // C * C * T
     esz = {ll.LL_F32: 4, ll.LL_BF16: 2, ll.LL_I8: 1}[c.kv_dtype]
-    kvb = _align(H * rows * D * esz)
+    kb = _align(H * rows * D * esz)
+    if c.kv_dtype == ll.LL_BF16:     # V transposed in whole 64-key tiles per chunk slot
+        slots = S // C + (W - C) // C
+        vb = _align(H * slots * tiles_per_slot(C * T) * VT_KEYS * D * esz)
+    else:
+        vb = kb
     scb = _align(H * rows * 4) if c.kv_dtype == ll.LL_I8 else 0
-    assert ll.ll_cache_required_bytes(c, lib=libs) == L * max(2 * kvb + 2 * scb, 256)
-    if kw.get("L") == 30:     # the paper-shaped 30-layer bf16 cache
-        assert ll.ll_cache_required_bytes(c, lib=libs) == 30 * 2 * 12 * 14040 * 128 * 2
+    assert ll.ll_cache_required_bytes(c, lib=libs) == L * max(kb + vb + 2 * scb, 256)
+    if kw.get("L") == 30:     # the paper-shaped 30-layer bf16 cache: 3 slots of 74 tiles for V
+        assert ll.ll_cache_required_bytes(c, lib=libs) == 30 * (12 * 14040 * 128 * 2 + 12 * 3 * 74 * 64 * 128 * 2)
 
 
 def test_create_errors(libs):
@@ -149,6 +171,10 @@ def test_append_state_matches_fifo_model(libs):
                 want = where[1] * g.chunk_tokens if where[0] == "sink" else \
                     g.sink_frames * T + where[1] * g.chunk_tokens
                 assert rows[0] == want
+                tps, slot = ctypes.c_int32(), (ctypes.c_int32 * 40)()
+                assert libs.llh_last_copy_vt(ctypes.byref(tps), slot) == 1      # bf16 cache: tiled V
+                assert tps.value == tiles_per_slot(g.chunk_tokens)
+                assert slot[0] == (where[1] if where[0] == "sink" else g.sink_chunks + where[1])
             qd = query(libs, h, 1, R)
             assert qd["chunks_appended"] == j + 1
             assert qd["slot_chunk"] == sim.slot_chunk
@@ -206,6 +232,9 @@ def test_recache_targets_resident_window_oldest_first(libs):
             assert nl.value == (3 if layer == -1 else 1)
             want = [S * T + sim.slot_chunk.index(ch) * ct for ch in chunks]
             assert list(rows[:k]) == want
+            tps, slot = ctypes.c_int32(), (ctypes.c_int32 * 40)()
+            assert libs.llh_last_copy_vt(ctypes.byref(tps), slot) == 1
+            assert list(slot[:k]) == [g.sink_chunks + sim.slot_chunk.index(ch) for ch in chunks]
     # layers out of step: layer -1 refused
     assert libs.ll_cache_append_chunk(h, 0, FAKE_ACT, FAKE_ACT, None) == 0
     n = len(resident_window_chunks(8, g)) * ct
@@ -230,7 +259,8 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
         H, D = 3, 64
         k_sink_off, st_sink, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
         k_ring_off, st_ring, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_RING)
-        v_sink_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+        v_sink_off, st_v, _ = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+        slot_bytes = tiles_per_slot(ct) * VT_KEYS * D * 2
         for chunk in range(3 * (g.sink_chunks + g.ring_slots) + 3):
             for n_cur in (ct, 0):
                 st = libs.ll_sink_window_attn(h, 1, FAKE_ACT, 5, FAKE_ACT, FAKE_ACT, n_cur, 0.125,
@@ -240,28 +270,30 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
                     continue
                 assert st == 0, libs.ll_last_error()
                 nk = ctypes.c_int64()
-                runs = (ctypes.c_int64 * (7 * 40))()
+                runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
                 n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
                 covered = []
                 start = 0
                 for i in range(n_seg):
-                    kp, vp, hs, rs, ks, ln, q = runs[7 * i:7 * i + 7]
+                    kp, vp, hs, rs, ks, ln, q, vhs, vtl = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
                     assert ks == start and ln > 0 and q == 0
                     start += ln
                     if kp == FAKE_ACT:                 # current chunk, token-major
                         assert i == n_seg - 1 and ln == ct and vp == FAKE_ACT
-                        assert (hs, rs) == (D, H * D)
+                        assert (hs, rs, vtl) == (D, H * D, 0)
                         covered.append(chunk)
                         continue
                     assert (hs, rs) == (st_sink[0], D)
                     row = (kp - FAKE_BUF - k_sink_off) // (2 * D)
-                    assert (vp - FAKE_BUF - v_sink_off) // (2 * D) == row
-                    assert ln % ct == 0
-                    for r0 in range(row, row + ln, ct):
-                        if r0 < S * T:
-                            covered.append(r0 // ct)               # sink chunk index
-                        else:
-                            covered.append(sim.slot_chunk[(r0 - S * T) // ct])
+                    # one chunk slot per run; V in the slot's transposed tiles
+                    assert ln == ct and row % ct == 0 or row >= S * T and (row - S * T) % ct == 0
+                    assert ln == ct and vtl == 1 and vhs == st_v[0]
+                    slot = row // ct if row < S * T else S // C + (row - S * T) // ct
+                    assert vp - FAKE_BUF - v_sink_off == slot * slot_bytes
+                    if row < S * T:
+                        covered.append(row // ct)                  # sink chunk index
+                    else:
+                        covered.append(sim.slot_chunk[(row - S * T) // ct])
                 assert nk.value == start
                 ok = allowed_frames(chunk, frames_per_chunk=C, sink_frames=S, window_frames=W)
                 want = sorted({f // C for f in ok if n_cur or f // C != chunk})
@@ -300,9 +332,9 @@ def test_attention_and_cross_attention_errors(libs):
     assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 0, 64, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
     assert libs.ll_cross_attn(A, 5, A, A, 3, 2, 64, ll.LL_BF16, 0.1, A, A, None) == 0
     nk = ctypes.c_int64()
-    runs = (ctypes.c_int64 * (7 * 40))()
+    runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
     assert libs.llh_last_attn(ctypes.byref(nk), runs) == 1 and nk.value == 3
-    assert tuple(runs[2:4]) == (64, 128)
+    assert tuple(runs[2:4]) == (64, 128) and runs[8] == 0
     libs.ll_cache_destroy(h)
 
 
@@ -313,14 +345,22 @@ def test_layout_queries(libs):
     off_k, st_k, sh_k = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
     off_kr, st_kr, sh_kr = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_RING)
     off_s, st_s, sh_s = _layout(libs, h, 1, ll.LL_WHICH_VSCALE, ll.LL_SEG_RING)
-    assert st_k == (rows * 64, 64, 1) and sh_k == (3, 8, 64)
-    assert sh_kr == (3, 16, 64) and off_kr == off_k + 8 * 64
-    assert st_s == (rows, 1, 1) and sh_s == (3, 16, 1)
+    assert st_k == (rows * 64, 64, 1, 1) and sh_k == (3, 8, 64, 1)
+    assert sh_kr == (3, 16, 64, 1) and off_kr == off_k + 8 * 64
+    off_v, st_v, sh_v = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+    assert st_v == st_k and sh_v == sh_k                       # int8 V: rows, like K
+    assert st_s == (rows, 1, 1, 1) and sh_s == (3, 16, 1, 1)
     assert off_k % 256 == 0
     assert status(libs, libs.ll_cache_layout(h, 0, 9, 0, ctypes.byref(ctypes.c_size_t()),
-                                             (ctypes.c_int64 * 3)(), None)) == "LL_ERR_INVALID_ARG"
-    h2 = create(libs, cfg())
+                                             (ctypes.c_int64 * 4)(), None)) == "LL_ERR_INVALID_ARG"
+    h2 = create(libs, cfg(T=40, C=2, S=2, W=6, H=3, D=64))   # bf16: chunk of 80 keys = 2 tiles
     with pytest.raises(ll.LLError):
         _layout(libs, h2, 0, ll.LL_WHICH_KSCALE, ll.LL_SEG_SINK)
+    vhe = 3 * 2 * 64 * 64                                      # 3 slots x 2 tiles x [64][64]
+    off_vs, st_vs, sh_vs = _layout(libs, h2, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+    off_vr, st_vr, sh_vr = _layout(libs, h2, 1, ll.LL_WHICH_V, ll.LL_SEG_RING)
+    assert st_vs == st_vr == (vhe, 64 * 64, 64, 1)
+    assert sh_vs == (3, 2, 64, 64) and sh_vr == (3, 4, 64, 64)
+    assert off_vr == off_vs + 2 * 64 * 64 * 2 and off_vs % 256 == 0
     libs.ll_cache_destroy(h)
     libs.ll_cache_destroy(h2)

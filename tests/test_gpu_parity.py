@@ -41,7 +41,9 @@ def _check_cache_bytes(cache, layer, g, sim, payloads, dtype, int8):
         segs.append((ll.LL_SEG_RING, list(sim.slot_chunk)))
     for which, tensor_payloads in ((ll.LL_WHICH_K, payloads[0]), (ll.LL_WHICH_V, payloads[1])):
         for seg, chunks in segs:
-            got = cache.tensor(layer, which, seg)
+            got = cache.rows(layer, which, seg)
+            if which == ll.LL_WHICH_V and cache.v_tiled():
+                _check_v_padding(cache, layer, seg, chunks)
             for i, j in enumerate(chunks):
                 if j < 0:
                     continue
@@ -61,6 +63,14 @@ def _check_cache_bytes(cache, layer, g, sim, payloads, dtype, int8):
                 else:
                     gf = got[:, rows, :].cpu().numpy()
                     assert np.array_equal(gf.view(np.uint32), x.astype(np.float32).view(np.uint32))
+
+
+def _check_v_padding(cache, layer, seg, chunks):
+    """The transposed V tiles hold exact zeros after each stored chunk's last key."""
+    pad = cache.v_padding(layer, seg)                     # [H][slots][D][pad columns]
+    for i, j in enumerate(chunks):
+        if j >= 0 and pad.shape[-1]:
+            assert int(torch.count_nonzero(pad[:, i])) == 0, f"V padding not zero (seg {seg}, slot {i})"
 
 
 def run_stream(cfg_id, T, C, S, W, H, D, dtype, n_chunks, int8=False, check_bytes=True,
@@ -139,6 +149,12 @@ def test_bf16_max_ring_slots():
     run_stream(113, 8, 1, 1, 31, 2, 128, "bf16", 34, check_bytes=False)
 
 
+def test_bf16_max_key_runs():
+    """8 sink chunks + 30 ring slots + the current chunk: 39 key runs, the
+    most a BF16 cache walks (each sink chunk is a run of its own)."""
+    run_stream(114, 8, 1, 8, 31, 2, 64, "bf16", 40, check_bytes=False)
+
+
 def test_int8_stream_bitexact_and_parity():
     """INT8 KV: codes and scales bit-exact vs the oracle quantiser; attention
     vs the oracle on the identically dequantised values."""
@@ -181,10 +197,12 @@ def test_config1_snapshot_sampled():
     check_out(out[rows], want, "bf16", "config1 sampled rows")
     check_lse(lse[:, rows], wlse, "bf16", "config1 sampled rows")
     assert torch.isfinite(out.float()).all()
+    _check_v_padding(cache, 0, ll.LL_SEG_SINK, [0])
+    _check_v_padding(cache, 0, ll.LL_SEG_RING, [3, 2])
     # cache bytes: sink = chunk 0, slot 0 = chunk 3, slot 1 = chunk 2
     for which, src in ((ll.LL_WHICH_K, ks), (ll.LL_WHICH_V, vs)):
-        sink = cache.tensor(0, which, ll.LL_SEG_SINK).contiguous().view(torch.int16).cpu().numpy()
-        ring = cache.tensor(0, which, ll.LL_SEG_RING).contiguous().view(torch.int16).cpu().numpy()
+        sink = cache.rows(0, which, ll.LL_SEG_SINK).contiguous().view(torch.int16).cpu().numpy()
+        ring = cache.rows(0, which, ll.LL_SEG_RING).contiguous().view(torch.int16).cpu().numpy()
         assert np.array_equal(sink.view(np.uint16), synth.bf16_bits(src[0].transpose(1, 0, 2)))
         want_ring = np.concatenate([src[3], src[2]]).transpose(1, 0, 2)
         assert np.array_equal(ring.view(np.uint16), synth.bf16_bits(want_ring))
@@ -226,7 +244,7 @@ def test_recache_all_layers_and_order_invariance():
             # bytes: oldest resident chunk's slot holds the payload's first chunk
             sim = sims[layer]
             for which, p in ((ll.LL_WHICH_K, pk[layer]), (ll.LL_WHICH_V, pv[layer])):
-                ring = cache.tensor(layer, which, ll.LL_SEG_RING)
+                ring = cache.rows(layer, which, ll.LL_SEG_RING)
                 for i, ch in enumerate(sim.resident_ring_chunks()):
                     s = sim.slot_chunk.index(ch)
                     got = ring[:, s * ct:(s + 1) * ct].contiguous().view(torch.int16).cpu().numpy()
