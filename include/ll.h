@@ -151,7 +151,10 @@ ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const 
  *   q, out: [n_q][H][D] act_dtype (n_q >= 0; 0 is a no-op).
  *   scale:  logit scale, finite and > 0 (1/sqrt(D) in a standard DiT).
  *   lse:    nullable float [H][n_q]: natural-log sum of exp(scale * q.k).
- * Accumulation is fp32 (bf16 MFMA products for BF16 activations).
+ * Accumulation is fp32 (bf16 MFMA products for BF16 activations).  The scale
+ * is folded into the queries before their bf16 rounding.  With an I8 cache
+ * each stored code is dequantised inside the kernel to bf16(q * s) (s the
+ * token's fp32 scale); the current chunk is used as given.
  * LL_ERR_BAD_STATE if the key set is empty.
  */
 ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,

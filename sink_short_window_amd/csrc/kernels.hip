@@ -30,9 +30,9 @@
 //                            gfx950 transpose read (ds_read_b64_tr_b16).
 // The two halves of the workgroup alternate between an MFMA phase and a
 // softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
-// direct-to-LDS buffer loads, or, for int8 runs, through registers where they
-// are converted exactly to bf16 (|q| <= 127); the K scale then multiplies the
-// score and the V scale multiplies P before its bf16 cast.
+// direct-to-LDS buffer loads, or, for int8 runs, through registers where
+// each code is dequantised with its token's scale (q * s in fp32, then bf16)
+// before it is written to LDS, so the MFMA and softmax are those of bf16.
 // fp32 activations use a plainer kernel with the fp32 MFMA 32x32x2.
 
 #include <hip/hip_runtime.h>
@@ -91,20 +91,6 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// 8 int8 -> 8 bf16, exact for |q| <= 127.
-__device__ __forceinline__ u32x4 int8x8_to_bf16x8(u32x2 w) {
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t src = i < 2 ? w[0] : w[1];
-    const int sh = (i & 1) * 16;
-    const float f0 = float(int8_t((src >> sh) & 0xff));
-    const float f1 = float(int8_t((src >> (sh + 8)) & 0xff));
-    o[i] = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
-  }
-  return o;
-}
-
 // Walks the tiles of the key runs in order.
 struct TileCursor {
   int run;   // current run
@@ -157,8 +143,6 @@ struct SwzStage {
   static constexpr int kRowsPerLoad = 1024 / kRowB;  // rows one 64-lane 16-byte load covers
   __bf16 k[kBN * D];
   __bf16 v[kBN * D];
-  float ksc[kBN];
-  float vsc[kBN];
 };
 
 // Byte offset of logical granule g of row r inside a swizzled tile.  The two
@@ -292,15 +276,16 @@ __device__ __forceinline__ void dma_vt(const RunCursor& c, __bf16* tile_base, in
   }
 }
 
-// Register staging for the int8 kernel: each thread owns kItems 16-byte
-// (bf16) or 8-byte (int8) vectors of K and of V.
+// Register staging for the int8 kernel: each thread owns kItems 8-element
+// vectors of K and of V (16 bytes of bf16, or 8 bytes of int8 in the low two
+// words plus the row's fp32 scale).
 template <int D>
 struct PPRegs {
   static constexpr int kVec = D / 8;
   static constexpr int kItems = kBN * kVec / kPPThreads;
   u32x4 k[kItems];
   u32x4 v[kItems];
-  float ks, vs;
+  float ks[kItems], vs[kItems];
   bool q8;
 };
 
@@ -320,21 +305,30 @@ __device__ __forceinline__ void pp_load(const RunCursor& c, PPRegs<D>& r) {
       const u32x2 vq = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off + vec * 8, 0, 0);
       r.k[it] = u32x4{kq[0], kq[1], 0, 0};
       r.v[it] = u32x4{vq[0], vq[1], 0, 0};
+      r.ks[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rks, uint32_t(row0 + row) * 4, 0, 0));
+      r.vs[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rvs, uint32_t(row0 + row) * 4, 0, 0));
     } else {
       r.k[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rk, off + vec * 16, 0, 0);
       r.v[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rv, off + vec * 16, 0, 0);
     }
   }
   r.q8 = q8;
-  if (tid < kBN) {
-    if (q8) {
-      r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rks, uint32_t(row0 + tid) * 4, 0, 0));
-      r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rvs, uint32_t(row0 + tid) * 4, 0, 0));
-    } else {
-      r.ks = 1.f;
-      r.vs = 1.f;
-    }
+}
+
+// 8 int8 codes q (two words) -> 8 bf16 of q * s.  Each byte is read as the
+// unsigned u = q + 128 (sign bit flipped), so (u - 128) * s is one fma.
+__device__ __forceinline__ u32x4 int8x8_dequant_bf16x8(u32x2 w, float s) {
+  const float ms = -128.f * s;  // exact: a power-of-two multiple
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = w[h] ^ 0x80808080u;
+    const f32x2 lo = {fmaf(float(u & 0xff), s, ms), fmaf(float((u >> 8) & 0xff), s, ms)};
+    const f32x2 hi = {fmaf(float((u >> 16) & 0xff), s, ms), fmaf(float(u >> 24), s, ms)};
+    o[2 * h] = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, bf16x2));
+    o[2 * h + 1] = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf16x2));
   }
+  return o;
 }
 
 template <int D>
@@ -347,15 +341,11 @@ __device__ __forceinline__ void pp_store(SwzStage<D>& st, const PPRegs<D>& r) {
     const int row = item / R::kVec, vec = item % R::kVec;
     u32x4 kw = r.k[it], vw = r.v[it];
     if (r.q8) {
-      kw = int8x8_to_bf16x8(u32x2{kw[0], kw[1]});
-      vw = int8x8_to_bf16x8(u32x2{vw[0], vw[1]});
+      kw = int8x8_dequant_bf16x8(u32x2{kw[0], kw[1]}, r.ks[it]);
+      vw = int8x8_dequant_bf16x8(u32x2{vw[0], vw[1]}, r.vs[it]);
     }
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.k) + k_swz<D>(row, vec)) = kw;
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.v) + v_swz<D>(row, vec)) = vw;
-  }
-  if (tid < kBN) {
-    st.ksc[tid] = r.ks;
-    st.vsc[tid] = r.vs;
   }
 }
 
@@ -600,22 +590,8 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
         }
       }
     }
-    const S& st = stage[t % kPPStages];
     const int valid = min(kBN, cu.len - cu.tile * kBN);
     cu.advance(a, head);
-    if constexpr (kQ8) {
-      // int8 runs: score = ksc * (q'.k_int); cinit is 0 for this kernel
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 sc = *reinterpret_cast<const float4*>(&st.ksc[kb * 32 + 8 * gq + 4 * half]);
-          s[kb][4 * gq + 0] = fmaf(s[kb][4 * gq + 0], sc.x, -m_run);
-          s[kb][4 * gq + 1] = fmaf(s[kb][4 * gq + 1], sc.y, -m_run);
-          s[kb][4 * gq + 2] = fmaf(s[kb][4 * gq + 2], sc.z, -m_run);
-          s[kb][4 * gq + 3] = fmaf(s[kb][4 * gq + 3], sc.w, -m_run);
-        }
-    }
     if (valid < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -651,27 +627,13 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
-      if constexpr (!kQ8) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
-      }
+      for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
-    if constexpr (kQ8) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 sc = *reinterpret_cast<const float4*>(&st.vsc[kb * 32 + 8 * gq + 4 * half]);
-          // row sum uses the unscaled P; the V scale goes into P for PV
-          l_run += (s[kb][4 * gq + 0] + s[kb][4 * gq + 1]) + (s[kb][4 * gq + 2] + s[kb][4 * gq + 3]);
-          s[kb][4 * gq + 0] *= sc.x; s[kb][4 * gq + 1] *= sc.y;
-          s[kb][4 * gq + 2] *= sc.z; s[kb][4 * gq + 3] *= sc.w;
-        }
-    }
     float ls[2] = {0.f, 0.f};
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
@@ -683,7 +645,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
         const f32x2 f = {s[step >> 1][8 * (step & 1) + 2 * i], s[step >> 1][8 * (step & 1) + 2 * i + 1]};
         const bf16x2 b = __builtin_convertvector(f, bf16x2);
         pw[i] = __builtin_bit_cast(unsigned, b);
-        if constexpr (!kQ8) ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+        ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
       }
       pb[step] = __builtin_bit_cast(bf16x8, pw);
     }
