@@ -40,7 +40,7 @@ def _replay_history(wl, layer, chunk):
     """The layer's history as the oracle defines it, through chunk-1, with the
     recache of chunk ``chunk`` (if it is a switch) applied."""
     g = CacheGeometry(bench.T, bench.C, bench.S, bench.W)
-    hist = LayerHistory(g)
+    hist = LayerHistory(g, int8=wl.kv == "int8")
     for c in range(chunk + 1):
         if bench.is_switch(c):
             i = bench.recache_index(bench.switches_before(c), layer)
@@ -54,14 +54,17 @@ def _replay_history(wl, layer, chunk):
     return hist
 
 
-def test_fullsize_switch_workload_sampled():
-    wl = bench.Workload("switch", "bf16")
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_fullsize_switch_workload_sampled(kv):
+    """bf16 cache, and the int8 cache (the oracle attends over the exactly
+    dequantised stored K/V; the current chunk stays bf16)."""
+    wl = bench.Workload("switch", kv)
     last = max(CHUNKS)
     wl.prepare(range(last + 1))
     got = {}
     for c in range(last + 1):
         cap = {CHUNKS[c]} if c in CHUNKS else None
-        say(f"[fullsize] chunk {c}" + (f" capture {CHUNKS[c]}" if cap else ""))
+        say(f"[fullsize {kv}] chunk {c}" + (f" capture {CHUNKS[c]}" if cap else ""))
         out = wl.step(cap)
         if cap:
             got[c] = out
@@ -77,7 +80,7 @@ def test_fullsize_switch_workload_sampled():
         vc = _pool(wl, (bench.CT, bench.H, bench.D), i, synth.V)
         hist = _replay_history(wl, layer, c)
         hk, hv = hist.keys(kc, vc)
-        say(f"[fullsize] oracle chunk {c} pass {p} layer {layer}: {hk.shape[0]} history keys")
+        say(f"[fullsize {kv}] oracle chunk {c} pass {p} layer {layer}: {hk.shape[0]} history keys")
         want, _ = sink_window_attention(q[rows], hk, hv, c, tokens_per_frame=bench.T,
                                         frames_per_chunk=bench.C, sink_frames=bench.S,
                                         window_frames=bench.W, scale=scale)
