@@ -19,9 +19,9 @@
 //                            owns one query and 16 keys per 32-key block, so
 //                            row max / row sum are lane-local plus one swap
 //                            between the two 32-lane halves.
-//   online softmax in the log2 domain; O is rescaled only when the running
-//   max grows by more than 2^8 (exact: any reference max works, the bound
-//   keeps P within bf16/fp32 range).
+//   online softmax in the log2 domain against a reference that the first
+//   tile sets to its max and that moves only when a tile's P would leave the
+//   safe fp32/bf16 range (exact: any reference gives the same softmax).
 //   O^T[d][q] += V^T P^T     bf16 MFMA; B = P straight from the S^T
 //                            accumulators; A = V^T: for the bf16 cache, whose
 //                            V is stored transposed in 64-key tiles, a plain
@@ -61,7 +61,10 @@ constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleLog2 = 8.0f;   // fp32 kernel: rescale when the max grows by more than 2^8
+// bf16 kernel: a tile's sum of P above this (some score more than ~2^60
+// above the reference, or inf) makes the softmax raise its reference.
+constexpr float kTileSumLimit = 0x1p60f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -601,20 +604,26 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
           if (key >= valid) s[kb][r] = -INFINITY;
         }
     }
-    // tile max relative to m_run: four partial maxima, then the other half
-    float mp[4];
+    // Scores are relative to the reference m_run (cinit).  The first tile
+    // sets the reference to its max.  Later tiles skip the max: P = 2^s is
+    // formed and summed first, and only a tile whose sum leaves the safe range
+    // (a score more than ~2^60 above the reference, or an overflow to inf)
+    // takes the slow path that raises the reference and redoes P.  Any
+    // reference gives the same softmax; the bound keeps P, the row sum and O
+    // finite in fp32 and bf16.
+    auto tile_max = [&]() {
+      float mp[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
+      for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
-    const float mx = swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-    // The first tile sets the reference; later tiles move it only when a
-    // score exceeds it by more than 2^8 (P stays <= 256).
-    if (t == 0 || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2)) {
-      const float sh = t == 0 ? mx : fmaxf(mx, 0.f);
-      if (t != 0) {
+        for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
+      return swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    };
+    // Move the reference up by sh (all lanes; sh = 0 leaves a lane as is).
+    auto shift_reference = [&](float sh, bool rescale) {
+      if (rescale) {
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         l_run *= alpha;
 #pragma unroll
@@ -629,27 +638,33 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
-    }
+    };
+    // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand; the
+    // row sum adds exactly these rounded values, two per dot2.  s is kept.
+    auto form_p = [&]() {
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int step = 0; step < 4; ++step) {
+        u32x4 pw;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
-    float ls[2] = {0.f, 0.f};
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      // P as bf16 pairs (one 32-bit word each) for the PV operand; the row
-      // sum adds exactly these rounded values, two per dot2.
-      u32x4 pw;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 f = {s[step >> 1][8 * (step & 1) + 2 * i], s[step >> 1][8 * (step & 1) + 2 * i + 1]};
-        const bf16x2 b = __builtin_convertvector(f, bf16x2);
-        pw[i] = __builtin_bit_cast(unsigned, b);
-        ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+        for (int i = 0; i < 4; ++i) {
+          const f32x2 f = {__builtin_amdgcn_exp2f(s[step >> 1][8 * (step & 1) + 2 * i]),
+                           __builtin_amdgcn_exp2f(s[step >> 1][8 * (step & 1) + 2 * i + 1])};
+          const bf16x2 b = __builtin_convertvector(f, bf16x2);
+          pw[i] = __builtin_bit_cast(unsigned, b);
+          ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+        }
+        pb[step] = __builtin_bit_cast(bf16x8, pw);
       }
-      pb[step] = __builtin_bit_cast(bf16x8, pw);
+      return ls[0] + ls[1];
+    };
+    if (t == 0) shift_reference(tile_max(), false);
+    float lt = form_p();
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit))) {
+      shift_reference(fmaxf(tile_max(), 0.f), true);
+      lt = form_p();
     }
-    l_run += ls[0] + ls[1];
+    l_run += lt;
     if constexpr (!kQ8) {
       // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
       if (group == 0) {

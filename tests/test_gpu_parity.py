@@ -264,9 +264,12 @@ def test_recache_all_layers_and_order_invariance():
 
 
 @pytest.mark.parametrize("segment", ["sink", "ring_old", "ring_new", "current"])
-def test_planted_key_per_segment(segment):
-    """A key aligned with query i (k = 40 q_i/|q_i|) in each key run in turn:
-    the output row i is that key's value (detects a dropped run)."""
+@pytest.mark.parametrize("strength", [40.0, 300.0])
+def test_planted_key_per_segment(segment, strength):
+    """A key aligned with query i (k = strength * q_i/|q_i|) in each key run
+    in turn: the output row i is that key's value (detects a dropped run).
+    Strength 300 puts the score ~430 (log2 units) above the others, past the
+    fp32 range of 2^s: the softmax must move its reference."""
     T, C, S, W, H, D = 64, 1, 1, 3, 2, 128
     ct = T
     cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
@@ -275,7 +278,7 @@ def test_planted_key_per_segment(segment):
     frame = {"sink": 0, "ring_old": 4, "ring_new": 5, "current": 6}[segment]
     i, j = 9, 17
     q = synth.normal((ct, H, D), "bf16", 140, 0, c_now, 0, Q)
-    plant = 40.0 * q[i] / np.linalg.norm(q[i], axis=-1, keepdims=True)
+    plant = strength * q[i] / np.linalg.norm(q[i], axis=-1, keepdims=True)
     plant = synth.bf16_to_f32(synth.bf16_bits(plant.astype(np.float32)))
     vals = {}
     for c in range(c_now + 1):
@@ -292,8 +295,45 @@ def test_planted_key_per_segment(segment):
     torch.cuda.synchronize()
     got = host(out)[i]
     want = vals[frame][1][j]
-    say(f"[planted {segment}] max diff {np.abs(got - want).max():.3e}")
+    say(f"[planted {segment} {strength}] max diff {np.abs(got - want).max():.3e}")
     assert np.abs(got - want).max() <= 2e-2
+
+
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_extreme_score_ranges(order):
+    """Key magnitudes that grow (or shrink) by 2^6 per chunk: logits from
+    ~1e-2 to ~1e4.  Rising scores overflow 2^s against the first tile's
+    reference several times; falling ones underflow to zero.  The output must
+    still equal the float64 softmax."""
+    T, C, S, W, H, D = 64, 1, 1, 4, 2, 128
+    g = CacheGeometry(T, C, S, W)
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    hist = LayerHistory(g)
+    n = 6
+    factors = [2.0 ** (6 * c - 8) for c in range(n)]
+    if order == "falling":
+        factors = factors[::-1]
+    q = synth.normal((T, H, D), "bf16", 160, 0, n - 1, 0, Q)
+    for c in range(n):
+        k = synth.normal((T, H, D), "bf16", 160, 0, c, 0, K) * np.float32(factors[c])
+        v = synth.normal((T, H, D), "bf16", 160, 0, c, 0, V)
+        if c < n - 1:
+            cache.append_chunk(0, dev(k, "bf16"), dev(v, "bf16"))
+            hist.append(k, v)
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    cache.attn(0, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), 1 / math.sqrt(D), out, lse)
+    torch.cuda.synchronize()
+    hk, hv = hist.keys(k, v)
+    want, wlse = sink_window_attention(q, hk, hv, n - 1, tokens_per_frame=T, frames_per_chunk=C,
+                                       sink_frames=S, window_frames=W, scale=1 / math.sqrt(D))
+    assert torch.isfinite(out.float()).all()
+    check_out(out, want, "bf16", f"extreme scores {order}")
+    # lse reaches ~1e7 here; the scores carry the bf16 rounding of the scaled
+    # queries (relative 2^-9), so compare relative to the size
+    gl = host(lse)
+    assert np.all(np.abs(gl - wlse) <= 1e-2 + 4e-3 * np.abs(wlse))
 
 
 def test_single_query_and_zero_queries():
