@@ -24,6 +24,10 @@ What is computed, and where it is stated:
 * Text cross-attention: the prompt is injected by cross-attention layers that
   alternate with self-attention in each DiT block (same paper, §3.1
   "KV recache").  It is plain unmasked softmax attention to the text K/V.
+* Re-encoding at a KV-recache: at a prompt switch the cache is rebuilt by
+  encoding the frames already generated again, paired with the new prompt
+  (same paper, §3.1 "KV recache"; Fig. 2, right).  The self-attention of that
+  pass is :func:`window_reencode_attention`.
 """
 
 import numpy as np
@@ -117,3 +121,42 @@ def cross_attention(q, k_txt, v_txt, scale, query_block=512):
     """Unmasked softmax attention of the chunk's queries to the prompt's text
     K/V (LongLive paper, §3.1: cross-attention layers inject the prompt)."""
     return masked_attention(q, k_txt, v_txt, None, scale, query_block)
+
+
+def window_reencode_attention(q_win, hist_k, hist_v, window_chunks, *, tokens_per_frame,
+                              frames_per_chunk, sink_frames, window_frames, scale,
+                              query_block=512):
+    """Self-attention of the re-encoding pass of a KV-recache.
+
+    At a prompt switch the resident window chunks ``window_chunks``
+    (j_0 < ... < j_{n-1}, as :func:`oracle.resident_window_chunks` gives them)
+    are encoded again with the new prompt, and their keys/values replace the
+    cached ones (LongLive paper, §3.1 "KV recache"; §3.3: the cache holds the
+    sink and the short window only).  Reading taken here: each chunk j_r is
+    encoded as in generation, under the frame rule of its own chunk
+    (:func:`allowed_frames`), over what the rebuilt cache holds: the sink frames
+    and the frames of the window chunks j_0 .. j_r.  Frames before chunk j_0
+    that are not sink frames have left the cache and take no part, and no
+    chunk sees a later one (causal across chunks, none inside a chunk).
+
+    q_win: [n * C_tok, H, D], chunk j_0's queries first; hist_k/hist_v: the
+    layer's token history (with the recache payload applied), covering at
+    least every frame of chunk j_{n-1}.  Returns (out [n*C_tok, H, D],
+    lse [H, n*C_tok]) in float64.
+    """
+    T, C, S = tokens_per_frame, frames_per_chunk, sink_frames
+    ct = C * T
+    chunks = list(window_chunks)
+    if not chunks or q_win.shape[0] != len(chunks) * ct:
+        raise ValueError("one chunk of queries per window chunk is required")
+    frames = np.arange(hist_k.shape[0]) // T
+    first = chunks[0] * C
+    out = np.empty((q_win.shape[0], q_win.shape[1], hist_v.shape[2]), dtype=np.float64)
+    lse = np.empty((q_win.shape[1], q_win.shape[0]), dtype=np.float64)
+    for r, j in enumerate(chunks):
+        ok = allowed_frames(j, frames_per_chunk=C, sink_frames=S, window_frames=window_frames)
+        ok = [f for f in ok if f < S or f >= first]
+        mask = np.isin(frames, np.asarray(ok, dtype=np.int64))
+        sl = slice(r * ct, (r + 1) * ct)
+        out[sl], lse[:, sl] = masked_attention(q_win[sl], hist_k, hist_v, mask, scale, query_block)
+    return out, lse

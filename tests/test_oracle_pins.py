@@ -17,7 +17,8 @@ from hypothesis import given, settings, strategies as st, HealthCheck
 
 from oracle import (allowed_frames, frame_mask, masked_attention,
                     sink_window_attention, cross_attention, CacheGeometry,
-                    LayerHistory, quantize_int8, dequantize_int8)
+                    LayerHistory, quantize_int8, dequantize_int8,
+                    window_reencode_attention, resident_window_chunks)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "attended_chunks.txt")
 
@@ -413,6 +414,101 @@ def test_empty_key_set_is_rejected():
     with pytest.raises(ValueError):
         masked_attention(np.zeros((1, 1, 2)), np.zeros((3, 1, 2)), np.zeros((3, 1, 2)),
                          np.zeros(3, dtype=bool), 1.0)
+
+
+# --------------------------------------------------------------------------
+# re-encoding attention of a KV-recache
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,C,nsc,R,H,D", [(3, 2, 0, 3, 2, 8), (2, 1, 1, 3, 1, 16),
+                                           (2, 3, 1, 2, 3, 4), (1, 1, 2, 1, 2, 8)])
+def test_reencode_before_eviction_is_block_causal(T, C, nsc, R, H, D):
+    """Right after the window first fills nothing has been evicted, so the
+    re-encoding is chunk-causal attention over every chunk generated: torch
+    SDPA (float64) with a block lower-triangular mask, rows of the window
+    chunks."""
+    S, W = nsc * C, (R + 1) * C
+    g = CacheGeometry(T, C, S, W)
+    ct = C * T
+    n = nsc + R
+    win = resident_window_chunks(n, g)
+    assert win == list(range(nsc, n))
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((n * ct, H, D)) for _ in range(3))
+    chunk_of = np.arange(n * ct) // ct
+    want = _sdpa(q, k, v, chunk_of[None, :] <= chunk_of[:, None], 0.4)
+    got, _ = window_reencode_attention(q[nsc * ct:], k, v, win, tokens_per_frame=T,
+                                       frames_per_chunk=C, sink_frames=S, window_frames=W,
+                                       scale=0.4)
+    np.testing.assert_allclose(got, want[nsc * ct:], rtol=0, atol=1e-12)
+
+
+@settings(max_examples=25, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(geom_strategy)
+def test_reencode_bruteforce_after_eviction(params):
+    """After evictions: a pure-Python FIFO says which chunks the cache holds;
+    window chunk r's queries attend, by chunk index, to the sink chunks and
+    window chunks 0..r (pure-Python softmax loops)."""
+    T, C, nsc, R, H, D, seed = params
+    R = max(R, 1)
+    S, W = nsc * C, (R + 1) * C
+    g = CacheGeometry(T, C, S, W)
+    ct = C * T
+    n = nsc + R + 2
+    rng = np.random.default_rng(seed)
+    _, ks, vs = _draw(rng, n, ct, H, D)
+    fifo = deque(maxlen=R)
+    for j in range(nsc, n):
+        fifo.append(j)
+    win = list(fifo)
+    assert resident_window_chunks(n, g) == win
+    qw = rng.standard_normal((R * ct, H, D))
+    scale = 1.0 / math.sqrt(D)
+    got, got_lse = window_reencode_attention(qw, np.concatenate(ks), np.concatenate(vs), win,
+                                             tokens_per_frame=T, frames_per_chunk=C,
+                                             sink_frames=S, window_frames=W, scale=scale)
+    for r in range(R):
+        seen = list(range(nsc)) + win[:r + 1]
+        for h in range(H):
+            keys = [ks[c][t, h].tolist() for c in seen for t in range(ct)]
+            vals = [vs[c][t, h].tolist() for c in seen for t in range(ct)]
+            for i in range(ct):
+                o, l = _bf_attend(qw[r * ct + i, h].tolist(), keys, vals, scale)
+                np.testing.assert_allclose(got[r * ct + i, h], o, rtol=0, atol=1e-12)
+                assert abs(got_lse[h, r * ct + i] - l) <= 1e-12
+
+
+def test_reencode_closed_form_and_causality():
+    """Q = 0 gives the mean of V over exactly the sink and window chunks 0..r
+    (and lse = log of their count); changing a later window chunk leaves the
+    earlier chunks' outputs alone; changing an evicted chunk changes nothing."""
+    T, C, S, W, H, D = 2, 2, 2, 6, 2, 8        # sink = chunk 0, R = 2 slots
+    g = CacheGeometry(T, C, S, W)
+    ct = C * T
+    n = 6                                       # chunks 0..5; cache: 0 | 4, 5
+    win = resident_window_chunks(n, g)
+    assert win == [4, 5]
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((n * ct, H, D))
+    v = rng.standard_normal((n * ct, H, D))
+    kw = dict(tokens_per_frame=T, frames_per_chunk=C, sink_frames=S, window_frames=W, scale=0.5)
+    got, lse = window_reencode_attention(np.zeros((2 * ct, H, D)), k, v, win, **kw)
+    for r, seen in enumerate(([0, 4], [0, 4, 5])):
+        rows = np.concatenate([np.arange(c * ct, (c + 1) * ct) for c in seen])
+        np.testing.assert_allclose(got[r * ct:(r + 1) * ct],
+                                   np.broadcast_to(v[rows].mean(0), (ct, H, D)), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, r * ct:(r + 1) * ct], math.log(len(rows)), rtol=0, atol=1e-12)
+    q = rng.standard_normal((2 * ct, H, D))
+    base, _ = window_reencode_attention(q, k, v, win, **kw)
+    k2, v2 = k.copy(), v.copy()
+    k2[5 * ct:], v2[5 * ct:] = 3.0, -2.0        # the newest window chunk
+    alt, _ = window_reencode_attention(q, k2, v2, win, **kw)
+    np.testing.assert_array_equal(alt[:ct], base[:ct])
+    assert np.abs(alt[ct:] - base[ct:]).max() > 1e-3
+    k3, v3 = k.copy(), v.copy()
+    k3[ct:4 * ct], v3[ct:4 * ct] = 5.0, 7.0     # evicted chunks 1..3
+    np.testing.assert_array_equal(window_reencode_attention(q, k3, v3, win, **kw)[0], base)
 
 
 # --------------------------------------------------------------------------
