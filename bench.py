@@ -109,12 +109,15 @@ class Workload:
             self.vtxt = [gen((N_TXT, H, D), i, synth.V_TXT) for i in range(TXT_POOL)]
             self.rk = [gen((2 * CT, H, D), i, synth.RK) for i in range(RECACHE_POOL)]
             self.rv = [gen((2 * CT, H, D), i, synth.RV) for i in range(RECACHE_POOL)]
+        # queries of the re-encoding pass after a recache (the 2 window chunks)
+        self.qwin = gen((2 * CT, H, D), POOL, synth.Q)
         self.payload = {}
         kvcode = ll.LL_I8 if kv == "int8" else ll.LL_BF16
         cfg = ll.make_config(L, H, D, T, C, S, W, ll.LL_BF16, kvcode)
         self.cache = ll.Cache(cfg, device)
         self.out = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
         self.xout = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
+        self.xwin = torch.empty((2 * CT, H, D), dtype=torch.bfloat16, device=device)
         self.chunk = 0
         self.timers = None
         self.timed_kinds = ("attn", "cross", "append", "recache")
@@ -177,6 +180,28 @@ class Workload:
             self._timed("append", lambda: cache.append_chunk(layer, self.k[i], self.v[i]))
         self.chunk += 1
         return got
+
+
+def reencode_flops():
+    """Algorithmic flop of one re-encoding call over the 2 resident window
+    chunks: window chunk r's C_tok queries attend sink + chunks 0..r."""
+    return 4.0 * D * H * CT * sum(CT + (r + 1) * CT for r in range((W - C) // C))
+
+
+def time_reencode(wl, reps=3):
+    """Re-encoding attention of every layer on the cache as the timed steps
+    left it (sink + 2 window chunks), HIP events around each launch."""
+    t = wl.torch
+    ms = []
+    for _ in range(reps):
+        for layer in range(L):
+            a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            a.record()
+            wl.cache.reencode_attn(layer, wl.qwin, wl.scale, wl.xwin)
+            b.record()
+            ms.append((a, b))
+    t.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ms) / len(ms)
 
 
 def kernel_stats(timers, kind):
@@ -401,6 +426,13 @@ def main():
         rc_bytes = L * 2 * (2 * CT * H * D) * (2 + elt) + (L * 2 * 2 * CT * H * 4 if args.kv == "int8" else 0)
         extra["recache_ms"] = rc_ms
         extra["recache_GBps"] = rc_bytes / (rc_ms * 1e-3) / 1e9
+
+    # After the timed region: the re-encoding attention of a recache
+    # (window queries over sink + window, causal across chunks).
+    re_ms = time_reencode(wl)
+    extra["reencode_ms_per_call"] = re_ms
+    extra["reencode_flop_per_call"] = reencode_flops()
+    extra["reencode_tflops"] = reencode_flops() / (re_ms * 1e-3) / 1e12
 
     roofline = None
     if tflops:

@@ -162,6 +162,24 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
                               void* out, float* lse, ll_stream_t stream);
 
 /*
+ * Self-attention of the re-encoding pass of a KV-recache (paper §3.1 "KV
+ * recache": at a prompt switch the frames already generated are encoded again
+ * with the new prompt to rebuild the cache; §3.3: the cache holds the sink and
+ * the short window).  Call it after ll_cache_recache has written the new K/V
+ * of layer `layer`.  The queries are the resident window chunks', oldest chunk
+ * first: q, out [n_q][H][D] of act_dtype with n_q = (resident window chunks)
+ * * C_tok.  The queries of window chunk r attend, in one softmax, to the
+ * resident sink tokens and the window chunks 0..r (causal across chunks, no
+ * mask inside a chunk); frames evicted before the switch take no part.
+ *   scale: finite and > 0;  lse: nullable float [H][n_q].
+ * Numerics as ll_sink_window_attn.  LL_ERR_BAD_STATE if no window chunk is
+ * resident; LL_ERR_INVALID_ARG if n_q differs from the resident token count.
+ */
+ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const void* q,
+                                  int64_t n_q, float scale, void* out, float* lse,
+                                  ll_stream_t stream);
+
+/*
  * Text cross-attention (paper §3.1: cross-attention injects the prompt):
  * unmasked softmax attention of q [n_q][H][D] to k_txt, v_txt [n_txt][H][D],
  * all of `dtype` (F32 or BF16); out [n_q][H][D]; lse nullable [H][n_q];

@@ -125,7 +125,7 @@ def cross_attention(q, k_txt, v_txt, scale, query_block=512):
 
 def window_reencode_attention(q_win, hist_k, hist_v, window_chunks, *, tokens_per_frame,
                               frames_per_chunk, sink_frames, window_frames, scale,
-                              query_block=512):
+                              rows=None, query_block=512):
     """Self-attention of the re-encoding pass of a KV-recache.
 
     At a prompt switch the resident window chunks ``window_chunks``
@@ -142,21 +142,25 @@ def window_reencode_attention(q_win, hist_k, hist_v, window_chunks, *, tokens_pe
     q_win: [n * C_tok, H, D], chunk j_0's queries first; hist_k/hist_v: the
     layer's token history (with the recache payload applied), covering at
     least every frame of chunk j_{n-1}.  Returns (out [n*C_tok, H, D],
-    lse [H, n*C_tok]) in float64.
+    lse [H, n*C_tok]) in float64; with ``rows`` (sorted query indices) only
+    those queries are computed and returned, in that order.
     """
     T, C, S = tokens_per_frame, frames_per_chunk, sink_frames
     ct = C * T
     chunks = list(window_chunks)
     if not chunks or q_win.shape[0] != len(chunks) * ct:
         raise ValueError("one chunk of queries per window chunk is required")
+    rows = np.arange(q_win.shape[0]) if rows is None else np.asarray(rows)
     frames = np.arange(hist_k.shape[0]) // T
     first = chunks[0] * C
-    out = np.empty((q_win.shape[0], q_win.shape[1], hist_v.shape[2]), dtype=np.float64)
-    lse = np.empty((q_win.shape[1], q_win.shape[0]), dtype=np.float64)
+    out = np.empty((len(rows), q_win.shape[1], hist_v.shape[2]), dtype=np.float64)
+    lse = np.empty((q_win.shape[1], len(rows)), dtype=np.float64)
     for r, j in enumerate(chunks):
         ok = allowed_frames(j, frames_per_chunk=C, sink_frames=S, window_frames=window_frames)
         ok = [f for f in ok if f < S or f >= first]
         mask = np.isin(frames, np.asarray(ok, dtype=np.int64))
-        sl = slice(r * ct, (r + 1) * ct)
-        out[sl], lse[:, sl] = masked_attention(q_win[sl], hist_k, hist_v, mask, scale, query_block)
+        sel = np.nonzero((rows >= r * ct) & (rows < (r + 1) * ct))[0]
+        if len(sel):
+            out[sel], lse[:, sel] = masked_attention(q_win[rows[sel]], hist_k, hist_v, mask,
+                                                     scale, query_block)
     return out, lse

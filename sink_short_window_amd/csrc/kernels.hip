@@ -107,10 +107,22 @@ struct TileCursor {
   }
 };
 
-__device__ __forceinline__ int count_tiles(const AttnArgs& a) {
+__device__ __forceinline__ int count_tiles(const AttnArgs& a, int n_seg) {
   int n = 0;
-  for (int r = 0; r < a.n_seg; ++r) n += (a.seg[r].len + kBN - 1) / kBN;
+  for (int r = 0; r < n_seg; ++r) n += (a.seg[r].len + kBN - 1) / kBN;
   return n;
+}
+
+// Queries [q0, q_end) of query tile `qtile` (tile height bm) and the number of
+// leading runs they attend.  With chunk-causal queries, chunk r of q_chunk
+// tokens is cut into q_tiles tiles and attends runs [0, n_seg0 + r).
+struct QueryTile {
+  int q0, q_end, n_seg;
+};
+__device__ __forceinline__ QueryTile query_tile(const AttnArgs& a, int qtile, int bm) {
+  if (a.q_chunk == 0) return {qtile * bm, a.n_q, a.n_seg};
+  const int r = qtile / a.q_tiles;
+  return {r * a.q_chunk + (qtile - r * a.q_tiles) * bm, (r + 1) * a.q_chunk, a.n_seg0 + r};
 }
 
 // ---------------------------------------------------------------------------
@@ -440,8 +452,10 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int wq = wave & 3;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  const int qi = qtile * kPPBM + wave * 32 + r32;
-  const bool q_ok = qi < a.n_q;
+  const QueryTile qt = query_tile(a, qtile, kPPBM);
+  const int n_seg = __builtin_amdgcn_readfirstlane(qt.n_seg);
+  const int qi = qt.q0 + wave * 32 + r32;
+  const bool q_ok = qi < qt.q_end;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
 
@@ -508,12 +522,12 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   }
 
   // Tiles in the key set; the host never launches an empty one.
-  const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a);
+  const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a, n_seg);
   if (n == 0) return;
   // tiles of the leading runs whose V is in transposed tiles
   int n_vt = 0;
   if constexpr (!kQ8) {
-    for (int r = 0; r < a.n_seg && a.seg[r].v_tiled; ++r) n_vt += (a.seg[r].len + kBN - 1) / kBN;
+    for (int r = 0; r < n_seg && a.seg[r].v_tiled; ++r) n_vt += (a.seg[r].len + kBN - 1) / kBN;
     n_vt = __builtin_amdgcn_readfirstlane(n_vt);
   }
   RunCursor cu;  // tile being softmaxed (masking)
@@ -757,8 +771,9 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  const int qi = blockIdx.x * kBM + wave * 32 + r32;
-  const bool q_ok = qi < a.n_q;
+  const QueryTile qt = query_tile(a, blockIdx.x, kBM);
+  const int qi = qt.q0 + wave * 32 + r32;
+  const bool q_ok = qi < qt.q_end;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
 
@@ -778,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
   constexpr int kVec = D / 4;
   constexpr int kItems = kBN * kVec / kThreads;
-  const int n_tiles = count_tiles(a);
+  const int n_tiles = count_tiles(a, qt.n_seg);
   TileCursor cu{0, 0};
   for (int g = 0; g < n_tiles; ++g) {
     const KvSeg& sg = a.seg[cu.run];
@@ -990,13 +1005,22 @@ int launch(K kernel, dim3 grid, dim3 block, const void* arg, void* stream) {
                              static_cast<hipStream_t>(stream)));
 }
 
+// Query tiles per head for tile height bm; fills in q_tiles for chunk-causal
+// queries (the host checks that q_chunk divides n_q).
+int query_tiles(AttnArgs& a, int bm) {
+  if (a.q_chunk == 0) return (a.n_q + bm - 1) / bm;
+  a.q_tiles = (a.q_chunk + bm - 1) / bm;
+  return a.n_q / a.q_chunk * a.q_tiles;
+}
+
 template <int D>
-int launch_attention_d(const AttnArgs& a, void* stream) {
+int launch_attention_d(const AttnArgs& args, void* stream) {
+  AttnArgs a = args;
   if (a.act == LL_F32) {
-    const dim3 grid((a.n_q + kBM - 1) / kBM, a.H);
+    const dim3 grid(query_tiles(a, kBM), a.H);
     return launch(attn_f32_kernel<D>, grid, dim3(kThreads), &a, stream);
   }
-  const dim3 grid((a.n_q + kPPBM - 1) / kPPBM, a.H);
+  const dim3 grid(query_tiles(a, kPPBM), a.H);
   const dim3 block(kPPThreads);
   if (a.kv == LL_I8) return launch(attn_pp_kernel<D, true, false>, grid, block, &a, stream);
   if (a.n_seg == 1) return launch(attn_pp_kernel<D, false, true>, grid, block, &a, stream);

@@ -45,6 +45,13 @@ struct AttnArgs {
   int32_t act = LL_BF16;    // dtype of q/out and of non-quantised runs
   int32_t kv = LL_BF16;     // LL_I8 when some runs are int8
   float scale = 1.f;
+  // Chunk-causal queries (re-encoding pass of a KV-recache): with q_chunk > 0
+  // the n_q queries are chunks of q_chunk tokens and chunk r attends only the
+  // first n_seg0 + r runs.  q_tiles (query tiles per chunk) is set by the
+  // launcher for the kernel's tile height.
+  int32_t q_chunk = 0;
+  int32_t n_seg0 = 0;
+  int32_t q_tiles = 0;
 };
 
 // Copy (or quantise) whole chunks of token-major K/V into cache rows.

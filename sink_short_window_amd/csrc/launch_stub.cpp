@@ -69,6 +69,13 @@ int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][9] */) {
   return a.n_seg;
 }
 
+// Last attention launch, chunk-causal fields: returns q_chunk (0 = one key set
+// for all queries); n_seg0 receives the runs the first query chunk attends.
+int llh_last_attn_chunks(int32_t* n_seg0) {
+  *n_seg0 = ll::g_attn.n_seg0;
+  return ll::g_attn.q_chunk;
+}
+
 // Last copy launch: n_chunks, n_layers and the destination row of each chunk.
 int llh_last_copy(int32_t* n_layers, int32_t* dst_row0 /* [n_chunks] */) {
   const ll::CopyArgs& c = ll::g_copy;

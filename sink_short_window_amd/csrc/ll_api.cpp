@@ -42,6 +42,50 @@ ll_status launched(int err, const char* what) {
   return LL_OK;
 }
 
+// Key runs of a layer's cache, in the order the attention kernels walk them:
+// the sink (for a BF16 cache one run per sink chunk, each with its own slot of
+// V tiles; otherwise one run), then the resident ring chunks, oldest first.
+// Appends to a.seg and keys; returns the number of sink runs.
+int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int32_t& keys) {
+  const ll::Geometry& g = cs.geom();
+  const ll::Layout& lay = cs.layout();
+  const char* base = static_cast<const char*>(cs.buffer()) + lay.layer_bytes * size_t(layer);
+  const size_t kelt = ll::dtype_bytes(g.kv);
+  const bool q8 = g.kv == LL_I8;
+  auto add_cache_run = [&](int64_t row0, int64_t len) {
+    ll::KvSeg& s = a.seg[a.n_seg++];
+    s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
+    s.ks = q8 ? reinterpret_cast<const float*>(base + lay.ks_off) + row0 : nullptr;
+    s.vs = q8 ? reinterpret_cast<const float*>(base + lay.vs_off) + row0 : nullptr;
+    s.head_stride = g.rows * g.D;
+    s.row_stride = g.D;
+    s.sc_head_stride = g.rows;
+    if (g.vt) {  // one chunk slot of the transposed tile layout
+      const int64_t slot = ll::slot_of_row(g, row0);
+      s.v = base + lay.v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * kelt;
+      s.v_head_stride = g.vt_head_elems;
+      s.v_tiled = 1;
+    } else {
+      s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
+      s.v_head_stride = 0;
+      s.v_tiled = 0;
+    }
+    s.key_start = keys;
+    s.len = int32_t(len);
+    s.quant = q8 ? 1 : 0;
+    keys += int32_t(len);
+  };
+  const int64_t sink_rows = cs.sink_valid_rows(layer);
+  if (g.vt) {
+    for (int64_t r0 = 0; r0 < sink_rows; r0 += g.ctok) add_cache_run(r0, g.ctok);
+  } else if (sink_rows > 0) {
+    add_cache_run(0, sink_rows);
+  }
+  const int n_sink = a.n_seg;
+  for (int32_t slot : cs.resident_slots(layer)) add_cache_run(g.sink_rows + int64_t(slot) * g.ctok, g.ctok);
+  return n_sink;
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,42 +311,9 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
     if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK)
       return st;
   }
-  const ll::Layout& lay = cs.layout();
-  const char* base = static_cast<const char*>(cs.buffer()) + lay.layer_bytes * size_t(layer);
-  const size_t kelt = ll::dtype_bytes(g.kv);
-  const bool q8 = g.kv == LL_I8;
   ll::AttnArgs a;
   int32_t keys = 0;
-  auto add_cache_run = [&](int64_t row0, int64_t len) {
-    ll::KvSeg& s = a.seg[a.n_seg++];
-    s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
-    s.ks = q8 ? reinterpret_cast<const float*>(base + lay.ks_off) + row0 : nullptr;
-    s.vs = q8 ? reinterpret_cast<const float*>(base + lay.vs_off) + row0 : nullptr;
-    s.head_stride = g.rows * g.D;
-    s.row_stride = g.D;
-    s.sc_head_stride = g.rows;
-    if (g.vt) {  // one chunk slot of the transposed tile layout
-      const int64_t slot = ll::slot_of_row(g, row0);
-      s.v = base + lay.v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * kelt;
-      s.v_head_stride = g.vt_head_elems;
-      s.v_tiled = 1;
-    } else {
-      s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
-      s.v_head_stride = 0;
-      s.v_tiled = 0;
-    }
-    s.key_start = keys;
-    s.len = int32_t(len);
-    s.quant = q8 ? 1 : 0;
-    keys += int32_t(len);
-  };
-  const int64_t sink_rows = cs.sink_valid_rows(layer);
-  if (g.vt) {  // each sink chunk is its own run (its own slot of V tiles)
-    for (int64_t r0 = 0; r0 < sink_rows; r0 += g.ctok) add_cache_run(r0, g.ctok);
-  } else if (sink_rows > 0) {
-    add_cache_run(0, sink_rows);
-  }
-  for (int32_t slot : cs.resident_slots(layer)) add_cache_run(g.sink_rows + int64_t(slot) * g.ctok, g.ctok);
+  add_cache_runs(cs, layer, a, keys);
   if (n_cur > 0) {
     ll::KvSeg& s = a.seg[a.n_seg++];
     s.k = k_cur;
@@ -331,6 +342,41 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   a.kv = g.kv;
   a.scale = scale;
   return launched(ll::launch_attention(a, stream), "attention launch");
+}
+
+ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const void* q,
+                                  int64_t n_q, float scale, void* out, float* lse,
+                                  ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  const int64_t resident = cs.layer(layer).ring_valid;
+  if (resident == 0) return fail(LL_ERR_BAD_STATE, "no window chunk is resident");
+  if (n_q != resident * g.ctok)
+    return fail(LL_ERR_INVALID_ARG, "n_q must be (resident window chunks) * C_tok = " +
+                                        std::to_string(resident * g.ctok));
+  if (n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK) return st;
+  if (lse && !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  ll::AttnArgs a;
+  int32_t keys = 0;
+  const int n_sink = add_cache_runs(cs, layer, a, keys);
+  a.n_keys = keys;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.n_q = int32_t(n_q);
+  a.H = g.H;
+  a.D = g.D;
+  a.act = g.act;
+  a.kv = g.kv;
+  a.scale = scale;
+  a.q_chunk = int32_t(g.ctok);
+  a.n_seg0 = n_sink + 1;
+  return launched(ll::launch_attention(a, stream), "re-encoding attention launch");
 }
 
 ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const void* v_txt,

@@ -25,8 +25,8 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
 
 # Every function include/ll.h declares (checked against the header by the tests).
 EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
-           "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn", "ll_cross_attn",
-           "ll_cache_query", "ll_cache_layout", "ll_status_str", "ll_last_error")
+           "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
+           "ll_window_reencode_attn", "ll_cross_attn", "ll_cache_query", "ll_cache_layout", "ll_status_str", "ll_last_error")
 
 
 class ll_cache_config(ctypes.Structure):
@@ -55,6 +55,7 @@ _SIGS = {
     "ll_cache_append_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "ll_cache_recache": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
     "ll_sink_window_attn": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
+    "ll_window_reencode_attn": (_i32, [_vp, _i32, _vp, _i64, _f32, _vp, _vp, _vp]),
     "ll_cross_attn": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "ll_cache_query": (_i32, [_vp, _i32, _P(_i64), _P(_i32), _P(_i32), _P(_i64)]),
     "ll_cache_layout": (_i32, [_vp, _i32, _i32, _i32, _P(_sz), _P(_i64), _P(_i64)]),
@@ -194,6 +195,16 @@ def ll_sink_window_attn(handle, layer, q, k_cur, v_cur, scale, out, act_dtype, l
         _stream(stream, q)))
 
 
+def ll_window_reencode_attn(handle, layer, q, scale, out, act_dtype, lse=None, stream=None,
+                            lib=None):
+    """q, out: [resident window chunks * C_tok, H, D], oldest chunk first."""
+    lib = lib or load()
+    dt = _ACT[act_dtype]
+    _check(lib, lib.ll_window_reencode_attn(
+        handle, layer, _dev_ptr(q, "q", dt), q.shape[0], float(scale), _dev_ptr(out, "out", dt),
+        _dev_ptr(lse, "lse", "float32", True), _stream(stream, q)))
+
+
 def ll_cross_attn(q, k_txt, v_txt, scale, out, act_dtype, lse=None, stream=None, lib=None):
     """q, out: [n_q, H, D]; k_txt, v_txt: [n_txt, H, D]."""
     lib = lib or load()
@@ -281,6 +292,9 @@ class Cache:
     def attn(self, layer, q, k_cur, v_cur, scale, out, lse=None, stream=None):
         ll_sink_window_attn(self.handle, layer, q, k_cur, v_cur, scale, out, self.cfg.act_dtype,
                             lse, stream)
+
+    def reencode_attn(self, layer, q, scale, out, lse=None, stream=None):
+        ll_window_reencode_attn(self.handle, layer, q, scale, out, self.cfg.act_dtype, lse, stream)
 
     def reset(self):
         ll_cache_reset(self.handle)

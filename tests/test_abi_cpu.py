@@ -33,6 +33,7 @@ def libs():
     stub.llh_last_attn.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     stub.llh_last_copy.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     stub.llh_last_copy_vt.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    stub.llh_last_attn_chunks.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     return stub
 
 
@@ -302,6 +303,63 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
             assert libs.ll_cache_append_chunk(h, 1, FAKE_ACT, FAKE_ACT, None) == 0
             sim.append()
         libs.ll_cache_destroy(h)
+
+
+@pytest.mark.parametrize("T,C,S,W,act,kv", [
+    (4, 2, 2, 6, ll.LL_BF16, ll.LL_BF16), (4, 1, 0, 3, ll.LL_BF16, ll.LL_BF16),
+    (3, 1, 2, 5, ll.LL_BF16, ll.LL_BF16), (4, 2, 2, 8, ll.LL_BF16, ll.LL_I8),
+    (2, 2, 4, 8, ll.LL_F32, ll.LL_F32)])
+def test_reencode_runs_are_sink_then_window_oldest_first(libs, T, C, S, W, act, kv):
+    """The re-encoding call walks the sink, then the resident window chunks
+    oldest first, with the chunk-causal split recorded: window chunk r attends
+    the first n_seg0 + r runs, i.e. exactly the sink chunks and the window
+    chunks 0..r the oracle's reading names."""
+    c = cfg(L=2, T=T, C=C, S=S, W=W, H=3, D=64, act=act, kv=kv)
+    g = CacheGeometry(T, C, S, W)
+    h = create(libs, c)
+    sim = DequeCacheModel(g)
+    ct, D = g.chunk_tokens, 64
+    elt = {ll.LL_BF16: 2, ll.LL_I8: 1, ll.LL_F32: 4}[kv]
+    k_sink_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
+    A = FAKE_ACT
+    for chunk in range(g.sink_chunks + 2 * g.ring_slots + 2):
+        win = resident_window_chunks(chunk, g) if chunk > g.sink_chunks else []
+        n_q = len(win) * ct
+        st = libs.ll_window_reencode_attn(h, 1, A, n_q, 0.125, A, None, None)
+        if not win:
+            assert status(libs, st) == "LL_ERR_BAD_STATE"
+        else:
+            assert st == 0, libs.ll_last_error()
+            nk = ctypes.c_int64()
+            runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+            n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+            n_seg0 = ctypes.c_int32()
+            assert libs.llh_last_attn_chunks(ctypes.byref(n_seg0)) == ct
+            chunks_of_run = []
+            for i in range(n_seg):
+                kp, ln = runs[RUN_FIELDS * i], runs[RUN_FIELDS * i + 5]
+                row = (kp - FAKE_BUF - k_sink_off) // (elt * D)
+                if row < S * T:
+                    chunks_of_run.append(list(range(row // ct, (row + ln) // ct)))
+                else:
+                    assert ln == ct
+                    chunks_of_run.append([sim.slot_chunk[(row - S * T) // ct]])
+            n_sink = n_seg0.value - 1
+            assert n_seg == n_sink + len(win)
+            for r in range(len(win)):
+                seen = [j for run in chunks_of_run[:n_sink + r + 1] for j in run]
+                assert seen == list(range(g.sink_chunks)) + win[:r + 1]
+            bad = libs.ll_window_reencode_attn(h, 1, A, n_q - 1, 0.125, A, None, None)
+            assert status(libs, bad) == "LL_ERR_INVALID_ARG"
+            bad = libs.ll_window_reencode_attn(h, 1, A, n_q, float("inf"), A, None, None)
+            assert status(libs, bad) == "LL_ERR_INVALID_ARG"
+            bad = libs.ll_window_reencode_attn(h, 1, A, n_q, 0.125, A + 2, None, None)
+            assert status(libs, bad) == "LL_ERR_INVALID_ARG"
+            bad = libs.ll_window_reencode_attn(h, 2, A, n_q, 0.125, A, None, None)
+            assert status(libs, bad) == "LL_ERR_INVALID_ARG"
+        assert libs.ll_cache_append_chunk(h, 1, A, A, None) == 0
+        sim.append()
+    libs.ll_cache_destroy(h)
 
 
 def test_attention_and_cross_attention_errors(libs):

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import (CacheGeometry, DequeCacheModel, LayerHistory, sink_window_attention,
+                    window_reencode_attention, resident_window_chunks,
                     masked_attention, cross_attention, quantize_int8)
 from sink_short_window_amd import ll, synth
 from sink_short_window_amd.synth import Q, K, V, K_TXT, V_TXT, RK, RV
@@ -374,3 +375,105 @@ def test_cross_attention(dtype, D, n_q, n_txt):
     check_lse(lse[:, rows], wlse, dtype, "cross")
     if n_txt == 1:
         assert np.abs(host(out) - vt[0][None]).max() <= (1e-6 if dtype == "f32" else 1e-2)
+
+
+# --------------------------------------------------------------------------
+# re-encoding attention after a KV-recache
+# --------------------------------------------------------------------------
+
+def run_reencode(cfg_id, T, C, S, W, H, D, dtype, n_chunks, check_at, int8=False):
+    """Append ``n_chunks`` chunks; after each chunk in ``check_at`` recache the
+    resident window with a fresh payload and run the re-encoding attention of
+    the window chunks through the ABI, against the oracle on the same history
+    (the int8 cache: on the exactly dequantised stored K/V)."""
+    kv = ll.LL_I8 if int8 else act_code(dtype)
+    cfg = ll.make_config(1, H, D, T, C, S, W, act_code(dtype), kv)
+    cache = ll.Cache(cfg)
+    g = CacheGeometry(T, C, S, W)
+    hist = LayerHistory(g, int8=int8)
+    ct = g.chunk_tokens
+    scale = 1.0 / math.sqrt(D)
+    for c in range(n_chunks):
+        k = synth.normal((ct, H, D), dtype, cfg_id, 0, c, 0, K)
+        v = synth.normal((ct, H, D), dtype, cfg_id, 0, c, 0, V)
+        cache.append_chunk(0, dev(k, dtype), dev(v, dtype))
+        hist.append(k, v)
+        if c not in check_at:
+            continue
+        win = resident_window_chunks(c + 1, g)
+        n = len(win) * ct
+        rk = synth.normal((n, H, D), dtype, cfg_id, 1, c, 0, RK)
+        rv = synth.normal((n, H, D), dtype, cfg_id, 1, c, 0, RV)
+        q = synth.normal((n, H, D), dtype, cfg_id, 1, c, 0, Q)
+        say(f"[reencode cfg={cfg_id} T={T} C={C} S={S} W={W} H={H} D={D} {dtype}"
+            f"{' i8' if int8 else ''}] after chunk {c}: window chunks {win}")
+        cache.recache(0, dev(rk, dtype), dev(rv, dtype), n)
+        hist.recache(rk, rv)
+        dq = dev(q, dtype)
+        out = torch.empty_like(dq)
+        lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
+        cache.reencode_attn(0, dq, scale, out, lse)
+        torch.cuda.synchronize()
+        hk, hv = hist.keys()
+        want, wlse = window_reencode_attention(q, hk, hv, win, tokens_per_frame=T,
+                                               frames_per_chunk=C, sink_frames=S,
+                                               window_frames=W, scale=scale)
+        check_out(out, want, dtype, f"re-encode after chunk {c}")
+        check_lse(lse, wlse, dtype, f"re-encode after chunk {c}")
+
+
+def test_reencode_bf16_ragged_partial_and_full_window():
+    """100-token chunks (ragged key and query tiles), sink = 1 chunk, 3 ring
+    slots: a window of 1, 2, then 3 chunks after evictions."""
+    run_reencode(140, 50, 2, 2, 8, 2, 128, "bf16", 7, (1, 2, 5))
+
+
+def test_reencode_bf16_d64_no_sink_two_query_tiles_per_chunk():
+    """No sink; 300-token chunks span two query tiles, the second ragged."""
+    run_reencode(141, 150, 2, 0, 6, 3, 64, "bf16", 5, (0, 1, 4))
+
+
+def test_reencode_bf16_two_sink_chunks():
+    run_reencode(142, 24, 1, 2, 4, 3, 128, "bf16", 7, (2, 6))
+
+
+def test_reencode_int8_cache():
+    run_reencode(143, 50, 2, 2, 6, 2, 128, "bf16", 5, (1, 4), int8=True)
+
+
+def test_reencode_fp32():
+    run_reencode(144, 37, 2, 2, 6, 2, 128, "f32", 5, (1, 4))
+
+
+def test_reencode_config1_sampled():
+    """Full size: 12 heads x 128, 4680-token chunks, sink 1 chunk, 2 ring
+    slots.  Chunks 0..3 appended, the window (chunks 2, 3) recached, then the
+    9360 window queries re-encoded; sampled rows of both chunks vs the oracle."""
+    T, C, S, W, H, D = 1560, 3, 3, 9, 12, 128
+    g = CacheGeometry(T, C, S, W)
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    hist = LayerHistory(g)
+    for c in range(4):
+        k, v = _config1_inputs(c, K), _config1_inputs(c, V)
+        cache.append_chunk(0, dev(k, "bf16"), dev(v, "bf16"))
+        hist.append(k, v)
+    win = resident_window_chunks(4, g)
+    assert win == [2, 3]
+    pay = [synth.normal((9360, H, D), "bf16", 1, 1, 4, 0, t) for t in (RK, RV, Q)]
+    cache.recache(0, dev(pay[0], "bf16"), dev(pay[1], "bf16"), 9360)
+    hist.recache(pay[0], pay[1])
+    out = torch.empty((9360, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, 9360), dtype=torch.float32, device="cuda")
+    say("[reencode config1] 9360 window queries over sink + window (9360 / 14040 keys)")
+    cache.reencode_attn(0, dev(pay[2], "bf16"), 1 / math.sqrt(D), out, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 255, 256, 4607, 4608, 4679, 4680, 4681, 4935, 4936,
+                                      9287, 9288, 9359], rng.choice(9360, 120, replace=False)]))
+    hk, hv = hist.keys()
+    want, wlse = window_reencode_attention(pay[2], hk, hv, win, tokens_per_frame=T,
+                                           frames_per_chunk=C, sink_frames=S, window_frames=W,
+                                           scale=1 / math.sqrt(D), rows=rows)
+    check_out(out[rows], want, "bf16", "config1 re-encode sampled rows")
+    check_lse(lse[:, rows], wlse, "bf16", "config1 re-encode sampled rows")
