@@ -477,3 +477,40 @@ def test_reencode_config1_sampled():
                                            scale=1 / math.sqrt(D), rows=rows)
     check_out(out[rows], want, "bf16", "config1 re-encode sampled rows")
     check_lse(lse[:, rows], wlse, "bf16", "config1 re-encode sampled rows")
+
+
+# --------------------------------------------------------------------------
+# window/sink sweep shapes at full size
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,W", [(0, 21), (3, 27), (0, 3), (3, 3), (0, 12)])
+def test_window_sweep_shapes_sampled(S, W):
+    """The sweep's extreme shapes at full size (12 heads x 128, 4680-token
+    chunks): the paper's long window (21 frames, no sink), the longest window
+    with sink, a window of the current chunk alone with and without sink, and
+    the short window without sink.  The sink and ring are filled and one
+    chunk evicted; sampled rows of the next chunk's call vs the oracle."""
+    T, C, H, D = 1560, 3, 12, 128
+    g = CacheGeometry(T, C, S, W)
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    hist = LayerHistory(g)
+    n = S // C + (W - C) // C + 1
+    for c in range(n):
+        k = synth.normal((4680, H, D), "bf16", 150, S, c, W, K)
+        v = synth.normal((4680, H, D), "bf16", 150, S, c, W, V)
+        cache.append_chunk(0, dev(k, "bf16"), dev(v, "bf16"))
+        hist.append(k, v)
+    q, k, v = (synth.normal((4680, H, D), "bf16", 150, S, n, W, t) for t in (Q, K, V))
+    out = torch.empty((4680, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, 4680), dtype=torch.float32, device="cuda")
+    say(f"[sweep S={S} W={W}] chunk {n}: {S * T + W * T} keys")
+    cache.attn(0, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), 1 / math.sqrt(D), out, lse)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 255, 256, 4607, 4608, 4679],
+                                     np.random.default_rng(S + W).choice(4680, 40, replace=False)]))
+    hk, hv = hist.keys(k, v)
+    want, wlse = sink_window_attention(q[rows], hk, hv, n, tokens_per_frame=T, frames_per_chunk=C,
+                                       sink_frames=S, window_frames=W, scale=1 / math.sqrt(D))
+    check_out(out[rows], want, "bf16", f"sweep S={S} W={W}")
+    check_lse(lse[:, rows], wlse, "bf16", f"sweep S={S} W={W}")
