@@ -21,13 +21,15 @@ seeded input generator, which holds none of the method's arithmetic.
 """
 
 from .attention import (allowed_frames, frame_mask, masked_attention,
-                        sink_window_attention, cross_attention, window_reencode_attention)
+                        sink_window_attention, cross_attention, window_reencode_attention,
+                        sink_window_attention_grad)
 from .cache_model import (CacheGeometry, slot_of_chunk, DequeCacheModel,
                           resident_window_chunks, LayerHistory)
 from .quant import quantize_int8, dequantize_int8
 
 __all__ = [
     "allowed_frames", "frame_mask", "masked_attention", "sink_window_attention",
-    "cross_attention", "window_reencode_attention", "CacheGeometry", "slot_of_chunk", "DequeCacheModel",
+    "cross_attention", "window_reencode_attention", "sink_window_attention_grad",
+    "CacheGeometry", "slot_of_chunk", "DequeCacheModel",
     "resident_window_chunks", "LayerHistory", "quantize_int8", "dequantize_int8",
 ]

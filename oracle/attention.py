@@ -28,6 +28,12 @@ What is computed, and where it is stated:
   encoding the frames already generated again, paired with the new prompt
   (same paper, §3.1 "KV recache"; Fig. 2, right).  The self-attention of that
   pass is :func:`window_reencode_attention`.
+* Training side (streaming long tuning): each step keeps the last W frames'
+  K/V of the earlier context without gradient, the current supervised clip's
+  K/V with gradient, and the sink tokens concatenated to every layer (same
+  paper, §3.3 "Consistency between training and inference"; §3.2: generated
+  frames are detached, gradients flow through the current clip only).  The
+  backward of the attention call is :func:`sink_window_attention_grad`.
 """
 
 import numpy as np
@@ -164,3 +170,52 @@ def window_reencode_attention(q_win, hist_k, hist_v, window_chunks, *, tokens_pe
             out[sel], lse[:, sel] = masked_attention(q_win[rows[sel]], hist_k, hist_v, mask,
                                                      scale, query_block)
     return out, lse
+
+
+def sink_window_attention_grad(q, hist_k, hist_v, chunk, dout, n_grad, *, tokens_per_frame,
+                               frames_per_chunk, sink_frames, window_frames, scale,
+                               query_block=512):
+    """Gradients of :func:`sink_window_attention` for the training step.
+
+    The last ``n_grad`` tokens of the history (the current clip's K/V) carry
+    gradient; the earlier ones (sink and window context) are detached (LongLive
+    paper, §3.2 and §3.3).  With P = softmax(S) over the allowed keys,
+    S = scale * q.k, O = P V and upstream gradient dO:
+
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(P * dP)),
+        dQ = scale * dS K,   dK = scale * dS^T Q,
+
+    the textbook derivative of softmax attention, in float64.  Returns
+    (dq [n_q, H, D], dk [n_grad, H, D], dv [n_grad, H, Dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(hist_k, dtype=np.float64)
+    v = np.asarray(hist_v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    mask = frame_mask(n_k, chunk, tokens_per_frame=tokens_per_frame,
+                      frames_per_chunk=frames_per_chunk, sink_frames=sink_frames,
+                      window_frames=window_frames)
+    if not mask.any():
+        raise ValueError("attention over an empty key set is undefined")
+    g0 = n_k - n_grad
+    dq = np.zeros_like(q)
+    dk = np.zeros((n_grad, H, D), dtype=np.float64)
+    dv = np.zeros((n_grad, H, v.shape[2]), dtype=np.float64)
+    for h in range(H):
+        kh, vh = k[:, h, :], v[:, h, :]
+        for q0 in range(0, n_q, query_block):
+            qb = q[q0:q0 + query_block, h, :]
+            dob = do[q0:q0 + query_block, h, :]
+            logits = scale * (qb @ kh.T)
+            logits[:, ~mask] = -np.inf
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            dp = dob @ vh.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[q0:q0 + query_block, h, :] = scale * (ds @ kh)
+            dk[:, h, :] += scale * (ds[:, g0:].T @ qb)
+            dv[:, h, :] += p[:, g0:].T @ dob
+    return dq, dk, dv

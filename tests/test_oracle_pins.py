@@ -18,7 +18,8 @@ from hypothesis import given, settings, strategies as st, HealthCheck
 from oracle import (allowed_frames, frame_mask, masked_attention,
                     sink_window_attention, cross_attention, CacheGeometry,
                     LayerHistory, quantize_int8, dequantize_int8,
-                    window_reencode_attention, resident_window_chunks)
+                    window_reencode_attention, resident_window_chunks,
+                    sink_window_attention_grad)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "attended_chunks.txt")
 
@@ -509,6 +510,77 @@ def test_reencode_closed_form_and_causality():
     k3, v3 = k.copy(), v.copy()
     k3[ct:4 * ct], v3[ct:4 * ct] = 5.0, 7.0     # evicted chunks 1..3
     np.testing.assert_array_equal(window_reencode_attention(q, k3, v3, win, **kw)[0], base)
+
+
+# --------------------------------------------------------------------------
+# gradients of the sink+window call (training step)
+# --------------------------------------------------------------------------
+
+def _grad_case(seed, T=3, C=2, S=2, W=6, H=2, D=8, chunk=4):
+    rng = np.random.default_rng(seed)
+    ct = C * T
+    n_hist = (chunk + 1) * ct
+    q = rng.standard_normal((ct, H, D))
+    k = rng.standard_normal((n_hist, H, D))
+    v = rng.standard_normal((n_hist, H, D))
+    do = rng.standard_normal((ct, H, D))
+    kw = dict(tokens_per_frame=T, frames_per_chunk=C, sink_frames=S, window_frames=W, scale=0.35)
+    return q, k, v, do, ct, kw, chunk
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_grad_matches_torch_autograd(seed):
+    """dQ, and dK/dV of the current chunk, equal torch autograd through SDPA
+    (float64, boolean key mask); the detached context gets no gradient."""
+    q, k, v, do, ct, kw, chunk = _grad_case(seed)
+    dq, dk, dv = sink_window_attention_grad(q, k, v, chunk, do, ct, **kw)
+    mask = frame_mask(k.shape[0], chunk, tokens_per_frame=kw["tokens_per_frame"],
+                      frames_per_chunk=kw["frames_per_chunk"], sink_frames=kw["sink_frames"],
+                      window_frames=kw["window_frames"])
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None].requires_grad_()
+    ctx_k = torch.from_numpy(k[:-ct]).permute(1, 0, 2)[None]
+    ctx_v = torch.from_numpy(v[:-ct]).permute(1, 0, 2)[None]
+    cur_k = torch.from_numpy(k[-ct:]).permute(1, 0, 2)[None].requires_grad_()
+    cur_v = torch.from_numpy(v[-ct:]).permute(1, 0, 2)[None].requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, torch.cat([ctx_k, cur_k], 2), torch.cat([ctx_v, cur_v], 2),
+        attn_mask=torch.from_numpy(np.broadcast_to(mask, (ct, mask.size)).copy()), scale=kw["scale"])
+    o.backward(torch.from_numpy(do).permute(1, 0, 2)[None])
+    np.testing.assert_allclose(dq, tq.grad[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, cur_k.grad[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, cur_v.grad[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_grad_matches_finite_differences():
+    """Central differences of L = sum(dO * O) through the forward oracle."""
+    q, k, v, do, ct, kw, chunk = _grad_case(7, T=2, C=1, S=1, W=3, H=1, D=4, chunk=3)
+    dq, dk, dv = sink_window_attention_grad(q, k, v, chunk, do, ct, **kw)
+    loss = lambda q_, k_, v_: float((sink_window_attention(q_, k_, v_, chunk, **kw)[0] * do).sum())
+    eps = 1e-6
+    n0 = k.shape[0] - ct
+    for (i, d) in [(0, 0), (1, 3)]:
+        e = np.zeros_like(q); e[i, 0, d] = eps
+        assert abs((loss(q + e, k, v) - loss(q - e, k, v)) / (2 * eps) - dq[i, 0, d]) < 1e-7
+        e = np.zeros_like(k); e[n0 + i, 0, d] = eps
+        assert abs((loss(q, k + e, v) - loss(q, k - e, v)) / (2 * eps) - dk[i, 0, d]) < 1e-7
+        e = np.zeros_like(v); e[n0 + i, 0, d] = eps
+        assert abs((loss(q, k, v + e) - loss(q, k, v - e)) / (2 * eps) - dv[i, 0, d]) < 1e-7
+
+
+def test_grad_closed_forms():
+    """Q = 0 (uniform weights over the allowed keys): dV of a current key is
+    the sum of dO over queries divided by the allowed key count.  Constant V:
+    dP is the same for every key, so dS, dQ and dK vanish."""
+    q, k, v, do, ct, kw, chunk = _grad_case(3)
+    n_allowed = int(frame_mask(k.shape[0], chunk, tokens_per_frame=kw["tokens_per_frame"],
+                               frames_per_chunk=kw["frames_per_chunk"],
+                               sink_frames=kw["sink_frames"],
+                               window_frames=kw["window_frames"]).sum())
+    _, _, dv = sink_window_attention_grad(np.zeros_like(q), k, v, chunk, do, ct, **kw)
+    np.testing.assert_allclose(dv, np.broadcast_to(do.sum(0) / n_allowed, dv.shape), rtol=0, atol=1e-12)
+    vc = np.broadcast_to(np.random.default_rng(4).standard_normal((1,) + v.shape[1:]), v.shape).copy()
+    dq, dk, _ = sink_window_attention_grad(q, k, vc, chunk, do, ct, **kw)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
 
 
 # --------------------------------------------------------------------------
