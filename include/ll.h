@@ -162,6 +162,30 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
                               void* out, float* lse, ll_stream_t stream);
 
 /*
+ * Backward of ll_sink_window_attn for the training step (paper §3.2: frames
+ * generated earlier are detached and gradients flow through the current clip
+ * only; §3.3: training keeps the last W frames' K/V without gradient, the
+ * current clip's K/V with gradient, and the sink concatenated to every layer).
+ * The key set is the one the forward call with the same arguments used: the
+ * cached sink and window (detached: they get no gradient) and, when
+ * n_cur == C_tok, the current chunk k_cur/v_cur, which does.
+ *   q, out, dout: [n_q][H][D] bf16 (out and lse from the forward call);
+ *   lse:   float [H][n_q], required;
+ *   delta: float [H][n_q] device workspace, overwritten with rowsum(dout*out);
+ *   dq:    float [n_q][H][D], written;
+ *   dk_cur, dv_cur: float [C_tok][H][D], written when n_cur == C_tok (ignored
+ *          when n_cur == 0).
+ * Gradients are fp32, accumulated in fp32 from bf16 MFMA products of bf16
+ * operands (P and dS rounded to bf16); P is recomputed from the forward's lse.
+ * Only BF16 activations with a BF16 cache are supported (else
+ * LL_ERR_UNSUPPORTED).  n_q >= 1.  LL_ERR_BAD_STATE if the key set is empty.
+ */
+ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                  const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                                  const void* out, const float* lse, const void* dout, float* delta,
+                                  float* dq, float* dk_cur, float* dv_cur, ll_stream_t stream);
+
+/*
  * Self-attention of the re-encoding pass of a KV-recache (paper §3.1 "KV
  * recache": at a prompt switch the frames already generated are encoded again
  * with the new prompt to rebuild the cache; §3.3: the cache holds the sink and

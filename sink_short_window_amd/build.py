@@ -28,6 +28,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-munsafe-fp-atomics"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
+DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip")
 LIB_LL = os.path.join(LIB, "libll.so")
 LIB_HOSTSTUB = os.path.join(LIB, "libll_hoststub.so")
 
@@ -55,10 +56,12 @@ def build_ll(verbose=False):
     os.makedirs(LIB, exist_ok=True)
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    kern_o = os.path.join(BUILD, "kernels.o")
-    out = _run([HIPCC] + DEVICE_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
-                                         os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
-    objs.append(kern_o)
+    out = ""
+    for src in DEVICE_SOURCES:
+        o = os.path.join(BUILD, src.replace(".hip", ".o"))
+        out += _run([HIPCC] + DEVICE_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                              os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     for f in ("cache_state.cpp", "ll_api.cpp"):
         o = os.path.join(BUILD, f.replace(".cpp", ".o"))
         _run(["g++"] + HOST_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, f), "-o", o])

@@ -54,6 +54,20 @@ struct AttnArgs {
   int32_t q_tiles = 0;
 };
 
+// Backward of one sink+window call (training step): the runs of `a` as the
+// forward walked them, the last of which (the caller's current chunk,
+// token-major) carries gradient.
+struct AttnBwdArgs {
+  AttnArgs a;
+  const void* out = nullptr;   // [n_q][H][D] forward output
+  const void* dout = nullptr;  // [n_q][H][D] upstream gradient
+  const float* lse = nullptr;  // [H][n_q] forward log-sum-exp (natural log)
+  float* delta = nullptr;      // [H][n_q] workspace: rowsum(dout * out)
+  float* dq = nullptr;         // [n_q][H][D]
+  float* dk = nullptr;         // [len of the last run][H][D], null when it carries none
+  float* dv = nullptr;
+};
+
 // Copy (or quantise) whole chunks of token-major K/V into cache rows.
 // Source chunk i of layer z is src + (z*src_layer_stride + i*ctok*H*D) elements
 // (token-major [ctok][H][D]); it goes to rows dst_row0[i] .. + ctok of every
@@ -85,6 +99,7 @@ struct CopyArgs {
 
 // Each returns 0 on success or the hipError_t code of the failed launch.
 int launch_attention(const AttnArgs& a, void* stream);
+int launch_attention_bwd(const AttnBwdArgs& a, void* stream);
 int launch_copy_chunks(const CopyArgs& a, void* stream);
 const char* hip_error_string(int err);
 

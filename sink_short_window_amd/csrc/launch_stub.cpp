@@ -11,8 +11,10 @@
 namespace ll {
 namespace {
 AttnArgs g_attn;
+AttnBwdArgs g_bwd;
 CopyArgs g_copy;
 int g_attn_calls = 0;
+int g_bwd_calls = 0;
 int g_copy_calls = 0;
 int g_fail_next = 0;
 }  // namespace
@@ -24,6 +26,17 @@ int launch_attention(const AttnArgs& a, void*) {
   }
   g_attn = a;
   ++g_attn_calls;
+  return 0;
+}
+
+int launch_attention_bwd(const AttnBwdArgs& a, void*) {
+  if (g_fail_next) {
+    g_fail_next = 0;
+    return 1;
+  }
+  g_bwd = a;
+  g_attn = a.a;  // the run table, readable through llh_last_attn
+  ++g_bwd_calls;
   return 0;
 }
 
@@ -74,6 +87,22 @@ int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][9] */) {
 int llh_last_attn_chunks(int32_t* n_seg0) {
   *n_seg0 = ll::g_attn.n_seg0;
   return ll::g_attn.q_chunk;
+}
+
+int llh_bwd_calls(void) { return ll::g_bwd_calls; }
+
+// Last backward launch: whether dK/dV are produced (the last run carries
+// gradient) and the workspace / gradient pointers as integers.
+int llh_last_bwd(int64_t* ptrs /* [delta, dq, dk, dv, out, dout, lse] */) {
+  const ll::AttnBwdArgs& b = ll::g_bwd;
+  ptrs[0] = int64_t(reinterpret_cast<intptr_t>(b.delta));
+  ptrs[1] = int64_t(reinterpret_cast<intptr_t>(b.dq));
+  ptrs[2] = int64_t(reinterpret_cast<intptr_t>(b.dk));
+  ptrs[3] = int64_t(reinterpret_cast<intptr_t>(b.dv));
+  ptrs[4] = int64_t(reinterpret_cast<intptr_t>(b.out));
+  ptrs[5] = int64_t(reinterpret_cast<intptr_t>(b.dout));
+  ptrs[6] = int64_t(reinterpret_cast<intptr_t>(b.lse));
+  return b.dk != nullptr;
 }
 
 // Last copy launch: n_chunks, n_layers and the destination row of each chunk.

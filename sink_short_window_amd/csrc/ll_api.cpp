@@ -86,6 +86,24 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
   return n_sink;
 }
 
+// The caller's current chunk (token-major [n_cur][H][D]) as the last run.
+void add_current_run(const ll::Geometry& g, const void* k_cur, const void* v_cur, int64_t n_cur,
+                     ll::AttnArgs& a, int32_t& keys) {
+  ll::KvSeg& s = a.seg[a.n_seg++];
+  s.k = k_cur;
+  s.v = v_cur;
+  s.ks = s.vs = nullptr;
+  s.head_stride = g.D;
+  s.row_stride = int64_t(g.H) * g.D;
+  s.sc_head_stride = 0;
+  s.v_head_stride = 0;
+  s.v_tiled = 0;
+  s.key_start = keys;
+  s.len = int32_t(n_cur);
+  s.quant = 0;
+  keys += int32_t(n_cur);
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,21 +332,7 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   ll::AttnArgs a;
   int32_t keys = 0;
   add_cache_runs(cs, layer, a, keys);
-  if (n_cur > 0) {
-    ll::KvSeg& s = a.seg[a.n_seg++];
-    s.k = k_cur;
-    s.v = v_cur;
-    s.ks = s.vs = nullptr;
-    s.head_stride = g.D;
-    s.row_stride = int64_t(g.H) * g.D;
-    s.sc_head_stride = 0;
-    s.v_head_stride = 0;
-    s.v_tiled = 0;
-    s.key_start = keys;
-    s.len = int32_t(n_cur);
-    s.quant = 0;
-    keys += int32_t(n_cur);
-  }
+  if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, a, keys);
   if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
   if (n_q == 0) return LL_OK;
   a.n_keys = keys;
@@ -342,6 +346,56 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   a.kv = g.kv;
   a.scale = scale;
   return launched(ll::launch_attention(a, stream), "attention launch");
+}
+
+ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                  const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                                  const void* out, const float* lse, const void* dout, float* delta,
+                                  float* dq, float* dk_cur, float* dv_cur, ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  if (g.act != LL_BF16 || g.kv != LL_BF16)
+    return fail(LL_ERR_UNSUPPORTED, "the backward supports BF16 activations with a BF16 cache");
+  if (n_q < 1 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q must be in [1, 2^30)");
+  if (n_cur != 0 && n_cur != g.ctok)
+    return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK ||
+      (st = check_act_ptr(dout, "dout")) != LL_OK || (st = check_act_ptr(dq, "dq")) != LL_OK)
+    return st;
+  if (!lse || !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is NULL or not 4-byte aligned");
+  if (!delta || !aligned(delta, 4)) return fail(LL_ERR_INVALID_ARG, "delta is NULL or not 4-byte aligned");
+  if (n_cur > 0) {
+    if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK ||
+        (st = check_act_ptr(dk_cur, "dk_cur")) != LL_OK || (st = check_act_ptr(dv_cur, "dv_cur")) != LL_OK)
+      return st;
+  }
+  ll::AttnBwdArgs b;
+  int32_t keys = 0;
+  add_cache_runs(cs, layer, b.a, keys);
+  if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, b.a, keys);
+  if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
+  b.a.n_keys = keys;
+  b.a.q = q;
+  b.a.out = nullptr;
+  b.a.lse = nullptr;
+  b.a.n_q = int32_t(n_q);
+  b.a.H = g.H;
+  b.a.D = g.D;
+  b.a.act = g.act;
+  b.a.kv = g.kv;
+  b.a.scale = scale;
+  b.out = out;
+  b.dout = dout;
+  b.lse = lse;
+  b.delta = delta;
+  b.dq = dq;
+  b.dk = n_cur > 0 ? dk_cur : nullptr;
+  b.dv = n_cur > 0 ? dv_cur : nullptr;
+  return launched(ll::launch_attention_bwd(b, stream), "attention backward launch");
 }
 
 ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const void* q,

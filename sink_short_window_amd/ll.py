@@ -26,7 +26,7 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
 # Every function include/ll.h declares (checked against the header by the tests).
 EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
            "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
-           "ll_window_reencode_attn", "ll_cross_attn", "ll_cache_query", "ll_cache_layout", "ll_status_str", "ll_last_error")
+           "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_cross_attn", "ll_cache_query", "ll_cache_layout", "ll_status_str", "ll_last_error")
 
 
 class ll_cache_config(ctypes.Structure):
@@ -56,6 +56,8 @@ _SIGS = {
     "ll_cache_recache": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
     "ll_sink_window_attn": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "ll_window_reencode_attn": (_i32, [_vp, _i32, _vp, _i64, _f32, _vp, _vp, _vp]),
+    "ll_sink_window_attn_bwd": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp]),
     "ll_cross_attn": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "ll_cache_query": (_i32, [_vp, _i32, _P(_i64), _P(_i32), _P(_i32), _P(_i64)]),
     "ll_cache_layout": (_i32, [_vp, _i32, _i32, _i32, _P(_sz), _P(_i64), _P(_i64)]),
@@ -205,6 +207,22 @@ def ll_window_reencode_attn(handle, layer, q, scale, out, act_dtype, lse=None, s
         _dev_ptr(lse, "lse", "float32", True), _stream(stream, q)))
 
 
+def ll_sink_window_attn_bwd(handle, layer, q, k_cur, v_cur, scale, out, lse, dout, delta, dq,
+                            dk_cur=None, dv_cur=None, stream=None, lib=None):
+    """Backward of ll_sink_window_attn (bf16).  q, out, dout: [n_q, H, D] bf16;
+    lse, delta: float32 [H, n_q]; dq: float32 [n_q, H, D]; k_cur/v_cur: bf16
+    [C_tok, H, D] or None; dk_cur/dv_cur: float32 [C_tok, H, D] with them."""
+    lib = lib or load()
+    n_cur = 0 if k_cur is None else k_cur.shape[0]
+    _check(lib, lib.ll_sink_window_attn_bwd(
+        handle, layer, _dev_ptr(q, "q", "bfloat16"), q.shape[0],
+        _dev_ptr(k_cur, "k_cur", "bfloat16", True), _dev_ptr(v_cur, "v_cur", "bfloat16", True), n_cur,
+        float(scale), _dev_ptr(out, "out", "bfloat16"), _dev_ptr(lse, "lse", "float32"),
+        _dev_ptr(dout, "dout", "bfloat16"), _dev_ptr(delta, "delta", "float32"),
+        _dev_ptr(dq, "dq", "float32"), _dev_ptr(dk_cur, "dk_cur", "float32", n_cur == 0),
+        _dev_ptr(dv_cur, "dv_cur", "float32", n_cur == 0), _stream(stream, q)))
+
+
 def ll_cross_attn(q, k_txt, v_txt, scale, out, act_dtype, lse=None, stream=None, lib=None):
     """q, out: [n_q, H, D]; k_txt, v_txt: [n_txt, H, D]."""
     lib = lib or load()
@@ -292,6 +310,11 @@ class Cache:
     def attn(self, layer, q, k_cur, v_cur, scale, out, lse=None, stream=None):
         ll_sink_window_attn(self.handle, layer, q, k_cur, v_cur, scale, out, self.cfg.act_dtype,
                             lse, stream)
+
+    def attn_bwd(self, layer, q, k_cur, v_cur, scale, out, lse, dout, delta, dq, dk_cur=None,
+                 dv_cur=None, stream=None):
+        ll_sink_window_attn_bwd(self.handle, layer, q, k_cur, v_cur, scale, out, lse, dout, delta,
+                                dq, dk_cur, dv_cur, stream)
 
     def reencode_attn(self, layer, q, scale, out, lse=None, stream=None):
         ll_window_reencode_attn(self.handle, layer, q, scale, out, self.cfg.act_dtype, lse, stream)

@@ -34,6 +34,7 @@ def libs():
     stub.llh_last_copy.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     stub.llh_last_copy_vt.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     stub.llh_last_attn_chunks.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    stub.llh_last_bwd.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     return stub
 
 
@@ -360,6 +361,52 @@ def test_reencode_runs_are_sink_then_window_oldest_first(libs, T, C, S, W, act, 
         assert libs.ll_cache_append_chunk(h, 1, A, A, None) == 0
         sim.append()
     libs.ll_cache_destroy(h)
+
+
+def test_backward_validation_and_launch(libs):
+    """The backward takes the forward's run table; only the current chunk
+    carries dK/dV; bf16 only; every pointer is checked before launching."""
+    c = cfg(L=2, T=4, C=2, S=2, W=6, H=3, D=64)
+    h = create(libs, c)
+    ct = 8
+    A, F = FAKE_ACT, FAKE_ACT + (1 << 24)
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("layer", 1), ("q", A), ("n_q", 5), ("k", A), ("v", A), ("n_cur", ct), ("scale", 0.1),
+        ("out", A), ("lse", F), ("dout", A), ("delta", F), ("dq", F), ("dk", F), ("dv", F))] + [None]
+    call = lambda **kw: status(libs, libs.ll_sink_window_attn_bwd(h, *args(**kw)))
+    for _ in range(3):
+        assert libs.ll_cache_append_chunk(h, 1, A, A, None) == 0
+    assert call() == "LL_OK"
+    nk = ctypes.c_int64()
+    runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+    n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+    libs.ll_sink_window_attn(h, 1, A, 5, A, A, ct, 0.1, A, None, None)
+    nk2 = ctypes.c_int64()
+    runs2 = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+    assert libs.llh_last_attn(ctypes.byref(nk2), runs2) == n_seg and nk.value == nk2.value
+    assert list(runs[:RUN_FIELDS * n_seg]) == list(runs2[:RUN_FIELDS * n_seg])
+    assert runs[RUN_FIELDS * (n_seg - 1)] == A                     # the current chunk is last
+    ptrs = (ctypes.c_int64 * 7)()
+    assert libs.llh_last_bwd(ptrs) == 1 and list(ptrs[:4]) == [F, F, F, F]
+    assert call(n_cur=0, dk=None, dv=None, k=None, v=None) == "LL_OK"
+    assert libs.llh_last_bwd(ptrs) == 0 and ptrs[2] == 0 and ptrs[3] == 0
+    for bad in (dict(n_q=0), dict(n_cur=ct - 1), dict(scale=0.0), dict(lse=None), dict(delta=None),
+                dict(dq=None), dict(dq=F + 4), dict(dk=None), dict(dv=F + 8), dict(dout=None),
+                dict(out=A + 2), dict(q=None), dict(layer=2)):
+        calls = libs.llh_bwd_calls()
+        assert call(**bad) == "LL_ERR_INVALID_ARG", bad
+        assert libs.llh_bwd_calls() == calls
+    libs.llh_fail_next_launch()
+    assert call() == "LL_ERR_HIP"
+    libs.ll_cache_destroy(h)
+    for act, kv in ((ll.LL_F32, ll.LL_F32), (ll.LL_BF16, ll.LL_I8)):
+        h2 = create(libs, cfg(act=act, kv=kv))
+        assert status(libs, libs.ll_sink_window_attn_bwd(h2, *args(layer=0))) == "LL_ERR_UNSUPPORTED"
+        libs.ll_cache_destroy(h2)
+    h3 = create(libs, cfg())
+    assert status(libs, libs.ll_sink_window_attn_bwd(h3, *args(layer=0, n_cur=0, k=None, v=None))) \
+        == "LL_ERR_BAD_STATE"
+    libs.ll_cache_destroy(h3)
 
 
 def test_attention_and_cross_attention_errors(libs):

@@ -1,0 +1,117 @@
+"""GPU parity of the backward of the sink+window call (training step).
+
+LongLive: Real-time Interactive Long Video Generation, §3.2 (gradients flow
+through the current clip only; earlier frames are detached) and §3.3 (the
+window's K/V without gradient, the current clip's with gradient, the sink
+concatenated).  The forward runs through ll_sink_window_attn (which also gives
+the lse the backward needs); the backward's dQ, dK_cur and dV_cur are
+compared with the float64 oracle on the same bf16 inputs.
+
+Tolerance: the kernel rounds Q*scale*log2(e), P and dS to bf16 (relative
+2^-9 each) and forms delta from the bf16 forward output, with fp32
+accumulation; the gradients are checked per tensor by relative L2 error
+(<= 2e-2) and max-abs error relative to the tensor's largest value (<= 3e-2).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import CacheGeometry, LayerHistory, sink_window_attention_grad
+from sink_short_window_amd import ll, synth
+from sink_short_window_amd.synth import Q, K, V
+from gpu_util import need_gpu, say, dev, host
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_L2 = 2e-2
+GRAD_MAX_REL = 3e-2
+DOUT = 20     # synth tensor id of the upstream gradient
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def check_grad(got, want, what):
+    g = host(got)
+    assert np.isfinite(g).all(), f"{what}: non-finite gradient"
+    err = np.abs(g - want)
+    scale = max(float(np.abs(want).max()), 1e-30)
+    rel = float(np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30))
+    say(f"  {what}: rel_l2={rel:.3e} max_abs={float(err.max()):.3e} (max |want| {scale:.3e})")
+    assert rel <= GRAD_REL_L2, f"{what}: rel L2 {rel}"
+    assert float(err.max()) <= GRAD_MAX_REL * scale, f"{what}: max abs {float(err.max())}"
+
+
+def run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=True, rows=None):
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg)
+    g = CacheGeometry(T, C, S, W)
+    hist = LayerHistory(g)
+    ct = g.chunk_tokens
+    scale = 1.0 / math.sqrt(D)
+    for c in range(n_pre):
+        k = synth.normal((ct, H, D), "bf16", cfg_id, 0, c, 0, K)
+        v = synth.normal((ct, H, D), "bf16", cfg_id, 0, c, 0, V)
+        cache.append_chunk(0, dev(k, "bf16"), dev(v, "bf16"))
+        hist.append(k, v)
+    c = n_pre
+    q, k, v, do = (synth.normal((ct, H, D), "bf16", cfg_id, 0, c, 0, t) for t in (Q, K, V, DOUT))
+    dq_, dk_, dv_, ddo = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    out = torch.empty_like(dq_)
+    lse = torch.empty((H, ct), dtype=torch.float32, device="cuda")
+    say(f"[bwd cfg={cfg_id} T={T} C={C} S={S} W={W} H={H} D={D}] chunk {c}"
+        f"{'' if with_cur else ' (cache only)'}")
+    kc, vc = (dk_, dv_) if with_cur else (None, None)
+    cache.attn(0, dq_, kc, vc, scale, out, lse)
+    delta = torch.empty((H, ct), dtype=torch.float32, device="cuda")
+    gq = torch.empty((ct, H, D), dtype=torch.float32, device="cuda")
+    gk = torch.empty((ct, H, D), dtype=torch.float32, device="cuda") if with_cur else None
+    gv = torch.empty((ct, H, D), dtype=torch.float32, device="cuda") if with_cur else None
+    cache.attn_bwd(0, dq_, kc, vc, scale, out, lse, ddo, delta, gq, gk, gv)
+    torch.cuda.synchronize()
+    hk, hv = hist.keys(k, v) if with_cur else hist.keys()
+    n_grad = ct if with_cur else 0
+    wq, wk, wv = sink_window_attention_grad(q, hk, hv, c, do, n_grad, tokens_per_frame=T,
+                                            frames_per_chunk=C, sink_frames=S, window_frames=W,
+                                            scale=scale)
+    sel = slice(None) if rows is None else rows
+    check_grad(gq[sel], wq[sel], "dq")
+    if with_cur:
+        check_grad(gk[sel], wk[sel], "dk_cur")
+        check_grad(gv[sel], wv[sel], "dv_cur")
+
+
+def test_bwd_ragged_tiles_d128():
+    """100-token chunks: ragged key tiles in every run, one ragged query tile
+    and one ragged key block of the current chunk; sink + full ring."""
+    run_bwd(160, 50, 2, 2, 6, 2, 128, 4)
+
+
+def test_bwd_d64_no_sink_several_tiles():
+    """300-token chunks: three query tiles and three key blocks, no sink."""
+    run_bwd(161, 150, 2, 0, 6, 3, 64, 3)
+
+
+def test_bwd_cache_only_dq():
+    """n_cur = 0: the key set is the cached context alone; only dQ."""
+    run_bwd(162, 40, 2, 2, 6, 2, 128, 3, with_cur=False)
+
+
+def test_bwd_two_sink_chunks_first_chunk():
+    """Early chunk (window not full yet) and a sink of two chunks."""
+    run_bwd(163, 24, 1, 2, 4, 3, 128, 1)
+    run_bwd(164, 24, 1, 2, 4, 3, 128, 5)
+
+
+def test_bwd_config1_full():
+    """Full size: 12 heads x 128, 4680 queries over sink + 2 window chunks +
+    the current chunk (18720 keys), every gradient checked on sampled rows
+    against the full float64 oracle."""
+    rows = np.unique(np.concatenate([[0, 127, 128, 4607, 4608, 4679],
+                                     np.random.default_rng(3).choice(4680, 200, replace=False)]))
+    run_bwd(165, 1560, 3, 3, 9, 12, 128, 4, rows=rows)
