@@ -273,6 +273,38 @@ def window_sweep():
                                     "keys": short["keys_per_call"] / nosink["keys_per_call"]}}))
 
 
+def backward_flops():
+    """Algorithmic flop of one backward call at 18720 keys: S, dP and dQ over
+    every key, dV and dK over the current chunk's keys:
+    2 * D * H * L_q * (3 * L_k + 2 * C_tok)."""
+    return 2.0 * D * H * CT * (3 * keys_at(10) + 2 * CT)
+
+
+def time_backward(wl, reps=10):
+    """Backward of layer 0's call (sink + 2 window chunks + the current chunk,
+    18720 keys) on the cache as the timed steps left it: forward once for out
+    and lse, then HIP events around each backward call (its three kernels)."""
+    t = wl.torch
+    q, k, v, g = wl.q[0], wl.k[0], wl.v[0], wl.q[1]
+    out = t.empty_like(q)
+    lse = t.empty((H, CT), dtype=t.float32, device=wl.device)
+    wl.cache.attn(0, q, k, v, wl.scale, out, lse)
+    delta = t.empty((H, CT), dtype=t.float32, device=wl.device)
+    dq, dk, dv = (t.empty((CT, H, D), dtype=t.float32, device=wl.device) for _ in range(3))
+    call = lambda: wl.cache.attn_bwd(0, q, k, v, wl.scale, out, lse, g, delta, dq, dk, dv)
+    for _ in range(3):
+        call()
+    ms = []
+    for _ in range(reps):
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ms.append((a, b))
+    t.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ms)[reps // 2]
+
+
 def kernel_stats(timers, kind):
     """(average ms per launch, total work, total ms) of one kernel kind."""
     ev = timers.get(kind, [])
@@ -508,6 +540,12 @@ def main():
     extra["reencode_ms_per_call"] = re_ms
     extra["reencode_flop_per_call"] = reencode_flops()
     extra["reencode_tflops"] = reencode_flops() / (re_ms * 1e-3) / 1e12
+    # The training step's backward of one call (bf16 cache only).
+    if args.kv == "bf16":
+        bw_ms = time_backward(wl)
+        extra["backward_ms_per_call"] = bw_ms
+        extra["backward_flop_per_call"] = backward_flops()
+        extra["backward_tflops"] = backward_flops() / (bw_ms * 1e-3) / 1e12
 
     roofline = None
     if tflops:

@@ -28,9 +28,10 @@
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
 //
-// Tiles reach LDS through registers into rows padded by 16 bytes.  A V tile
-// of the bf16 cache (stored transposed, [D][64] per 64 keys) is transposed
-// back to key-major rows while it is staged.
+// Tiles reach LDS through registers into rows padded by 16 bytes.  In the dQ
+// kernel V stays transposed ([D][64] per 64 keys, as the bf16 cache stores
+// it; the caller's row-major current chunk is transposed while staged) and
+// its rows are read back with transpose reads.
 
 #include <hip/hip_runtime.h>
 
@@ -148,11 +149,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
-  constexpr int RB = (D + 8) * 2;  // LDS row bytes
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(AttnBwdArgs p) {
+  constexpr int RB = (D + 8) * 2;  // LDS row bytes of K rows
+  constexpr int VRB = (kTile + 8) * 2;  // LDS row bytes of the transposed V tile
   constexpr int NV = D / 8;        // 16-byte vectors per row
   __shared__ __attribute__((aligned(16))) char ks[kTile * RB];
-  __shared__ __attribute__((aligned(16))) char vs[kTile * RB];
+  __shared__ __attribute__((aligned(16))) char vs[D * VRB];  // [d][column], column p = key vt_key(p)
   const AttnArgs& a = p.a;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -187,6 +189,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
   const int rd = r32 * RB + half * 16;  // A = K/V rows: row r32, granule 2j + half
   int toff[2][D / 32];
   tr_offsets<D>(lane, toff);
+  // V rows (A of dP^T: key 32*kb + r32, d = 16j + 8*half + 0..7) from the
+  // transposed tile by two transpose reads: the address lane (e = j16 >> 2,
+  // m = j16 & 3) of a 16-lane group points at row d = 16j + 8*half + 4*aa + e,
+  // at the column holding keys 16*(g16 & 1) + 4m .. +3, i.e. column
+  // 16*(g16 & 1) + 4*swap(m) where swap exchanges m's two bits.
+  int voff[2];
+  {
+    const int g16 = lane >> 4, j16 = lane & 15, m = j16 & 3;
+    const int col = 16 * (g16 & 1) + 4 * (((m & 1) << 1) | (m >> 1));
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) voff[aa] = (8 * (g16 >> 1) + 4 * aa + (j16 >> 2)) * VRB + col * 2;
+  }
 
   for (int r = 0; r < a.n_seg; ++r) {
     const KvSeg& sg = a.seg[r];
@@ -207,23 +221,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
             __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
       }
       if (vt) {
-        // [D][64] tile: row d, 16-byte granule g = columns 8g .. 8g+7
+        // [D][64] tile as stored (columns already in vt_key order): copy rows
         const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
 #pragma unroll
         for (int it = tid; it < D * 8; it += kBwdThreads) {
           const int d = it >> 3, g = it & 7;
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + d * 128 + g * 16, 0, 0);
-          const bf16x8 b = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<__bf16*>(vs + vt_key(8 * g + e) * RB + d * 2) = b[e];
+          *reinterpret_cast<u32x4*>(vs + d * VRB + g * 16) =
+              __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + d * 128 + g * 16, 0, 0);
         }
       } else {
+        // row-major V (the current chunk): key row -> column vt_key(row)
 #pragma unroll
         for (int it = tid; it < kTile * NV; it += kBwdThreads) {
           const int row = it / NV, vec = it % NV;
-          *reinterpret_cast<u32x4*>(vs + row * RB + vec * 16) =
-              __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
+          const bf16x8 b = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + row) * rs + vec * 16, 0, 0));
+          char* col = vs + vt_key(row) * 2 + vec * 8 * VRB;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) *reinterpret_cast<__bf16*>(col + e * VRB) = b[e];
         }
       }
       __syncthreads();
@@ -236,7 +251,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + rd + 32 * j);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + kb * 32 * RB + rd + 32 * j);
+          const char* vb = vs + j * 16 * VRB + kb * 64;
+          const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[0]), tr_read(vb + voff[1]), 0, 1, 2, 3, 4, 5, 6, 7);
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
         }
@@ -273,7 +289,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 // dK, dV of the current chunk (the last run)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(AttnBwdArgs p) {
   constexpr int RB = (D + 8) * 2;
   constexpr int NV = D / 8;
   __shared__ __attribute__((aligned(16))) char qs[kTile * RB];   // Q' rows
