@@ -14,13 +14,13 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // Three kernels on the stream:
 //   bwd_delta_kernel  delta[h][i] = dO_i . O_i (fp32).
-//   bwd_dq_kernel     per 128 queries of one head (4 waves x 32): walk every
+//   bwd_dq_kernel     per 256 queries of one head (8 waves x 32): walk every
 //                     64-key tile of every run; S^T = K Q'^T and dP^T = V dO^T
 //                     (bf16 MFMA 32x32x16, K/V rows from LDS, Q' and dO in
 //                     registers), P = 2^(S^T - lse2) from the forward's
 //                     log-sum-exp, dS^T in fp32 rounded to bf16, then
 //                     dQ^T += K^T dS^T with K^T from gfx950 transpose reads.
-//   bwd_dkv_kernel    per 128 keys of the current chunk: loop over 64-query
+//   bwd_dkv_kernel    per 256 keys of the current chunk: loop over 64-query
 //                     tiles; S = Q' K^T, dP = dO V^T (K/V fragments in
 //                     registers), then dV^T += dO^T P and dK^T += Q'^T dS with
 //                     dO^T and Q'^T from transpose reads.
@@ -49,9 +49,9 @@ typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int kBwdThreads = 256;  // 4 waves
-constexpr int kBwdBQ = 128;       // queries per dq workgroup
-constexpr int kBwdBK = 128;       // current-chunk keys per dk/dv workgroup
+constexpr int kBwdThreads = 512;  // 8 waves
+constexpr int kBwdBQ = 256;       // queries per dq workgroup (8 waves x 32)
+constexpr int kBwdBK = 256;       // current-chunk keys per dk/dv workgroup (8 waves x 32)
 constexpr int kTile = 64;         // keys (dq) or queries (dk/dv) per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
   constexpr int RB = (D + 8) * 2;  // LDS row bytes of K rows
   constexpr int VRB = (kTile + 8) * 2;  // LDS row bytes of the transposed V tile
   constexpr int NV = D / 8;        // 16-byte vectors per row
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(AttnBwdArgs p) {
 // dK, dV of the current chunk (the last run)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   constexpr int RB = (D + 8) * 2;
   constexpr int NV = D / 8;
   __shared__ __attribute__((aligned(16))) char qs[kTile * RB];   // Q' rows
