@@ -153,8 +153,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
   constexpr int RB = (D + 8) * 2;  // LDS row bytes of K rows
   constexpr int VRB = (kTile + 8) * 2;  // LDS row bytes of the transposed V tile
   constexpr int NV = D / 8;        // 16-byte vectors per row
-  __shared__ __attribute__((aligned(16))) char ks[kTile * RB];
-  __shared__ __attribute__((aligned(16))) char vs[D * VRB];  // [d][column], column p = key vt_key(p)
+  // two LDS buffers: tile t is read from one while tile t+1 is written to the other
+  __shared__ __attribute__((aligned(16))) char ks2[2][kTile * RB];
+  __shared__ __attribute__((aligned(16))) char vs2[2][D * VRB];  // [d][column], column p = key vt_key(p)
   const AttnArgs& a = p.a;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -202,76 +203,100 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
     for (int aa = 0; aa < 2; ++aa) voff[aa] = (8 * (g16 >> 1) + 4 * aa + (j16 >> 2)) * VRB + col * 2;
   }
 
-  for (int r = 0; r < a.n_seg; ++r) {
-    const KvSeg& sg = a.seg[r];
+  // Loads of one 64-key tile, held in registers from issue to LDS write.
+  constexpr int NL = kTile * NV / kBwdThreads;  // 16-byte loads per thread per side
+  u32x4 kreg[NL], vreg[NL];
+  bool vt_reg = false;
+  auto issue = [&](int run, int t0) {
+    const KvSeg& sg = a.seg[run];
     const int len = sg.len;
     const uint32_t rs = uint32_t(sg.row_stride) * 2;
     const auto rk = rsrc(static_cast<const char*>(sg.k) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
-    const bool vt = sg.v_tiled != 0;
+    vt_reg = sg.v_tiled != 0;
     const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
-    const auto rv = vt ? rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2, tiles * kTile * D * 2)
-                       : rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
-    for (int t0 = 0; t0 < len; t0 += kTile) {
-      __syncthreads();  // the previous tile's reads are done
+    const auto rv = vt_reg ? rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2,
+                                  tiles * kTile * D * 2)
+                           : rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
+    const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int it = tid + i * kBwdThreads;
+      const int row = it / NV, vec = it % NV;
       // K rows (rows past the run read as zero)
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
+      // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or row-major rows
+      vreg[i] = vt_reg ? __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + (it >> 3) * 128 + (it & 7) * 16, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
+    }
+  };
+  auto stage = [&](char* kbuf, char* vbuf) {
 #pragma unroll
-      for (int it = tid; it < kTile * NV; it += kBwdThreads) {
-        const int row = it / NV, vec = it % NV;
-        *reinterpret_cast<u32x4*>(ks + row * RB + vec * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
-      }
-      if (vt) {
-        // [D][64] tile as stored (columns already in vt_key order): copy rows
-        const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
+    for (int i = 0; i < NL; ++i) {
+      const int it = tid + i * kBwdThreads;
+      const int row = it / NV, vec = it % NV;
+      *reinterpret_cast<u32x4*>(kbuf + row * RB + vec * 16) = kreg[i];
+      if (vt_reg) {  // columns already in vt_key order: copy
+        *reinterpret_cast<u32x4*>(vbuf + (it >> 3) * VRB + (it & 7) * 16) = vreg[i];
+      } else {       // row-major V (the current chunk): key row -> column vt_key(row)
+        const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
+        char* col = vbuf + vt_key(row) * 2 + vec * 8 * VRB;
 #pragma unroll
-        for (int it = tid; it < D * 8; it += kBwdThreads) {
-          const int d = it >> 3, g = it & 7;
-          *reinterpret_cast<u32x4*>(vs + d * VRB + g * 16) =
-              __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + d * 128 + g * 16, 0, 0);
-        }
-      } else {
-        // row-major V (the current chunk): key row -> column vt_key(row)
-#pragma unroll
-        for (int it = tid; it < kTile * NV; it += kBwdThreads) {
-          const int row = it / NV, vec = it % NV;
-          const bf16x8 b = __builtin_bit_cast(
-              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + row) * rs + vec * 16, 0, 0));
-          char* col = vs + vt_key(row) * 2 + vec * 8 * VRB;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) *reinterpret_cast<__bf16*>(col + e * VRB) = b[e];
-        }
-      }
-      __syncthreads();
-      const int valid = min(kTile, len - t0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + rd + 32 * j);
-          const char* vb = vs + j * 16 * VRB + kb * 64;
-          const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[0]), tr_read(vb + voff[1]), 0, 1, 2, 3, 4, 5, 6, 7);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
-        }
-        float ds[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          const float pr = key < valid ? __builtin_amdgcn_exp2f(s[e] - lse2) : 0.f;
-          ds[e] = pr * (dp[e] - dl);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 b = pack8(ds, s2);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
-        }
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<__bf16*>(col + e * VRB) = b[e];
       }
     }
+  };
+
+  // Tiles in run order; runs are never empty.  Tile t is computed from
+  // buffer t & 1 while tile t+1's loads are in flight, then written to the
+  // other buffer; one barrier per tile.
+  int run = 0, t0 = 0;
+  issue(0, 0);
+  stage(ks2[0], vs2[0]);
+  __syncthreads();
+  for (int t = 0;; ++t) {
+    int nrun = run, nt0 = t0 + kTile;
+    if (nt0 >= a.seg[run].len) {
+      ++nrun;
+      nt0 = 0;
+    }
+    const bool has_next = nrun < a.n_seg;
+    if (has_next) issue(nrun, nt0);
+    const char* ks = ks2[t & 1];
+    const char* vs = vs2[t & 1];
+    const int valid = min(kTile, a.seg[run].len - t0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + rd + 32 * j);
+        const char* vb = vs + j * 16 * VRB + kb * 64;
+        const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[0]), tr_read(vb + voff[1]), 0, 1, 2, 3, 4, 5, 6, 7);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
+      }
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const float pr = key < valid ? __builtin_amdgcn_exp2f(s[e] - lse2) : 0.f;
+        ds[e] = pr * (dp[e] - dl);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 b = pack8(ds, s2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
+      }
+    }
+    if (has_next) stage(ks2[(t + 1) & 1], vs2[(t + 1) & 1]);
+    __syncthreads();
+    if (!has_next) break;
+    run = nrun;
+    t0 = nt0;
   }
   if (!q_ok) return;
   float* out = p.dq + qrow;
