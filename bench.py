@@ -305,6 +305,44 @@ def time_backward(wl, reps=10):
     return sorted(a.elapsed_time(b) for a, b in ms)[reps // 2]
 
 
+def backward_only():
+    """One layer at the workload's shapes: chunks 0..3 appended (sink = chunk 0,
+    window = chunks 2, 3), the forward of chunk 4 for out and lse, then the
+    backward of that call timed after a warmup of ~40 calls (median of 5
+    batches of 10).  Prints one JSON line."""
+    import torch
+    from sink_short_window_amd import ll, synth
+    gen = lambda i, tensor: synth.to_torch(
+        synth.normal((CT, H, D), "bf16", SWEEP_CFG_ID, 1, i, 0, tensor), "bf16", "cuda")
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg, "cuda")
+    for c in range(4):
+        cache.append_chunk(0, gen(c, synth.K), gen(c, synth.V))
+    q, k, v, g = gen(4, synth.Q), gen(4, synth.K), gen(4, synth.V), gen(5, synth.Q)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    out, lse = torch.empty_like(q), f32(H, CT)
+    scale = 1.0 / math.sqrt(D)
+    cache.attn(0, q, k, v, scale, out, lse)
+    delta, dq, dk, dv = f32(H, CT), f32(CT, H, D), f32(CT, H, D), f32(CT, H, D)
+    call = lambda: cache.attn_bwd(0, q, k, v, scale, out, lse, g, delta, dq, dk, dv)
+
+    def batch(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    batch(40)
+    ms = sorted(batch(10) / 10 for _ in range(5))[2]
+    print(json.dumps({"backward_ms_per_call": ms, "keys_per_call": keys_at(10),
+                      "flop_per_call": backward_flops(),
+                      "tflops": backward_flops() / (ms * 1e-3) / 1e12}))
+    cache.close()
+
+
 def kernel_stats(timers, kind):
     """(average ms per launch, total work, total ms) of one kernel kind."""
     ev = timers.get(kind, [])
@@ -453,6 +491,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only time one layer's attention call for windows of 3..27 frames with and "
                          "without the 3-frame sink (JSON line per point) and exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time the backward of one layer's call (training step) and exit")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor bf16 GEMM on random and on zero operands and exit")
     args = ap.parse_args()
@@ -468,6 +508,9 @@ def main():
         return
     if args.sweep:
         window_sweep()
+        return
+    if args.backward:
+        backward_only()
         return
     if args.passes < 1:
         print("--passes must be >= 1", file=sys.stderr)
