@@ -63,13 +63,14 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g) {
   if (r.ctok > lim || r.rows > lim || r.rows * r.D > lim)
     return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit row indexing");
   r.vt = r.kv == LL_BF16;
+  r.staged = r.kv == LL_I8;
   r.nslots = r.nsc + r.R;
   r.tps = int32_t((r.ctok + kVtTileKeys - 1) / kVtTileKeys);
   r.vt_head_elems = int64_t(r.nslots) * r.tps * kVtTileKeys * r.D;
-  if (r.vt && r.nslots + 1 > kMaxKeyRuns)
-    return fail(LL_ERR_UNSUPPORTED, "a BF16 cache walks each sink chunk and ring slot as its own key run: "
+  if ((r.vt || r.staged) && r.nslots + 1 > kMaxKeyRuns)
+    return fail(LL_ERR_UNSUPPORTED, "BF16 and I8 caches walk each sink chunk and ring slot as its own key run: "
                                     "sink chunks + ring slots must be <= " + std::to_string(kMaxKeyRuns - 1));
-  if (r.vt && r.vt_head_elems > lim) return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit indexing");
+  if ((r.vt || r.staged) && r.vt_head_elems > lim) return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit indexing");
   // The kernels address a token-major chunk ([ctok][H][D] activations) with
   // one 32-bit buffer range.
   if (r.ctok * r.H * r.D * int64_t(dtype_bytes(r.act)) >= (int64_t(1) << 32))
@@ -90,6 +91,11 @@ Layout make_layout(const Geometry& g) {
   l.vs_off = off; off = align256(off + sc_bytes);
   l.layer_bytes = std::max<size_t>(off, 256);
   l.total_bytes = l.layer_bytes * size_t(g.L);
+  if (g.staged) {
+    l.stage_k_off = l.total_bytes;
+    l.stage_v_off = align256(l.stage_k_off + size_t(g.H) * g.rows * g.D * 2);
+    l.total_bytes = align256(l.stage_v_off + size_t(g.H) * size_t(g.vt_head_elems) * 2);
+  }
   return l;
 }
 

@@ -40,6 +40,10 @@ struct Geometry {
   // then ring slots) of tps tiles, each tile [D][64] with zero padding after
   // the chunk's last key.
   bool vt = false;
+  // An I8 cache is read by the attention through a bf16 staging copy of one
+  // layer's resident sink + ring in the BF16 layout (K rows, V tiles),
+  // written per call from the int8 codes and scales.
+  bool staged = false;
   int32_t tps = 0;            // tiles per chunk slot, ceil(ctok / 64)
   int32_t nslots = 0;         // nsc + R
   int64_t vt_head_elems = 0;  // nslots * tps * 64 * D
@@ -55,10 +59,12 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g);
 // 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype; for a BF16
 // cache V is [H][nslots*tps][D][64] instead, see Geometry), and with I8
 // K scales [H][rows], V scales [H][rows] (fp32).  Rows [0, sink_rows) are the
-// sink; ring slot s is rows sink_rows + [s*ctok, (s+1)*ctok).
+// sink; ring slot s is rows sink_rows + [s*ctok, (s+1)*ctok).  An I8 cache
+// ends with the bf16 staging area: K [H][rows][D], V [H][nslots*tps][D][64].
 struct Layout {
   size_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0;  // within a layer
   size_t layer_bytes = 0;
+  size_t stage_k_off = 0, stage_v_off = 0;  // from the buffer base (I8 only)
   size_t total_bytes = 0;
 };
 Layout make_layout(const Geometry& g);

@@ -952,6 +952,56 @@ __global__ __launch_bounds__(256) void copy_vt_kernel(CopyArgs a) {
   }
 }
 
+// bf16 staging of an I8 layer for the attention, one workgroup per (head,
+// 64-key tile, listed chunk): every code becomes bf16(q * s) with the row's
+// fp32 scale (the fma of int8x8_dequant_bf16x8), once per call instead of
+// once per query tile.  K rows are written in place of the same rows of the
+// staging K; V goes through LDS to the transposed tile of the chunk's slot
+// (column p holds key p with bits 2 and 3 swapped; zeros past the chunk).
+template <int D>
+__global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
+  constexpr int kG = D / 8;  // 8-code groups per row
+  __shared__ __attribute__((aligned(16))) __bf16 t[kBN][D + 8];
+  const int h = blockIdx.x / a.tps;
+  const int tile = blockIdx.x % a.tps;
+  const int chunk = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int valid = min(kBN, a.ctok - tile * kBN);
+  const int64_t row_base = int64_t(h) * a.rows + a.row0[chunk] + tile * kBN;  // head-major row index
+  const char* kq = a.layer + a.k_off;
+  const char* vq = a.layer + a.v_off;
+  const float* ks = reinterpret_cast<const float*>(a.layer + a.ks_off);
+  const float* vs = reinterpret_cast<const float*>(a.layer + a.vs_off);
+  __bf16* dk = reinterpret_cast<__bf16*>(a.dst_k);
+#pragma unroll
+  for (int it = tid; it < kBN * kG; it += 256) {
+    const int key = it / kG, g = it % kG;
+    u32x4 vw = {0, 0, 0, 0};
+    if (key < valid) {
+      const int64_t r = row_base + key;
+      const uint2 kc = *reinterpret_cast<const uint2*>(kq + r * D + g * 8);
+      const uint2 vc = *reinterpret_cast<const uint2*>(vq + r * D + g * 8);
+      *reinterpret_cast<u32x4*>(dk + r * D + g * 8) = int8x8_dequant_bf16x8(u32x2{kc.x, kc.y}, ks[r]);
+      vw = int8x8_dequant_bf16x8(u32x2{vc.x, vc.y}, vs[r]);
+    }
+    *reinterpret_cast<u32x4*>(&t[key][g * 8]) = vw;
+  }
+  __syncthreads();
+  __bf16* dst = reinterpret_cast<__bf16*>(a.dst_v) + int64_t(h) * a.vt_head_elems +
+                (int64_t(a.slot[chunk]) * a.tps + tile) * (kBN * D);
+#pragma unroll
+  for (int it = tid; it < D * (kBN / 8); it += 256) {
+    const int d = it / (kBN / 8), p0 = (it % (kBN / 8)) * 8;
+    bf16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j;
+      o[j] = t[(p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)][d];
+    }
+    *reinterpret_cast<bf16x8*>(dst + d * kBN + p0) = o;
+  }
+}
+
 // INT8 writer: one group of D/8 lanes per (head, row); each lane quantises
 // 8 values.  s = max|x| / 127 (IEEE fp32 division), q = clamp(rne(x / s)).
 __global__ __launch_bounds__(256) void quant_chunks_kernel(CopyArgs a) {
@@ -1050,6 +1100,13 @@ int launch_copy_chunks(const CopyArgs& a, void* stream) {
   const dim3 vgrid(unsigned(a.H * a.tps), a.n_chunks, a.n_layers);
   return a.D == 64 ? launch(copy_vt_kernel<64>, vgrid, dim3(256), &a, stream)
                    : launch(copy_vt_kernel<128>, vgrid, dim3(256), &a, stream);
+}
+
+int launch_stage_int8(const StageArgs& a, void* stream) {
+  if (a.n_chunks <= 0) return 0;
+  const dim3 grid(unsigned(a.H * a.tps), a.n_chunks);
+  return a.D == 64 ? launch(stage_int8_kernel<64>, grid, dim3(256), &a, stream)
+                   : launch(stage_int8_kernel<128>, grid, dim3(256), &a, stream);
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }

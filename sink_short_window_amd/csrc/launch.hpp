@@ -98,7 +98,29 @@ struct CopyArgs {
 };
 
 // Each returns 0 on success or the hipError_t code of the failed launch.
+// bf16 staging copy of an I8 layer's resident chunks for the attention: each
+// listed chunk (rows row0[i] .. + ctok of every head) is dequantised to
+// bf16(q * s) into K rows [H][rows][D] at dst_k (same row index) and V tiles
+// of chunk slot slot[i] at dst_v ([H][nslots*tps][D][64], key order and zero
+// padding as the BF16 cache stores V).
+struct StageArgs {
+  const char* layer = nullptr;  // I8 layer base
+  int64_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0;
+  char* dst_k = nullptr;
+  char* dst_v = nullptr;
+  int64_t rows = 0;
+  int64_t vt_head_elems = 0;
+  int32_t n_chunks = 0;
+  int32_t row0[kMaxSeg];
+  int32_t slot[kMaxSeg];
+  int32_t tps = 0;
+  int32_t ctok = 0;
+  int32_t H = 0;
+  int32_t D = 0;
+};
+
 int launch_attention(const AttnArgs& a, void* stream);
+int launch_stage_int8(const StageArgs& a, void* stream);
 int launch_attention_bwd(const AttnBwdArgs& a, void* stream);
 int launch_copy_chunks(const CopyArgs& a, void* stream);
 const char* hip_error_string(int err);

@@ -12,9 +12,11 @@ namespace ll {
 namespace {
 AttnArgs g_attn;
 AttnBwdArgs g_bwd;
+StageArgs g_stage;
 CopyArgs g_copy;
 int g_attn_calls = 0;
 int g_bwd_calls = 0;
+int g_stage_calls = 0;
 int g_copy_calls = 0;
 int g_fail_next = 0;
 }  // namespace
@@ -37,6 +39,16 @@ int launch_attention_bwd(const AttnBwdArgs& a, void*) {
   g_bwd = a;
   g_attn = a.a;  // the run table, readable through llh_last_attn
   ++g_bwd_calls;
+  return 0;
+}
+
+int launch_stage_int8(const StageArgs& a, void*) {
+  if (g_fail_next) {
+    g_fail_next = 0;
+    return 1;
+  }
+  g_stage = a;
+  ++g_stage_calls;
   return 0;
 }
 
@@ -103,6 +115,22 @@ int llh_last_bwd(int64_t* ptrs /* [delta, dq, dk, dv, out, dout, lse] */) {
   ptrs[5] = int64_t(reinterpret_cast<intptr_t>(b.dout));
   ptrs[6] = int64_t(reinterpret_cast<intptr_t>(b.lse));
   return b.dk != nullptr;
+}
+
+int llh_stage_calls(void) { return ll::g_stage_calls; }
+
+// Last int8 staging launch: n_chunks; row0/slot receive each chunk's first
+// row and chunk slot; bases receive [layer, dst_k, dst_v] as integers.
+int llh_last_stage(int32_t* row0, int32_t* slot, int64_t* bases) {
+  const ll::StageArgs& s = ll::g_stage;
+  for (int i = 0; i < s.n_chunks; ++i) {
+    row0[i] = s.row0[i];
+    slot[i] = s.slot[i];
+  }
+  bases[0] = int64_t(reinterpret_cast<intptr_t>(s.layer));
+  bases[1] = int64_t(reinterpret_cast<intptr_t>(s.dst_k));
+  bases[2] = int64_t(reinterpret_cast<intptr_t>(s.dst_v));
+  return s.n_chunks;
 }
 
 // Last copy launch: n_chunks, n_layers and the destination row of each chunk.

@@ -43,40 +43,46 @@ ll_status launched(int err, const char* what) {
 }
 
 // Key runs of a layer's cache, in the order the attention kernels walk them:
-// the sink (for a BF16 cache one run per sink chunk, each with its own slot of
-// V tiles; otherwise one run), then the resident ring chunks, oldest first.
-// Appends to a.seg and keys; returns the number of sink runs.
+// the sink (for a BF16 or I8 cache one run per sink chunk, each with its own
+// slot of V tiles; for F32 one run), then the resident ring chunks, oldest
+// first.  An I8 cache's runs point into its bf16 staging area (see
+// stage_int8).  Appends to a.seg and keys; returns the number of sink runs.
 int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int32_t& keys) {
   const ll::Geometry& g = cs.geom();
   const ll::Layout& lay = cs.layout();
-  const char* base = static_cast<const char*>(cs.buffer()) + lay.layer_bytes * size_t(layer);
+  const char* buf = static_cast<const char*>(cs.buffer());
+  const char* base = buf + lay.layer_bytes * size_t(layer);
   const size_t kelt = ll::dtype_bytes(g.kv);
-  const bool q8 = g.kv == LL_I8;
   auto add_cache_run = [&](int64_t row0, int64_t len) {
     ll::KvSeg& s = a.seg[a.n_seg++];
-    s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
-    s.ks = q8 ? reinterpret_cast<const float*>(base + lay.ks_off) + row0 : nullptr;
-    s.vs = q8 ? reinterpret_cast<const float*>(base + lay.vs_off) + row0 : nullptr;
+    s.ks = s.vs = nullptr;
     s.head_stride = g.rows * g.D;
     s.row_stride = g.D;
-    s.sc_head_stride = g.rows;
-    if (g.vt) {  // one chunk slot of the transposed tile layout
-      const int64_t slot = ll::slot_of_row(g, row0);
+    s.sc_head_stride = 0;
+    const int64_t slot = ll::slot_of_row(g, row0);
+    if (g.staged) {  // bf16 staging copy in the BF16 layout
+      s.k = buf + lay.stage_k_off + size_t(row0 * g.D) * 2;
+      s.v = buf + lay.stage_v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * 2;
+      s.v_head_stride = g.vt_head_elems;
+      s.v_tiled = 1;
+    } else if (g.vt) {  // one chunk slot of the transposed tile layout
+      s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
       s.v = base + lay.v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * kelt;
       s.v_head_stride = g.vt_head_elems;
       s.v_tiled = 1;
     } else {
+      s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
       s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
       s.v_head_stride = 0;
       s.v_tiled = 0;
     }
     s.key_start = keys;
     s.len = int32_t(len);
-    s.quant = q8 ? 1 : 0;
+    s.quant = 0;
     keys += int32_t(len);
   };
   const int64_t sink_rows = cs.sink_valid_rows(layer);
-  if (g.vt) {
+  if (g.vt || g.staged) {
     for (int64_t r0 = 0; r0 < sink_rows; r0 += g.ctok) add_cache_run(r0, g.ctok);
   } else if (sink_rows > 0) {
     add_cache_run(0, sink_rows);
@@ -84,6 +90,40 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
   const int n_sink = a.n_seg;
   for (int32_t slot : cs.resident_slots(layer)) add_cache_run(g.sink_rows + int64_t(slot) * g.ctok, g.ctok);
   return n_sink;
+}
+
+// An I8 cache is attended through a bf16 copy of the layer's resident chunks
+// (sink chunks and resident ring slots) in the staging area, dequantised to
+// bf16(q * s) by one launch per call: each code is converted once rather than
+// once per query tile, and the attention runs the bf16 kernel.  No-op for
+// other caches.
+int stage_int8(const ll::CacheState& cs, int32_t layer, void* stream) {
+  const ll::Geometry& g = cs.geom();
+  if (!g.staged) return 0;
+  const ll::Layout& lay = cs.layout();
+  char* buf = static_cast<char*>(cs.buffer());
+  ll::StageArgs s;
+  s.layer = buf + lay.layer_bytes * size_t(layer);
+  s.k_off = int64_t(lay.k_off);
+  s.v_off = int64_t(lay.v_off);
+  s.ks_off = int64_t(lay.ks_off);
+  s.vs_off = int64_t(lay.vs_off);
+  s.dst_k = buf + lay.stage_k_off;
+  s.dst_v = buf + lay.stage_v_off;
+  s.rows = g.rows;
+  s.vt_head_elems = g.vt_head_elems;
+  s.tps = g.tps;
+  s.ctok = int32_t(g.ctok);
+  s.H = g.H;
+  s.D = g.D;
+  auto add = [&](int64_t row0) {
+    s.row0[s.n_chunks] = int32_t(row0);
+    s.slot[s.n_chunks] = ll::slot_of_row(g, row0);
+    ++s.n_chunks;
+  };
+  for (int64_t r0 = 0; r0 < cs.sink_valid_rows(layer); r0 += g.ctok) add(r0);
+  for (int32_t slot : cs.resident_slots(layer)) add(g.sink_rows + int64_t(slot) * g.ctok);
+  return ll::launch_stage_int8(s, stream);
 }
 
 // The caller's current chunk (token-major [n_cur][H][D]) as the last run.
@@ -343,8 +383,9 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   a.H = g.H;
   a.D = g.D;
   a.act = g.act;
-  a.kv = g.kv;
+  a.kv = g.staged ? LL_BF16 : g.kv;
   a.scale = scale;
+  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "attention launch");
 }
 
@@ -426,10 +467,11 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
   a.H = g.H;
   a.D = g.D;
   a.act = g.act;
-  a.kv = g.kv;
+  a.kv = g.staged ? LL_BF16 : g.kv;
   a.scale = scale;
   a.q_chunk = int32_t(g.ctok);
   a.n_seg0 = n_sink + 1;
+  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "re-encoding attention launch");
 }
 

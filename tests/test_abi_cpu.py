@@ -35,6 +35,8 @@ def libs():
     stub.llh_last_copy_vt.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     stub.llh_last_attn_chunks.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     stub.llh_last_bwd.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    stub.llh_last_stage.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int64)]
     return stub
 
 
@@ -93,6 +95,7 @@ def status(stub, st):
     (dict(act=ll.LL_I8, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
     (dict(act=ll.LL_F32, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),
     (dict(C=1, S=10, W=31), "LL_ERR_UNSUPPORTED"),   # bf16: 10 sink chunks + 30 slots + current > 40 runs
+    (dict(C=1, S=10, W=31, kv=ll.LL_I8), "LL_ERR_UNSUPPORTED"),  # int8 is attended through a bf16 copy
 ])
 def test_config_rejected(libs, bad, code):
     n = ctypes.c_size_t(123)
@@ -102,11 +105,14 @@ def test_config_rejected(libs, bad, code):
     assert n.value == 123
 
 
-def test_many_runs_fine_for_int8_cache(libs):
-    """Only the BF16 cache walks each sink chunk as its own run."""
+def test_many_runs_fine_for_fp32_cache(libs):
+    """BF16 and I8 caches walk each sink chunk as its own run; F32 keeps the
+    sink as one run."""
     n = ctypes.c_size_t(0)
-    assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=10, W=31, kv=ll.LL_I8)), ctypes.byref(n)) == 0
-    assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=9, W=31)), ctypes.byref(n)) == 0
+    assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=10, W=31, act=ll.LL_F32, kv=ll.LL_F32)),
+                                        ctypes.byref(n)) == 0
+    for kv in (ll.LL_BF16, ll.LL_I8):
+        assert libs.ll_cache_required_bytes(ctypes.byref(cfg(C=1, S=9, W=31, kv=kv)), ctypes.byref(n)) == 0
 
 
 def _align(x):
@@ -128,7 +134,11 @@ def test_required_bytes_matches_layout(libs, kw):
     else:
         vb = kb
     scb = _align(H * rows * 4) if c.kv_dtype == ll.LL_I8 else 0
-    assert ll.ll_cache_required_bytes(c, lib=libs) == L * max(kb + vb + 2 * scb, 256)
+    stage = 0
+    if c.kv_dtype == ll.LL_I8:        # one layer's bf16 staging copy: K rows + V tiles
+        slots = S // C + (W - C) // C
+        stage = _align(H * rows * D * 2) + _align(H * slots * tiles_per_slot(C * T) * VT_KEYS * D * 2)
+    assert ll.ll_cache_required_bytes(c, lib=libs) == L * max(kb + vb + 2 * scb, 256) + stage
     if kw.get("L") == 30:     # the paper-shaped 30-layer bf16 cache: 3 slots of 74 tiles for V
         assert ll.ll_cache_required_bytes(c, lib=libs) == 30 * (12 * 14040 * 128 * 2 + 12 * 3 * 74 * 64 * 128 * 2)
 
@@ -337,9 +347,21 @@ def test_reencode_runs_are_sink_then_window_oldest_first(libs, T, C, S, W, act, 
             n_seg0 = ctypes.c_int32()
             assert libs.llh_last_attn_chunks(ctypes.byref(n_seg0)) == ct
             chunks_of_run = []
+            k0, esz = FAKE_BUF + k_sink_off, elt
+            if kv == ll.LL_I8:   # runs read the bf16 staging copy the call launched first
+                row0 = (ctypes.c_int32 * 40)()
+                slot = (ctypes.c_int32 * 40)()
+                bases = (ctypes.c_int64 * 3)()
+                n_st = libs.llh_last_stage(row0, slot, bases)
+                want_rows = [j * ct for j in range(g.sink_chunks)] + \
+                    [S * T + s_ * ct for s_ in sorted(range(g.ring_slots), key=lambda x: sim.slot_chunk[x])
+                     if sim.slot_chunk[s_] >= 0]
+                assert list(row0[:n_st]) == want_rows
+                assert bases[0] == FAKE_BUF + k_sink_off and bases[1] > bases[0]
+                k0, esz = bases[1], 2
             for i in range(n_seg):
                 kp, ln = runs[RUN_FIELDS * i], runs[RUN_FIELDS * i + 5]
-                row = (kp - FAKE_BUF - k_sink_off) // (elt * D)
+                row = (kp - k0) // (esz * D)
                 if row < S * T:
                     chunks_of_run.append(list(range(row // ct, (row + ln) // ct)))
                 else:
