@@ -1,6 +1,7 @@
 // HIP kernels for gfx950 (MI355X): sink + short-window attention (also used
-// for text cross-attention) and the cache chunk writers (append / recache,
-// copy or int8 quantise).
+// for text cross-attention and the re-encoding pass of a recache), the cache
+// chunk writers (append / recache, copy or int8 quantise) and the bf16
+// staging of an int8 cache for the attention.
 //
 // Attention (LongLive: Real-time Interactive Long Video Generation, §3.3):
 // one softmax over the union of the frame-sink tokens, the resident window
@@ -26,13 +27,13 @@
 //                            accumulators; A = V^T: for the bf16 cache, whose
 //                            V is stored transposed in 64-key tiles, a plain
 //                            16-byte LDS read; for row-major V (the caller's
-//                            current chunk, text K/V, the int8 cache) the
-//                            gfx950 transpose read (ds_read_b64_tr_b16).
+//                            current chunk, text K/V) the gfx950 transpose
+//                            read (ds_read_b64_tr_b16).
 // The two halves of the workgroup alternate between an MFMA phase and a
 // softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
-// direct-to-LDS buffer loads, or, for int8 runs, through registers where
-// each code is dequantised with its token's scale (q * s in fp32, then bf16)
-// before it is written to LDS, so the MFMA and softmax are those of bf16.
+// direct-to-LDS buffer loads.  An int8 cache is read through a bf16 staging
+// copy in the bf16 cache's layout (stage_int8_kernel, one launch per call:
+// every code becomes bf16(q * s) once, not once per query tile).
 // fp32 activations use a plainer kernel with the fp32 MFMA 32x32x2.
 
 #include <hip/hip_runtime.h>
@@ -126,7 +127,7 @@ __device__ __forceinline__ QueryTile query_tile(const AttnArgs& a, int qtile, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 activations (bf16 or int8 cache)
+// bf16 activations
 // ---------------------------------------------------------------------------
 
 // ---------------------------------------------------------------------------
@@ -143,8 +144,7 @@ __device__ __forceinline__ QueryTile query_tile(const AttnArgs& a, int qtile, in
 // operand reads of 32 consecutive rows spread over the banks.  bf16 tiles are
 // loaded straight from memory into LDS (buffer_load ... lds): at the start of
 // its softmax phase t group A loads K(t+3) and group B V(t+3), three tiles
-// ahead.  The int8 kernel stages through registers instead (load tile t+3,
-// convert and store tile t+2 during V(t)).
+// ahead.
 // ---------------------------------------------------------------------------
 constexpr int kPPWaves = 8;
 constexpr int kPPThreads = 64 * kPPWaves;
@@ -206,10 +206,9 @@ struct RunCursor {
   int run;
   int tile;
   int len;
-  int quant;
   int vt;       // V of this run in transposed 64-key tiles
   uint32_t rs;  // row stride in bytes
-  __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
+  __amdgpu_buffer_rsrc_t rk, rv;
 
   // Every field is uniform across the workgroup; readfirstlane says so to the
   // compiler, which keeps the descriptors in scalar registers (a descriptor
@@ -226,9 +225,8 @@ struct RunCursor {
     tile = 0;
     if (r >= a.n_seg) return;
     const KvSeg& s = a.seg[r];
-    quant = __builtin_amdgcn_readfirstlane(s.quant);
     len = __builtin_amdgcn_readfirstlane(s.len);
-    const int elt = quant ? 1 : 2;
+    constexpr int elt = 2;  // bf16
     rs = __builtin_amdgcn_readfirstlane(uint32_t(s.row_stride) * elt);
     const int64_t hoff = int64_t(head) * s.head_stride * elt;
     rk = make_rsrc(uni(static_cast<const char*>(s.k) + hoff), uint32_t(len) * rs);
@@ -239,10 +237,6 @@ struct RunCursor {
       rv = make_rsrc(uni(static_cast<const char*>(s.v) + int64_t(head) * s.v_head_stride * elt), tiles * kBN * rs);
     } else {
       rv = make_rsrc(uni(static_cast<const char*>(s.v) + hoff), uint32_t(len) * rs);
-    }
-    if (quant) {
-      rks = make_rsrc(uni(s.ks + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
-      rvs = make_rsrc(uni(s.vs + int64_t(head) * s.sc_head_stride), uint32_t(len) * 4);
     }
   }
   __device__ void advance(const AttnArgs& a, int head) {
@@ -291,45 +285,6 @@ __device__ __forceinline__ void dma_vt(const RunCursor& c, __bf16* tile_base, in
   }
 }
 
-// Register staging for the int8 kernel: each thread owns kItems 8-element
-// vectors of K and of V (16 bytes of bf16, or 8 bytes of int8 in the low two
-// words plus the row's fp32 scale).
-template <int D>
-struct PPRegs {
-  static constexpr int kVec = D / 8;
-  static constexpr int kItems = kBN * kVec / kPPThreads;
-  u32x4 k[kItems];
-  u32x4 v[kItems];
-  float ks[kItems], vs[kItems];
-  bool q8;
-};
-
-template <int D>
-__device__ __forceinline__ void pp_load(const RunCursor& c, PPRegs<D>& r) {
-  using R = PPRegs<D>;
-  const int tid = threadIdx.x;
-  const int row0 = c.tile * kBN;
-  const bool q8 = c.quant;
-#pragma unroll
-  for (int it = 0; it < R::kItems; ++it) {
-    const int item = tid + it * kPPThreads;
-    const int row = item / R::kVec, vec = item % R::kVec;
-    const uint32_t off = uint32_t(row0 + row) * c.rs;
-    if (q8) {
-      const u32x2 kq = __builtin_amdgcn_raw_buffer_load_b64(c.rk, off + vec * 8, 0, 0);
-      const u32x2 vq = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off + vec * 8, 0, 0);
-      r.k[it] = u32x4{kq[0], kq[1], 0, 0};
-      r.v[it] = u32x4{vq[0], vq[1], 0, 0};
-      r.ks[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rks, uint32_t(row0 + row) * 4, 0, 0));
-      r.vs[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rvs, uint32_t(row0 + row) * 4, 0, 0));
-    } else {
-      r.k[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rk, off + vec * 16, 0, 0);
-      r.v[it] = __builtin_amdgcn_raw_buffer_load_b128(c.rv, off + vec * 16, 0, 0);
-    }
-  }
-  r.q8 = q8;
-}
-
 // 8 int8 codes q (two words) -> 8 bf16 of q * s.  Each byte is read as the
 // unsigned u = q + 128 (sign bit flipped), so (u - 128) * s is one fma.
 __device__ __forceinline__ u32x4 int8x8_dequant_bf16x8(u32x2 w, float s) {
@@ -344,24 +299,6 @@ __device__ __forceinline__ u32x4 int8x8_dequant_bf16x8(u32x2 w, float s) {
     o[2 * h + 1] = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf16x2));
   }
   return o;
-}
-
-template <int D>
-__device__ __forceinline__ void pp_store(SwzStage<D>& st, const PPRegs<D>& r) {
-  using R = PPRegs<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < R::kItems; ++it) {
-    const int item = tid + it * kPPThreads;
-    const int row = item / R::kVec, vec = item % R::kVec;
-    u32x4 kw = r.k[it], vw = r.v[it];
-    if (r.q8) {
-      kw = int8x8_dequant_bf16x8(u32x2{kw[0], kw[1]}, r.ks[it]);
-      vw = int8x8_dequant_bf16x8(u32x2{vw[0], vw[1]}, r.vs[it]);
-    }
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.k) + k_swz<D>(row, vec)) = kw;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(st.v) + v_swz<D>(row, vec)) = vw;
-  }
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
@@ -436,7 +373,7 @@ __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool kQ8, bool kOneRun>
+template <int D, bool kOneRun>
 __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   using S = SwzStage<D>;
   constexpr int kLoads = 16 / S::kRowsPerLoad;  // DMA loads per wave per tile side
@@ -526,34 +463,16 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   if (n == 0) return;
   // tiles of the leading runs whose V is in transposed tiles
   int n_vt = 0;
-  if constexpr (!kQ8) {
-    for (int r = 0; r < n_seg && a.seg[r].v_tiled; ++r) n_vt += (a.seg[r].len + kBN - 1) / kBN;
-    n_vt = __builtin_amdgcn_readfirstlane(n_vt);
-  }
+  for (int r = 0; r < n_seg && a.seg[r].v_tiled; ++r) n_vt += (a.seg[r].len + kBN - 1) / kBN;
+  n_vt = __builtin_amdgcn_readfirstlane(n_vt);
   RunCursor cu;  // tile being softmaxed (masking)
   cu.open(a, head, 0);
-  RunCursor ld;  // int8 kernel: next tile to stage; bf16: next K tile (group A) / V tile (group B)
+  RunCursor ld;  // next K tile (group A) / V tile (group B) to load
   ld.open(a, head, 0);
-  PPRegs<D> regs;
 
-  // Prologue.
-  if constexpr (kQ8) {
-    // tiles 0, 1 into stages 0, 1; tile 2 into registers
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if (p < n) {
-        pp_load<D>(ld, regs);
-        ld.advance(a, head);
-        pp_store<D>(stage[p], regs);
-      }
-    }
-    if (n > 2) {
-      pp_load<D>(ld, regs);
-      ld.advance(a, head);
-    }
-  } else {
-    // group A loads K(0..2), group B V(0..2); A waits for K(0) (B waits for
-    // V(0) after its first MFMA phase)
+  // Prologue: group A loads K(0..2), group B V(0..2); A waits for K(0) (B
+  // waits for V(0) after its first MFMA phase).
+  {
     const int pre = min(n, 3);
     for (int j = 0; j < pre; ++j) {
       if (group == 0) dma_rows<D>(ld, false, stage[j].k, 16 * wq, lane);
@@ -579,33 +498,20 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // outstanding LDS-DMA loads, and the compiler puts a full wait before each
   // transpose read, so loads issued any earlier would only stall the reads.)
   auto after_mfma = [&](int t) {
-    if constexpr (!kQ8) {
-      if (group == 1) {
-        if (t + 2 < n) wait_vmcnt<2 * kLoads>();
-        else if (t + 1 < n) wait_vmcnt<kLoads>();
-        else wait_vmcnt<0>();
-      }
+    if (group == 1) {
+      if (t + 2 < n) wait_vmcnt<2 * kLoads>();
+      else if (t + 1 < n) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
     }
   };
 
   // Softmax phase t: online softmax of S(t) -> P(t).
   auto softmax_phase = [&](int t) {
-    if constexpr (!kQ8) {
-      if (t + 3 < n) {  // A: K(t+3), B: V(t+3), straight into LDS
-        if (group == 0) dma_rows<D>(ld, false, stage[(t + 3) % kPPStages].k, 16 * wq, lane);
-        else if (ld.vt) dma_vt<D>(ld, stage[(t + 3) % kPPStages].v, wq, lane);
-        else dma_rows<D>(ld, true, stage[(t + 3) % kPPStages].v, 16 * wq, lane);
-        ld.advance(a, head);
-      }
-    } else {
-      // stage tile t+2 (in registers since V(t-1)) and start loading tile t+3
-      if (t + 2 < n) {
-        pp_store<D>(stage[(t + 2) % kPPStages], regs);
-        if (t + 3 < n) {
-          pp_load<D>(ld, regs);
-          ld.advance(a, head);
-        }
-      }
+    if (t + 3 < n) {  // A: K(t+3), B: V(t+3), straight into LDS
+      if (group == 0) dma_rows<D>(ld, false, stage[(t + 3) % kPPStages].k, 16 * wq, lane);
+      else if (ld.vt) dma_vt<D>(ld, stage[(t + 3) % kPPStages].v, wq, lane);
+      else dma_rows<D>(ld, true, stage[(t + 3) % kPPStages].v, 16 * wq, lane);
+      ld.advance(a, head);
     }
     const int valid = min(kBN, cu.len - cu.tile * kBN);
     cu.advance(a, head);
@@ -679,13 +585,11 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       lt = form_p();
     }
     l_run += lt;
-    if constexpr (!kQ8) {
-      // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
-      if (group == 0) {
-        if (t + 3 < n) wait_vmcnt<2 * kLoads>();
-        else if (t + 2 < n) wait_vmcnt<kLoads>();
-        else wait_vmcnt<0>();
-      }
+    // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
+    if (group == 0) {
+      if (t + 3 < n) wait_vmcnt<2 * kLoads>();
+      else if (t + 2 < n) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
     }
   };
 
@@ -709,7 +613,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int t1 = min(n_vt + 1, n);
   for (int t = 1; t < t1; ++t) {  // PV of tile t-1 < n_vt: transposed V
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase<D, true, true, !kQ8>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+    mfma_phase<D, true, true, true>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -726,7 +630,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     wg_barrier();
   }
   __builtin_amdgcn_s_setprio(1);
-  if (n - 1 < n_vt) mfma_phase<D, false, true, !kQ8>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+  if (n - 1 < n_vt) mfma_phase<D, false, true, true>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
   else mfma_phase<D, false, true, false>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(n);
@@ -1072,9 +976,8 @@ int launch_attention_d(const AttnArgs& args, void* stream) {
   }
   const dim3 grid(query_tiles(a, kPPBM), a.H);
   const dim3 block(kPPThreads);
-  if (a.kv == LL_I8) return launch(attn_pp_kernel<D, true, false>, grid, block, &a, stream);
-  if (a.n_seg == 1) return launch(attn_pp_kernel<D, false, true>, grid, block, &a, stream);
-  return launch(attn_pp_kernel<D, false, false>, grid, block, &a, stream);
+  if (a.n_seg == 1) return launch(attn_pp_kernel<D, true>, grid, block, &a, stream);
+  return launch(attn_pp_kernel<D, false>, grid, block, &a, stream);
 }
 
 }  // namespace

@@ -13,20 +13,16 @@ namespace ll {
 // elements, and likewise V unless v_tiled.  A v_tiled run (bf16 cache) keeps
 // V transposed in 64-key tiles: element (h, i, d) at
 // v + h*v_head_stride + (i/64)*64*D + d*64 + p, where p is i%64 with bits 2
-// and 3 swapped (the key order of the PV operand).  For int8 runs, the scale
-// of key i is at ks[h*sc_head_stride + i].
+// and 3 swapped (the key order of the PV operand).  Elements are of the
+// activation dtype (an I8 cache is attended through its bf16 staging copy).
 struct KvSeg {
   const void* k;
   const void* v;
-  const float* ks;  // int8 runs only
-  const float* vs;
   int64_t head_stride;     // elements
   int64_t row_stride;      // elements
-  int64_t sc_head_stride;  // floats
   int64_t v_head_stride;   // elements, v_tiled runs
   int32_t key_start;       // first key index of the run in the joint key space
   int32_t len;             // keys in the run
-  int32_t quant;           // 1: int8 with scales, 0: activation dtype
   int32_t v_tiled;         // 1: V in transposed 64-key tiles (see above)
 };
 
@@ -42,8 +38,7 @@ struct AttnArgs {
   int32_t n_q = 0;
   int32_t H = 0;
   int32_t D = 0;
-  int32_t act = LL_BF16;    // dtype of q/out and of non-quantised runs
-  int32_t kv = LL_BF16;     // LL_I8 when some runs are int8
+  int32_t act = LL_BF16;    // dtype of q/out and of every run
   float scale = 1.f;
   // Chunk-causal queries (re-encoding pass of a KV-recache): with q_chunk > 0
   // the n_q queries are chunks of q_chunk tokens and chunk r attends only the

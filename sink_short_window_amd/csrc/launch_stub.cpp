@@ -73,23 +73,22 @@ int llh_attn_calls(void) { return ll::g_attn_calls; }
 int llh_copy_calls(void) { return ll::g_copy_calls; }
 
 // Last attention launch: n_seg, n_keys, and per run [k, v, head_stride,
-// row_stride, key_start, len, quant, v_head_stride, v_tiled] (pointers as
+// row_stride, key_start, len, v_head_stride, v_tiled] (pointers as
 // integers).
-int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][9] */) {
+int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][8] */) {
   const ll::AttnArgs& a = ll::g_attn;
   *n_keys = a.n_keys;
   for (int i = 0; i < a.n_seg; ++i) {
     const ll::KvSeg& s = a.seg[i];
-    int64_t* r = runs + 9 * i;
+    int64_t* r = runs + 8 * i;
     r[0] = int64_t(reinterpret_cast<intptr_t>(s.k));
     r[1] = int64_t(reinterpret_cast<intptr_t>(s.v));
     r[2] = s.head_stride;
     r[3] = s.row_stride;
     r[4] = s.key_start;
     r[5] = s.len;
-    r[6] = s.quant;
-    r[7] = s.v_head_stride;
-    r[8] = s.v_tiled;
+    r[6] = s.v_head_stride;
+    r[7] = s.v_tiled;
   }
   return a.n_seg;
 }

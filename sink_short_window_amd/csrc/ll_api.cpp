@@ -55,10 +55,8 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
   const size_t kelt = ll::dtype_bytes(g.kv);
   auto add_cache_run = [&](int64_t row0, int64_t len) {
     ll::KvSeg& s = a.seg[a.n_seg++];
-    s.ks = s.vs = nullptr;
     s.head_stride = g.rows * g.D;
     s.row_stride = g.D;
-    s.sc_head_stride = 0;
     const int64_t slot = ll::slot_of_row(g, row0);
     if (g.staged) {  // bf16 staging copy in the BF16 layout
       s.k = buf + lay.stage_k_off + size_t(row0 * g.D) * 2;
@@ -78,7 +76,6 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
     }
     s.key_start = keys;
     s.len = int32_t(len);
-    s.quant = 0;
     keys += int32_t(len);
   };
   const int64_t sink_rows = cs.sink_valid_rows(layer);
@@ -132,15 +129,12 @@ void add_current_run(const ll::Geometry& g, const void* k_cur, const void* v_cur
   ll::KvSeg& s = a.seg[a.n_seg++];
   s.k = k_cur;
   s.v = v_cur;
-  s.ks = s.vs = nullptr;
   s.head_stride = g.D;
   s.row_stride = int64_t(g.H) * g.D;
-  s.sc_head_stride = 0;
   s.v_head_stride = 0;
   s.v_tiled = 0;
   s.key_start = keys;
   s.len = int32_t(n_cur);
-  s.quant = 0;
   keys += int32_t(n_cur);
 }
 
@@ -383,7 +377,6 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   a.H = g.H;
   a.D = g.D;
   a.act = g.act;
-  a.kv = g.staged ? LL_BF16 : g.kv;
   a.scale = scale;
   if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "attention launch");
@@ -427,7 +420,6 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
   b.a.H = g.H;
   b.a.D = g.D;
   b.a.act = g.act;
-  b.a.kv = g.kv;
   b.a.scale = scale;
   b.out = out;
   b.dout = dout;
@@ -467,7 +459,6 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
   a.H = g.H;
   a.D = g.D;
   a.act = g.act;
-  a.kv = g.staged ? LL_BF16 : g.kv;
   a.scale = scale;
   a.q_chunk = int32_t(g.ctok);
   a.n_seg0 = n_sink + 1;
@@ -497,15 +488,12 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   ll::KvSeg& s = a.seg[0];
   s.k = k_txt;
   s.v = v_txt;
-  s.ks = s.vs = nullptr;
   s.head_stride = head_dim;
   s.row_stride = int64_t(num_heads) * head_dim;
-  s.sc_head_stride = 0;
   s.v_head_stride = 0;
   s.v_tiled = 0;
   s.key_start = 0;
   s.len = int32_t(n_txt);
-  s.quant = 0;
   a.n_seg = 1;
   a.n_keys = int32_t(n_txt);
   a.q = q;
@@ -515,7 +503,6 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   a.H = num_heads;
   a.D = head_dim;
   a.act = dtype;
-  a.kv = dtype;
   a.scale = scale;
   return launched(ll::launch_attention(a, stream), "cross-attention launch");
 }

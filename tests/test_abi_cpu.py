@@ -40,7 +40,7 @@ def libs():
     return stub
 
 
-RUN_FIELDS = 9   # llh_last_attn: k, v, head_stride, row_stride, key_start, len, quant, v_head_stride, v_tiled
+RUN_FIELDS = 8   # llh_last_attn: k, v, head_stride, row_stride, key_start, len, v_head_stride, v_tiled
 VT_KEYS = 64
 
 
@@ -287,8 +287,8 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
                 covered = []
                 start = 0
                 for i in range(n_seg):
-                    kp, vp, hs, rs, ks, ln, q, vhs, vtl = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
-                    assert ks == start and ln > 0 and q == 0
+                    kp, vp, hs, rs, ks, ln, vhs, vtl = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
+                    assert ks == start and ln > 0
                     start += ln
                     if kp == FAKE_ACT:                 # current chunk, token-major
                         assert i == n_seg - 1 and ln == ct and vp == FAKE_ACT
@@ -461,7 +461,7 @@ def test_attention_and_cross_attention_errors(libs):
     nk = ctypes.c_int64()
     runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
     assert libs.llh_last_attn(ctypes.byref(nk), runs) == 1 and nk.value == 3
-    assert tuple(runs[2:4]) == (64, 128) and runs[8] == 0
+    assert tuple(runs[2:4]) == (64, 128) and runs[7] == 0
     libs.ll_cache_destroy(h)
 
 
