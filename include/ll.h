@@ -84,9 +84,9 @@ typedef enum { LL_SEG_SINK = 0, LL_SEG_RING = 1 } ll_segment;
  * fp32 scale per (token, head): s = max|x|/127 (IEEE fp32 division),
  * q = clamp(round_half_even(x/s), -127, 127), s = 0 and q = 0 for an all-zero
  * vector.  (The paper reports INT8 inference without giving a scheme; this
- * per-token, per-head KV scheme is this library's own.)  With kv_dtype BF16
- * every sink chunk and ring slot is its own key run: at most 39 of them.  One
- * chunk of activations ([C_tok][H][D]) must be smaller than 4 GiB.
+ * per-token, per-head KV scheme is this library's own.)  With kv_dtype BF16 or
+ * I8 every sink chunk and ring slot is its own key run: at most 39 of them.
+ * One chunk of activations ([C_tok][H][D]) must be smaller than 4 GiB.
  */
 typedef struct {
   int32_t num_layers;
@@ -100,7 +100,9 @@ typedef struct {
   int32_t kv_dtype;      /* ll_dtype of the cached K/V */
 } ll_cache_config;
 
-/* Device bytes the cache needs for `cfg` (all layers), written to *bytes. */
+/* Device bytes the cache needs for `cfg` (all layers), written to *bytes.  An
+ * I8 cache also holds one layer's bf16 staging area, which every attention
+ * call on the cache rewrites from the layer's codes before reading it. */
 ll_status ll_cache_required_bytes(const ll_cache_config* cfg, size_t* bytes);
 
 /*
@@ -153,8 +155,10 @@ ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const 
  *   lse:    nullable float [H][n_q]: natural-log sum of exp(scale * q.k).
  * Accumulation is fp32 (bf16 MFMA products for BF16 activations).  The scale
  * is folded into the queries before their bf16 rounding.  With an I8 cache
- * each stored code is dequantised inside the kernel to bf16(q * s) (s the
- * token's fp32 scale); the current chunk is used as given.
+ * the call first dequantises the layer's resident codes to bf16(q * s) (s the
+ * token's fp32 scale) into the cache's staging area, one extra launch on the
+ * same stream, and attends over that copy; the current chunk is used as
+ * given.
  * LL_ERR_BAD_STATE if the key set is empty.
  */
 ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
