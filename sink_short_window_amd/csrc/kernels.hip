@@ -396,24 +396,16 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
 
-  // Q fragment with the logit scale folded in: Q' = bf16(Q * scale * log2 e),
-  // so the MFMA yields scores in log2 units.
-  bf16x8 qf[D / 16];
+  // The wave's queries, raw; converted to the MFMA fragment once the first
+  // K/V tiles' loads are in flight, so the two memory latencies overlap.
+  // (They are issued before any LDS-DMA load, so every vmcnt wait below that
+  // covers a tile also covers them.)
+  u32x4 qw[D / 16];
   {
     const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const u32x4 w = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
-      f32x8 f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __builtin_bit_cast(float, w[i] << 16) * c;
-        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u) * c;
-      }
-      qf[j] = __builtin_convertvector(f, bf16x8);
-    }
+    for (int j = 0; j < D / 16; ++j) qw[j] = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
   }
-  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -485,6 +477,19 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       else if (pre == 2) wait_vmcnt<kLoads>();
       else wait_vmcnt<0>();
     }
+  }
+  // Q fragment with the logit scale folded in: Q' = bf16(Q * scale * log2 e),
+  // so the MFMA yields scores in log2 units.
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    f32x8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, qw[j][i] << 16) * c;
+      f[2 * i + 1] = __builtin_bit_cast(float, qw[j][i] & 0xffff0000u) * c;
+    }
+    qf[j] = __builtin_convertvector(f, bf16x8);
   }
   wg_barrier();
   if (group == 1) wg_barrier();  // group B runs one interval behind
