@@ -28,10 +28,13 @@
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
 //
-// Tiles reach LDS through registers into rows padded by 16 bytes.  In the dQ
-// kernel V stays transposed ([D][64] per 64 keys, as the bf16 cache stores
-// it; the caller's row-major current chunk is transposed while staged) and
-// its rows are read back with transpose reads.
+// Tiles reach LDS through registers.  Rows of K, Q' and dO tiles are padded
+// by 32 bytes, to a stride of 8 (mod 64) dwords, so the 4 rows x 8 bytes a
+// transpose read gathers per 16 lanes land in distinct banks (the 16-byte row
+// reads stay conflict-free too); the transposed V tile's 144-byte rows have
+// the same property.  In the dQ kernel V stays transposed ([D][64] per 64
+// keys, as the bf16 cache stores it; the caller's row-major current chunk is
+// transposed while staged) and its rows are read back with transpose reads.
 
 #include <hip/hip_runtime.h>
 
@@ -85,14 +88,14 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(u32x4 w, float c) {
 // involution the forward kernel's PV operand order asks for).
 __device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
-// Byte offsets (within a [kTile][D+8] bf16 LDS tile) of the two transpose
+// Byte offsets (within a [kTile][D+16] bf16 LDS tile) of the two transpose
 // reads that give lane (r32, half) the A operand of a 32x32x16 MFMA whose
 // rows are the tile's columns 32*db + r32 and whose 16 k values are tile rows
 // 16*step + {0..3, 8..11} (half 0) or {4..7, 12..15} (half 1): the row order
 // in which the C accumulator of the previous MFMA packs into a B operand.
 template <int D>
 __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
-  constexpr int RB = (D + 8) * 2;
+  constexpr int RB = (D + 16) * 2;
   const int g16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa)
@@ -106,7 +109,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
 
 template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int step, const int (&off)[2][D / 32], int db) {
-  constexpr int RB = (D + 8) * 2;
+  constexpr int RB = (D + 16) * 2;
   const char* base = tile + 16 * step * RB;
   const bf16x4 lo = tr_read(base + off[0][db]);
   const bf16x4 hi = tr_read(base + off[1][db]);
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
-  constexpr int RB = (D + 8) * 2;  // LDS row bytes of K rows
+  constexpr int RB = (D + 16) * 2;  // LDS row bytes of K rows
   constexpr int VRB = (kTile + 8) * 2;  // LDS row bytes of the transposed V tile
   constexpr int NV = D / 8;        // 16-byte vectors per row
   // two LDS buffers: tile t is read from one while tile t+1 is written to the other
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
-  constexpr int RB = (D + 8) * 2;
+  constexpr int RB = (D + 16) * 2;
   constexpr int NV = D / 8;
   __shared__ __attribute__((aligned(16))) char qs[kTile * RB];   // Q' rows
   __shared__ __attribute__((aligned(16))) char gs[kTile * RB];   // dO rows
