@@ -28,12 +28,10 @@
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
 //
-// Tiles reach LDS through registers.  Rows of K, Q' and dO tiles are padded
-// by 32 bytes, to a stride of 8 (mod 64) dwords, so the 4 rows x 8 bytes a
-// transpose read gathers per 16 lanes land in distinct banks (the 16-byte row
-// reads stay conflict-free too); the transposed V tile's 144-byte rows have
-// the same property.  In the dQ kernel V stays transposed ([D][64] per 64
-// keys, as the bf16 cache stores it; the caller's row-major current chunk is
+// Tiles reach LDS through registers, in layouts (RowTile, VtTile) whose XOR
+// swizzles keep both the 16-byte row reads and the transpose reads free of
+// bank conflicts.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
+// as the bf16 cache stores it; the caller's row-major current chunk is
 // transposed while staged) and its rows are read back with transpose reads.
 
 #include <hip/hip_runtime.h>
@@ -88,14 +86,47 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(u32x4 w, float c) {
 // involution the forward kernel's PV operand order asks for).
 __device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
-// Byte offsets (within a [kTile][D+16] bf16 LDS tile) of the two transpose
+// Row-major [kTile][D] bf16 LDS tile (K, Q' or dO), read both as rows
+// (16-byte reads, 16 consecutive rows at one granule) and by transpose reads
+// (per 32 lanes: 4 consecutive rows x 4 granules).  For D = 128 rows are 256
+// bytes and granule g of row r is stored at g ^ f(r), f(r) = ((r & 3) << 2) |
+// ((r >> 2) & 3), a rotation of r mod 16: both patterns then cover 16
+// distinct granules, i.e. all 64 banks.  Otherwise (D = 64, or a kernel
+// whose registers cannot spare the per-read address arithmetic) rows are
+// padded by 32 bytes, to a stride of 8 (mod 64) dwords, which keeps the
+// transpose reads conflict-free within 16 lanes.
+template <int D, bool kSwzOn = true>
+struct RowTile {
+  static constexpr bool kSwz = kSwzOn && D == 128;
+  static constexpr int RB = kSwz ? D * 2 : (D + 16) * 2;
+  static constexpr int kBytes = kTile * RB;
+  static __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+  static __device__ __forceinline__ int off(int row, int gran) {
+    if constexpr (kSwz) return row * RB + ((gran ^ swz(row)) << 4);
+    else return row * RB + gran * 16;
+  }
+};
+
+// Transposed [D][64] bf16 V tile of the dQ kernel, read by transpose reads
+// only (per 32 lanes: 4 consecutive rows d, two of each parity).  Rows are
+// 128 bytes; granule g of row d is stored at g ^ (((d >> 1) & 1) << 2) so the
+// two rows of one parity fall in different halves of their 32 banks.
+template <int D>
+struct VtTile {
+  static constexpr int RB = kTile * 2;
+  static constexpr int kBytes = D * RB;
+  static __device__ __forceinline__ int off(int d, int gran) { return d * RB + ((gran ^ (((d >> 1) & 1) << 2)) << 4); }
+};
+
+// Byte offsets (within a RowTile) of the two transpose
 // reads that give lane (r32, half) the A operand of a 32x32x16 MFMA whose
 // rows are the tile's columns 32*db + r32 and whose 16 k values are tile rows
 // 16*step + {0..3, 8..11} (half 0) or {4..7, 12..15} (half 1): the row order
 // in which the C accumulator of the previous MFMA packs into a B operand.
-template <int D>
+// (The swizzle depends on row mod 16 only, so the offsets of rows 0..15 serve
+// every 16-row step.)
+template <int D, typename T>
 __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
-  constexpr int RB = (D + 16) * 2;
   const int g16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa)
@@ -103,13 +134,20 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
     for (int db = 0; db < D / 32; ++db) {
       const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
       const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
-      off[aa][db] = row * RB + col * 2;
+      if constexpr (T::kSwz) off[aa][db] = T::off(row, col >> 3) + (col & 7) * 2;
+      else off[aa][db] = row * T::RB + col * 2;  // (this form keeps the compiler from spilling)
     }
 }
 
-template <int D>
+// 16-byte read of granule gran of row `row` of a RowTile.
+template <typename T>
+__device__ __forceinline__ bf16x8 row_read(const char* tile, int row, int gran) {
+  return *reinterpret_cast<const bf16x8*>(tile + T::off(row, gran));
+}
+
+template <int D, typename T>
 __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int step, const int (&off)[2][D / 32], int db) {
-  constexpr int RB = (D + 16) * 2;
+  constexpr int RB = T::RB;
   const char* base = tile + 16 * step * RB;
   const bf16x4 lo = tr_read(base + off[0][db]);
   const bf16x4 hi = tr_read(base + off[1][db]);
@@ -153,12 +191,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
-  constexpr int RB = (D + 16) * 2;  // LDS row bytes of K rows
-  constexpr int VRB = (kTile + 8) * 2;  // LDS row bytes of the transposed V tile
+  using KT = RowTile<D, true>;
+  using VT = VtTile<D>;
   constexpr int NV = D / 8;        // 16-byte vectors per row
   // two LDS buffers: tile t is read from one while tile t+1 is written to the other
-  __shared__ __attribute__((aligned(16))) char ks2[2][kTile * RB];
-  __shared__ __attribute__((aligned(16))) char vs2[2][D * VRB];  // [d][column], column p = key vt_key(p)
+  __shared__ __attribute__((aligned(16))) char ks2[2][KT::kBytes];
+  __shared__ __attribute__((aligned(16))) char vs2[2][VT::kBytes];  // [d][column], column p = key vt_key(p)
   const AttnArgs& a = p.a;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -190,20 +228,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
-  const int rd = r32 * RB + half * 16;  // A = K/V rows: row r32, granule 2j + half
   int toff[2][D / 32];
-  tr_offsets<D>(lane, toff);
+  tr_offsets<D, KT>(lane, toff);
   // V rows (A of dP^T: key 32*kb + r32, d = 16j + 8*half + 0..7) from the
   // transposed tile by two transpose reads: the address lane (e = j16 >> 2,
   // m = j16 & 3) of a 16-lane group points at row d = 16j + 8*half + 4*aa + e,
-  // at the column holding keys 16*(g16 & 1) + 4m .. +3, i.e. column
-  // 16*(g16 & 1) + 4*swap(m) where swap exchanges m's two bits.
-  int voff[2];
+  // at the column holding keys 32*kb + 16*(g16 & 1) + 4m .. +3, i.e. column
+  // 32*kb + 16*(g16 & 1) + 4*swap(m) where swap exchanges m's two bits.  The
+  // swizzle depends on (d >> 1) & 1 = (e >> 1) & 1 only, so 16j is a plain
+  // offset.
+  int voff[2][2];
   {
     const int g16 = lane >> 4, j16 = lane & 15, m = j16 & 3;
-    const int col = 16 * (g16 & 1) + 4 * (((m & 1) << 1) | (m >> 1));
 #pragma unroll
-    for (int aa = 0; aa < 2; ++aa) voff[aa] = (8 * (g16 >> 1) + 4 * aa + (j16 >> 2)) * VRB + col * 2;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        const int col = 32 * kb + 16 * (g16 & 1) + 4 * (((m & 1) << 1) | (m >> 1));
+        voff[kb][aa] = VT::off(8 * (g16 >> 1) + 4 * aa + (j16 >> 2), col >> 3) + (col & 7) * 2;
+      }
   }
 
   // Loads of one 64-key tile, held in registers from issue to LDS write.
@@ -237,14 +280,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
     for (int i = 0; i < NL; ++i) {
       const int it = tid + i * kBwdThreads;
       const int row = it / NV, vec = it % NV;
-      *reinterpret_cast<u32x4*>(kbuf + row * RB + vec * 16) = kreg[i];
+      *reinterpret_cast<u32x4*>(kbuf + KT::off(row, vec)) = kreg[i];
       if (vt_reg) {  // columns already in vt_key order: copy
-        *reinterpret_cast<u32x4*>(vbuf + (it >> 3) * VRB + (it & 7) * 16) = vreg[i];
+        *reinterpret_cast<u32x4*>(vbuf + VT::off(it >> 3, it & 7)) = vreg[i];
       } else {       // row-major V (the current chunk): key row -> column vt_key(row)
         const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
-        char* col = vbuf + vt_key(row) * 2 + vec * 8 * VRB;
+        const int p = vt_key(row);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<__bf16*>(col + e * VRB) = b[e];
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<__bf16*>(vbuf + VT::off(vec * 8 + e, p >> 3) + (p & 7) * 2) = b[e];
       }
     }
   };
@@ -274,9 +318,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + rd + 32 * j);
-        const char* vb = vs + j * 16 * VRB + kb * 64;
-        const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[0]), tr_read(vb + voff[1]), 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 ka = row_read<KT>(ks, kb * 32 + r32, 2 * j + half);
+        const char* vb = vs + j * 16 * VT::RB;
+        const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[kb][0]), tr_read(vb + voff[kb][1]), 0, 1, 2, 3, 4, 5, 6, 7);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
       }
@@ -292,7 +336,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
         const bf16x8 b = pack8(ds, s2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, KT>(ks, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
       }
     }
     if (has_next) stage(ks2[(t + 1) & 1], vs2[(t + 1) & 1]);
@@ -318,10 +362,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
-  constexpr int RB = (D + 16) * 2;
+  using QT = RowTile<D, false>;  // padded: the swizzle's address arithmetic spills here
   constexpr int NV = D / 8;
-  __shared__ __attribute__((aligned(16))) char qs[kTile * RB];   // Q' rows
-  __shared__ __attribute__((aligned(16))) char gs[kTile * RB];   // dO rows
+  __shared__ __attribute__((aligned(16))) char qs[QT::kBytes];   // Q' rows
+  __shared__ __attribute__((aligned(16))) char gs[QT::kBytes];   // dO rows
   __shared__ __attribute__((aligned(16))) float lse2s[kTile];
   __shared__ __attribute__((aligned(16))) float dls[kTile];
   const AttnArgs& a = p.a;
@@ -350,9 +394,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
-  const int rd = r32 * RB + half * 16;
   int toff[2][D / 32];
-  tr_offsets<D>(lane, toff);
+  tr_offsets<D, QT>(lane, toff);
   const __bf16* q = static_cast<const __bf16*>(a.q);
   const __bf16* g = static_cast<const __bf16*>(p.dout);
 
@@ -368,8 +411,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
         wq = *reinterpret_cast<const u32x4*>(q + e);
         wg = *reinterpret_cast<const u32x4*>(g + e);
       }
-      *reinterpret_cast<bf16x8*>(qs + row * RB + vec * 16) = scale_bf16x8(wq, c);
-      *reinterpret_cast<u32x4*>(gs + row * RB + vec * 16) = wg;
+      *reinterpret_cast<bf16x8*>(qs + QT::off(row, vec)) = scale_bf16x8(wq, c);
+      *reinterpret_cast<u32x4*>(gs + QT::off(row, vec)) = wg;
     }
     if (tid < kTile) {
       const int qi = q0 + tid;
@@ -384,8 +427,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + qb * 32 * RB + rd + 32 * j);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gs + qb * 32 * RB + rd + 32 * j);
+        const bf16x8 qa = row_read<QT>(qs, qb * 32 + r32, 2 * j + half);
+        const bf16x8 ga = row_read<QT>(gs, qb * 32 + r32, 2 * j + half);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[j], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[j], dp, 0, 0, 0);
       }
@@ -411,8 +454,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
         const bf16x8 db8 = pack8(ds, s2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(gs, 2 * qb + s2, toff, db), pb, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, 2 * qb + s2, toff, db), db8, dk[db], 0, 0, 0);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(gs, 2 * qb + s2, toff, db), pb, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(qs, 2 * qb + s2, toff, db), db8, dk[db], 0, 0, 0);
         }
       }
     }
