@@ -554,8 +554,12 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
+    marks = [start]  # one event per step boundary: switch-step vs steady-step latency
     for _ in range(args.steps):
         wl.step()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks.append(e)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -584,6 +588,14 @@ def main():
         xf = 4.0 * CT * N_TXT * D * H
         extra["cross_attn_ms"] = x_ms
         extra["cross_attn_tflops"] = xf / (x_ms * 1e-3) / 1e12
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    sw = [m for i, m in enumerate(step_ms) if is_switch(first + i)]
+    steady = [m for i, m in enumerate(step_ms) if not is_switch(first + i) and first + i >= 3]
+    if steady:
+        extra["steady_step_ms"] = sum(steady) / len(steady)
+    if sw and args.workload == "switch":
+        extra["switch_step_ms"] = sum(sw) / len(sw)
+        extra["switch_steps"] = len(sw)
     rc_ms, _, _ = kernel_stats(timers, "recache")
     if rc_ms:
         elt = 1 if args.kv == "int8" else 2
