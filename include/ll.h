@@ -181,8 +181,9 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
  *          when n_cur == 0).
  * Gradients are fp32, accumulated in fp32 from bf16 MFMA products of bf16
  * operands (P and dS rounded to bf16); P is recomputed from the forward's lse.
- * Only BF16 activations with a BF16 cache are supported (else
- * LL_ERR_UNSUPPORTED).  n_q >= 1.  LL_ERR_BAD_STATE if the key set is empty.
+ * BF16 activations only (else LL_ERR_UNSUPPORTED); with an I8 cache the
+ * context is the same bf16(q * s) staging copy the forward attends over.
+ * n_q >= 1.  LL_ERR_BAD_STATE if the key set is empty.
  */
 ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
                                   const void* k_cur, const void* v_cur, int64_t n_cur, float scale,

@@ -391,8 +391,7 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
   if (st != LL_OK) return st;
   const ll::CacheState& cs = cache->state;
   const ll::Geometry& g = cs.geom();
-  if (g.act != LL_BF16 || g.kv != LL_BF16)
-    return fail(LL_ERR_UNSUPPORTED, "the backward supports BF16 activations with a BF16 cache");
+  if (g.act != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "the backward supports BF16 activations");
   if (n_q < 1 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q must be in [1, 2^30)");
   if (n_cur != 0 && n_cur != g.ctok)
     return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
@@ -428,6 +427,7 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
   b.dq = dq;
   b.dk = n_cur > 0 ? dk_cur : nullptr;
   b.dv = n_cur > 0 ? dv_cur : nullptr;
+  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention_bwd(b, stream), "attention backward launch");
 }
 

@@ -421,10 +421,15 @@ def test_backward_validation_and_launch(libs):
     libs.llh_fail_next_launch()
     assert call() == "LL_ERR_HIP"
     libs.ll_cache_destroy(h)
-    for act, kv in ((ll.LL_F32, ll.LL_F32), (ll.LL_BF16, ll.LL_I8)):
-        h2 = create(libs, cfg(act=act, kv=kv))
-        assert status(libs, libs.ll_sink_window_attn_bwd(h2, *args(layer=0))) == "LL_ERR_UNSUPPORTED"
-        libs.ll_cache_destroy(h2)
+    h2 = create(libs, cfg(act=ll.LL_F32, kv=ll.LL_F32))
+    assert status(libs, libs.ll_sink_window_attn_bwd(h2, *args(layer=0))) == "LL_ERR_UNSUPPORTED"
+    libs.ll_cache_destroy(h2)
+    h2 = create(libs, cfg(kv=ll.LL_I8))            # int8 context: staged, then the bf16 backward
+    stages = libs.llh_stage_calls()
+    assert libs.ll_cache_append_chunk(h2, 0, A, A, None) == 0
+    assert status(libs, libs.ll_sink_window_attn_bwd(h2, *args(layer=0))) == "LL_OK"
+    assert libs.llh_stage_calls() == stages + 1
+    libs.ll_cache_destroy(h2)
     h3 = create(libs, cfg())
     assert status(libs, libs.ll_sink_window_attn_bwd(h3, *args(layer=0, n_cur=0, k=None, v=None))) \
         == "LL_ERR_BAD_STATE"

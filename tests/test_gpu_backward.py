@@ -47,11 +47,11 @@ def check_grad(got, want, what):
     assert float(err.max()) <= GRAD_MAX_REL * scale, f"{what}: max abs {float(err.max())}"
 
 
-def run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=True, rows=None):
-    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+def run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=True, rows=None, int8=False):
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_I8 if int8 else ll.LL_BF16)
     cache = ll.Cache(cfg)
     g = CacheGeometry(T, C, S, W)
-    hist = LayerHistory(g)
+    hist = LayerHistory(g, int8=int8)
     ct = g.chunk_tokens
     scale = 1.0 / math.sqrt(D)
     for c in range(n_pre):
@@ -64,7 +64,7 @@ def run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=True, rows=None):
     dq_, dk_, dv_, ddo = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
     out = torch.empty_like(dq_)
     lse = torch.empty((H, ct), dtype=torch.float32, device="cuda")
-    say(f"[bwd cfg={cfg_id} T={T} C={C} S={S} W={W} H={H} D={D}] chunk {c}"
+    say(f"[bwd cfg={cfg_id} T={T} C={C} S={S} W={W} H={H} D={D}{' i8' if int8 else ''}] chunk {c}"
         f"{'' if with_cur else ' (cache only)'}")
     kc, vc = (dk_, dv_) if with_cur else (None, None)
     cache.attn(0, dq_, kc, vc, scale, out, lse)
@@ -115,3 +115,9 @@ def test_bwd_config1_full():
     rows = np.unique(np.concatenate([[0, 127, 128, 4607, 4608, 4679],
                                      np.random.default_rng(3).choice(4680, 200, replace=False)]))
     run_bwd(165, 1560, 3, 3, 9, 12, 128, 4, rows=rows)
+
+
+def test_bwd_int8_cache():
+    """INT8 cache: the detached context is the exactly dequantised stored K/V
+    (the oracle's int8 history); the current chunk stays bf16."""
+    run_bwd(166, 50, 2, 2, 6, 2, 128, 4, int8=True)
