@@ -514,3 +514,32 @@ def test_window_sweep_shapes_sampled(S, W):
                                        sink_frames=S, window_frames=W, scale=1 / math.sqrt(D))
     check_out(out[rows], want, "bf16", f"sweep S={S} W={W}")
     check_lse(lse[:, rows], wlse, "bf16", f"sweep S={S} W={W}")
+
+
+# --------------------------------------------------------------------------
+# random small geometries (fixed draw)
+# --------------------------------------------------------------------------
+
+def _random_geometries(n=12, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        C = int(rng.integers(1, 4))
+        T = int(rng.integers(3, 70))
+        nsc = int(rng.integers(0, 3))
+        R = int(rng.integers(0, 6))
+        H = int(rng.integers(1, 4))
+        D = int(rng.choice([64, 128]))
+        kind = ["bf16", "f32", "int8"][i % 3]
+        out.append((200 + i, T, C, nsc * C, (R + 1) * C, H, D, kind, nsc + R + 2))
+    return out
+
+
+@pytest.mark.parametrize("geom", _random_geometries(), ids=lambda g: f"cfg{g[0]}-{g[7]}")
+def test_random_geometry_stream(geom):
+    """A fixed draw of small geometries (tokens per frame, frames per chunk,
+    sink chunks, ring slots, heads, head dim, bf16 / fp32 / int8 cache),
+    streamed past the first eviction: every attention output against the
+    oracle and the cache bytes after every append."""
+    cfg_id, T, C, S, W, H, D, kind, n = geom
+    run_stream(cfg_id, T, C, S, W, H, D, "f32" if kind == "f32" else "bf16", n, int8=kind == "int8")
