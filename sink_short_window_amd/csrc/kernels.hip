@@ -793,20 +793,21 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Cache writers.  Grid: x over (head, row, 16-byte vector) of one chunk,
-// y = chunk * 2 + (0: K, 1: V), z = layer.  Destination rows are contiguous
-// per head (coalesced writes); each source row is one contiguous D-vector.
+// Cache writers (append / recache of whole chunks).
 // ---------------------------------------------------------------------------
+
+// fp32 cache (K and V row-major).  Grid: x over (head, row, 16-byte vector)
+// of one chunk, y = chunk * 2 + (0: K, 1: V), z = layer.  Destination rows
+// are contiguous per head (coalesced writes); each source row is one
+// contiguous D-vector.
 template <int kElt>
 __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
   const int vpr = a.D * kElt / 16;
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = int64_t(a.ctok) * a.H * vpr;
   if (e >= total) return;
-  // y = chunk * parts + part; with the transposed V layout this kernel copies K only
-  const int parts = a.vt ? 1 : 2;
-  const int chunk = blockIdx.y / parts;
-  const int isv = blockIdx.y % parts;
+  const int chunk = blockIdx.y >> 1;
+  const int isv = blockIdx.y & 1;
   const int z = blockIdx.z;
   const int vec = int(e % vpr);
   const int64_t rh = e / vpr;
@@ -820,29 +821,50 @@ __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
-// V writer for the transposed tile layout: one workgroup per (head, 64-key
-// tile) of a chunk.  The tile is staged key-major in LDS and written as
-// [D][64] (16 KB contiguous for D = 128), physical column p holding key p with
-// bits 2 and 3 swapped (the key order of the PV operand); keys past the
-// chunk's end are written as zeros.
+// bf16 cache, K rows and transposed V tiles in one launch.  Grid: x over
+// (head, 64-key tile) of one chunk, y = chunk * 2 + (0: K, 1: V), z = layer.
+// A K block copies the tile's rows into the head-major cache rows (16 KB
+// contiguous for D = 128).  A V block stages the tile key-major in LDS and
+// writes it as [D][64] into the chunk slot's tile, physical column p holding
+// key p with bits 2 and 3 swapped (the key order of the PV operand); keys
+// past the chunk's end are written as zeros.
 template <int D>
-__global__ __launch_bounds__(256) void copy_vt_kernel(CopyArgs a) {
+__global__ __launch_bounds__(256) void append_bf16_kernel(CopyArgs a) {
   constexpr int kG = D / 8;  // 16-byte granules per key row
   __shared__ __attribute__((aligned(16))) __bf16 t[kBN][D + 8];
   const int h = blockIdx.x / a.tps;
   const int tile = blockIdx.x % a.tps;
-  const int chunk = blockIdx.y;
+  const int chunk = blockIdx.y >> 1;
+  const bool isv = blockIdx.y & 1;
   const int z = blockIdx.z;
   const int tid = threadIdx.x;
-  const __bf16* src = static_cast<const __bf16*>(a.src_v) + int64_t(z) * a.src_layer_elems +
+  const __bf16* src = static_cast<const __bf16*>(isv ? a.src_v : a.src_k) + int64_t(z) * a.src_layer_elems +
                       int64_t(chunk) * a.ctok * a.H * D + int64_t(h) * D;
+  constexpr int kPer = kBN * kG / 256;  // 16-byte loads per thread
+  // all loads of the thread first, then the stores
+  uint4 w[kPer];
 #pragma unroll
-  for (int it = tid; it < kBN * kG; it += 256) {
-    const int key = it / kG, g = it % kG;
-    const int row = tile * kBN + key;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < a.ctok) w = *reinterpret_cast<const uint4*>(src + int64_t(row) * a.H * D + g * 8);
-    *reinterpret_cast<uint4*>(&t[key][g * 8]) = w;
+  for (int i = 0; i < kPer; ++i) {
+    const int it = tid + 256 * i;
+    const int row = tile * kBN + it / kG, g = it % kG;
+    w[i] = row < a.ctok ? *reinterpret_cast<const uint4*>(src + int64_t(row) * a.H * D + g * 8)
+                        : make_uint4(0, 0, 0, 0);
+  }
+  if (!isv) {
+    __bf16* dst = reinterpret_cast<__bf16*>(a.dst + int64_t(z) * a.dst_layer_bytes + a.k_off) +
+                  (int64_t(h) * a.rows + a.dst_row0[chunk]) * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int it = tid + 256 * i;
+      const int row = tile * kBN + it / kG, g = it % kG;
+      if (row < a.ctok) *reinterpret_cast<uint4*>(dst + int64_t(row) * D + g * 8) = w[i];
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int it = tid + 256 * i;
+    *reinterpret_cast<uint4*>(&t[it / kG][(it % kG) * 8]) = w[i];
   }
   __syncthreads();
   __bf16* dst = reinterpret_cast<__bf16*>(a.dst + int64_t(z) * a.dst_layer_bytes + a.v_off) +
@@ -999,15 +1021,15 @@ int launch_copy_chunks(const CopyArgs& a, void* stream) {
     const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * 2, a.n_layers);
     return launch(quant_chunks_kernel, grid, dim3(256), &a, stream);
   }
-  const int elt = a.act == LL_F32 ? 4 : 2;
-  const int64_t threads = int64_t(a.ctok) * a.H * (a.D * elt / 16);
-  const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * (a.vt ? 1 : 2), a.n_layers);
-  if (elt == 4) return launch(copy_chunks_kernel<4>, grid, dim3(256), &a, stream);
-  int err = launch(copy_chunks_kernel<2>, grid, dim3(256), &a, stream);
-  if (err != 0 || !a.vt) return err;
-  const dim3 vgrid(unsigned(a.H * a.tps), a.n_chunks, a.n_layers);
-  return a.D == 64 ? launch(copy_vt_kernel<64>, vgrid, dim3(256), &a, stream)
-                   : launch(copy_vt_kernel<128>, vgrid, dim3(256), &a, stream);
+  if (a.vt) {  // bf16 cache (the only one with transposed V)
+    const dim3 grid(unsigned(a.H * a.tps), a.n_chunks * 2, a.n_layers);
+    return a.D == 64 ? launch(append_bf16_kernel<64>, grid, dim3(256), &a, stream)
+                     : launch(append_bf16_kernel<128>, grid, dim3(256), &a, stream);
+  }
+  // fp32 cache (fp32 activations)
+  const int64_t threads = int64_t(a.ctok) * a.H * (a.D * 4 / 16);
+  const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * 2, a.n_layers);
+  return launch(copy_chunks_kernel<4>, grid, dim3(256), &a, stream);
 }
 
 int launch_stage_int8(const StageArgs& a, void* stream) {
