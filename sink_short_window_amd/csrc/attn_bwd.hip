@@ -270,9 +270,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
       const int row = it / NV, vec = it % NV;
       // K rows (rows past the run read as zero)
       kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
-      // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or row-major rows
+      // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or
+      // row-major rows with the key in the low bits of it (see stage)
       vreg[i] = vt_reg ? __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + (it >> 3) * 128 + (it & 7) * 16, 0, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
+                       : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + it % kTile) * rs + it / kTile * 16, 0, 0);
     }
   };
   auto stage = [&](char* kbuf, char* vbuf) {
@@ -283,12 +284,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
       *reinterpret_cast<u32x4*>(kbuf + KT::off(row, vec)) = kreg[i];
       if (vt_reg) {  // columns already in vt_key order: copy
         *reinterpret_cast<u32x4*>(vbuf + VT::off(it >> 3, it & 7)) = vreg[i];
-      } else {       // row-major V (the current chunk): key row -> column vt_key(row)
+      } else {
+        // Row-major V (the current chunk): the 64 lanes of a wave hold the 64
+        // keys of one 16-byte column (dims 8*vv .. 8*vv+7), so each 2-byte
+        // store below fills one whole 128-byte row d of the transposed tile
+        // (key -> column vt_key(key)) without bank conflicts.
         const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
-        const int p = vt_key(row);
+        const int key = it % kTile, vv = it / kTile;
+        const int p = vt_key(key);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<__bf16*>(vbuf + VT::off(vec * 8 + e, p >> 3) + (p & 7) * 2) = b[e];
+          *reinterpret_cast<__bf16*>(vbuf + VT::off(vv * 8 + e, p >> 3) + (p & 7) * 2) = b[e];
       }
     }
   };
