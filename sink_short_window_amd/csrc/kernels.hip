@@ -800,8 +800,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // of one chunk, y = chunk * 2 + (0: K, 1: V), z = layer.  Destination rows
 // are contiguous per head (coalesced writes); each source row is one
 // contiguous D-vector.
-template <int kElt>
 __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
+  constexpr int kElt = 4;  // fp32
   const int vpr = a.D * kElt / 16;
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = int64_t(a.ctok) * a.H * vpr;
@@ -1029,7 +1029,7 @@ int launch_copy_chunks(const CopyArgs& a, void* stream) {
   // fp32 cache (fp32 activations)
   const int64_t threads = int64_t(a.ctok) * a.H * (a.D * 4 / 16);
   const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * 2, a.n_layers);
-  return launch(copy_chunks_kernel<4>, grid, dim3(256), &a, stream);
+  return launch(copy_chunks_kernel, grid, dim3(256), &a, stream);
 }
 
 int launch_stage_int8(const StageArgs& a, void* stream) {
