@@ -15,6 +15,8 @@ written from the paper "LongLive: Real-time Interactive Long Video Generation":
   seen (with recache payloads applied).
 * ``quant``       -- the per-token, per-head symmetric INT8 quantiser used by
   the INT8 KV-cache variant, in float32 as the variant defines it.
+* ``linear_attention`` -- the linear-attention variant over the same key set
+  (feature map max(x, 0), normalised weighted sum), pairwise form.
 
 It shares no code with the HIP path; the only module both sides use is the
 seeded input generator, which holds none of the method's arithmetic.
@@ -26,10 +28,13 @@ from .attention import (allowed_frames, frame_mask, masked_attention,
 from .cache_model import (CacheGeometry, slot_of_chunk, DequeCacheModel,
                           resident_window_chunks, LayerHistory)
 from .quant import quantize_int8, dequantize_int8
+from .linear_attention import (LINEAR_EPS, feature_map, linear_masked_attention,
+                               linear_sink_window_attention)
 
 __all__ = [
     "allowed_frames", "frame_mask", "masked_attention", "sink_window_attention",
     "cross_attention", "window_reencode_attention", "sink_window_attention_grad",
     "CacheGeometry", "slot_of_chunk", "DequeCacheModel",
     "resident_window_chunks", "LayerHistory", "quantize_int8", "dequantize_int8",
+    "LINEAR_EPS", "feature_map", "linear_masked_attention", "linear_sink_window_attention",
 ]
