@@ -18,7 +18,7 @@ One step = one generated chunk:
 Warmup steps generate chunks 0.. W-1 untimed; the K timed steps continue the
 same stream.  ``--workload stream`` drops cross-attention and recache (the
 30-layer cache step alone); ``--kv int8`` stores K/V as int8 with per-token,
-per-head scales, dequantised inside the attention kernel.
+per-head scales, dequantised to a bf16 staging copy once per attention call.
 
 All inputs are seeded synthetic N(0,1) values (bf16) drawn on the host from
 pools and copied to the device once before timing.
@@ -316,6 +316,76 @@ def time_backward(wl, reps=10):
     return sorted(a.elapsed_time(b) for a, b in ms)[reps // 2]
 
 
+def linear_bytes():
+    """Algorithmic HBM bytes of one linear-attention call at 18720 keys: Q and
+    O once, the K/V of every key once (the state and normaliser are a few MB
+    of on-chip-sized partials)."""
+    return float(H * D * 2 * (2 * CT + 2 * keys_at(10)))
+
+
+def linear_flops():
+    """Algorithmic flop of one linear-attention call: phi(K)^T V and phi(K)^T 1
+    over the keys, phi(Q) S and phi(Q) . z over the queries."""
+    return 2.0 * H * D * (D + 1) * (keys_at(10) + CT)
+
+
+def time_linear(wl, reps=10):
+    """Linear-attention variant of layer 0's call (same key set as the softmax
+    call, 18720 keys): HIP events around each call (its three kernels)."""
+    t = wl.torch
+    q, k, v = wl.q[0], wl.k[0], wl.v[0]
+    out = t.empty_like(q)
+    call = lambda: wl.cache.linear_attn(0, q, k, v, out)
+    for _ in range(3):
+        call()
+    ms = []
+    for _ in range(reps):
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ms.append((a, b))
+    t.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ms)[reps // 2]
+
+
+def linear_only():
+    """One layer at the workload's shapes: chunks 0..3 appended (sink = chunk 0,
+    window = chunks 2, 3), then the linear-attention variant of chunk 4's call
+    (18720 keys) timed after a warmup of ~40 calls (median of 5 batches of
+    10), next to the softmax call on the same inputs.  Prints one JSON line."""
+    import torch
+    from sink_short_window_amd import ll, synth
+    gen = lambda i, tensor: synth.to_torch(
+        synth.normal((CT, H, D), "bf16", SWEEP_CFG_ID, 2, i, 0, tensor), "bf16", "cuda")
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg, "cuda")
+    for c in range(4):
+        cache.append_chunk(0, gen(c, synth.K), gen(c, synth.V))
+    q, k, v = gen(4, synth.Q), gen(4, synth.K), gen(4, synth.V)
+    out = torch.empty_like(q)
+
+    def timed(call):
+        def batch(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b)
+        batch(40)
+        return sorted(batch(10) / 10 for _ in range(5))[2]
+
+    ms = timed(lambda: cache.linear_attn(0, q, k, v, out))
+    sm = timed(lambda: cache.attn(0, q, k, v, 1.0 / math.sqrt(D), out))
+    print(json.dumps({"linear_ms_per_call": ms, "keys_per_call": keys_at(10),
+                      "bytes_per_call": linear_bytes(), "GBps": linear_bytes() / (ms * 1e-3) / 1e9,
+                      "flop_per_call": linear_flops(), "tflops": linear_flops() / (ms * 1e-3) / 1e12,
+                      "softmax_ms_per_call": sm, "speedup_vs_softmax": sm / ms}))
+    cache.close()
+
+
 def backward_only():
     """One layer at the workload's shapes: chunks 0..3 appended (sink = chunk 0,
     window = chunks 2, 3), the forward of chunk 4 for out and lse, then the
@@ -504,6 +574,8 @@ def main():
                          "without the 3-frame sink (JSON line per point) and exit")
     ap.add_argument("--backward", action="store_true",
                     help="only time the backward of one layer's call (training step) and exit")
+    ap.add_argument("--linear", action="store_true",
+                    help="only time the linear-attention variant of one layer's call and exit")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor bf16 GEMM on random and on zero operands and exit")
     args = ap.parse_args()
@@ -522,6 +594,9 @@ def main():
         return
     if args.backward:
         backward_only()
+        return
+    if args.linear:
+        linear_only()
         return
     if args.passes < 1:
         print("--passes must be >= 1", file=sys.stderr)
@@ -615,6 +690,11 @@ def main():
         extra["backward_ms_per_call"] = bw_ms
         extra["backward_flop_per_call"] = backward_flops()
         extra["backward_tflops"] = backward_flops() / (bw_ms * 1e-3) / 1e12
+    # The linear-attention variant of the same call (same cache, same key set).
+    li_ms = time_linear(wl)
+    extra["linear_ms_per_call"] = li_ms
+    extra["linear_GBps"] = linear_bytes() / (li_ms * 1e-3) / 1e9
+    extra["linear_tflops"] = linear_flops() / (li_ms * 1e-3) / 1e12
 
     roofline = None
     if tflops:

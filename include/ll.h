@@ -209,6 +209,34 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
                                   ll_stream_t stream);
 
 /*
+ * Linear-attention variant of ll_sink_window_attn (paper §4 "Implementation":
+ * the method was also built on a linear-attention video model for more speed;
+ * the paper gives no formulation, so this is the plain reading): the same key
+ * set (resident sink, resident window, and the current chunk when
+ * n_cur == C_tok) with the weights w_ij = phi(q_i) . phi(k_j),
+ * phi(x) = max(x, 0) elementwise, and
+ *   out_i = sum_j w_ij v_j / (sum_j w_ij + 1e-6)
+ * (no logit scale; a query with no positive weight gets 0).  Computed in the
+ * associative form S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j) per head:
+ * fp32 accumulation of bf16 MFMA products, S kept as a bf16 pair (~16
+ * significant bits) for the output product.
+ *   q, out: [n_q][H][D] bf16 (n_q >= 0; 0 is a no-op after validation).
+ *   work:   device workspace of at least ll_linear_attn_workspace_bytes,
+ *           256-byte aligned, owned by the caller; overwritten (partial sums).
+ * Three launches on the stream (plus the int8 staging launch for an I8
+ * cache, as ll_sink_window_attn).  BF16 activations only (else
+ * LL_ERR_UNSUPPORTED); LL_ERR_BUFFER_TOO_SMALL if work_bytes is short;
+ * LL_ERR_BAD_STATE if the key set is empty.  Calls sharing one workspace
+ * must be stream-ordered.
+ */
+ll_status ll_sink_window_linear_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                     const void* k_cur, const void* v_cur, int64_t n_cur, void* out,
+                                     void* work, size_t work_bytes, ll_stream_t stream);
+
+/* Workspace bytes ll_sink_window_linear_attn needs for this cache's H and D. */
+ll_status ll_linear_attn_workspace_bytes(const ll_cache* cache, size_t* bytes);
+
+/*
  * Text cross-attention (paper §3.1: cross-attention injects the prompt):
  * unmasked softmax attention of q [n_q][H][D] to k_txt, v_txt [n_txt][H][D],
  * all of `dtype` (F32 or BF16); out [n_q][H][D]; lse nullable [H][n_q];

@@ -28,7 +28,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-munsafe-fp-atomics"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
-DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip")
+DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip", "linear_attn.hip")
 LIB_LL = os.path.join(LIB, "libll.so")
 LIB_HOSTSTUB = os.path.join(LIB, "libll_hoststub.so")
 

@@ -114,7 +114,45 @@ struct StageArgs {
   int32_t D = 0;
 };
 
+// Linear-attention variant (ll_sink_window_linear_attn): per head the state
+// S = sum_j phi(k_j) v_j^T ([D][D]) and z = sum_j phi(k_j) over the runs of
+// `a` are summed in n_split partial sums of tiles_per_split 64-key tiles each,
+// reduced, then applied: out_i = phi(q_i)^T S / (phi(q_i) . z + eps), phi(x) =
+// max(x, 0).  The workspace pointers are parts of the caller's buffer
+// (linear_workspace_layout).
+constexpr int kLinMaxSplits = 32;
+struct LinArgs {
+  AttnArgs a;                 // runs, q, out, n_q, H, D (scale and lse unused)
+  float* part_s = nullptr;    // [n_split][H][D][D] fp32, [d1][d2]
+  float* part_z = nullptr;    // [n_split][H][D] fp32
+  void* st_hi = nullptr;      // [H][D][D] bf16: S transposed ([d2][d1]), high part
+  void* st_lo = nullptr;      // [H][D][D] bf16: S - hi, rounded
+  float* z = nullptr;         // [H][D] fp32
+  int32_t n_split = 0;
+  int32_t tiles_per_split = 0;
+  float eps = 1e-6f;
+};
+
+// Byte offsets of the parts of the linear-attention workspace for H heads of
+// dimension D, each 256-byte aligned; returns the total size.
+struct LinLayout {
+  size_t part_s, part_z, st_hi, st_lo, z, total;
+};
+inline LinLayout linear_workspace_layout(int H, int D) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  LinLayout l{};
+  size_t o = 0;
+  l.part_s = o; o += up(size_t(kLinMaxSplits) * H * D * D * 4);
+  l.part_z = o; o += up(size_t(kLinMaxSplits) * H * D * 4);
+  l.st_hi = o;  o += up(size_t(H) * D * D * 2);
+  l.st_lo = o;  o += up(size_t(H) * D * D * 2);
+  l.z = o;      o += up(size_t(H) * D * 4);
+  l.total = o;
+  return l;
+}
+
 int launch_attention(const AttnArgs& a, void* stream);
+int launch_linear_attention(const LinArgs& a, void* stream);
 int launch_stage_int8(const StageArgs& a, void* stream);
 int launch_attention_bwd(const AttnBwdArgs& a, void* stream);
 int launch_copy_chunks(const CopyArgs& a, void* stream);

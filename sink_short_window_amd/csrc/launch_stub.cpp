@@ -14,6 +14,8 @@ AttnArgs g_attn;
 AttnBwdArgs g_bwd;
 StageArgs g_stage;
 CopyArgs g_copy;
+LinArgs g_lin;
+int g_lin_calls = 0;
 int g_attn_calls = 0;
 int g_bwd_calls = 0;
 int g_stage_calls = 0;
@@ -28,6 +30,17 @@ int launch_attention(const AttnArgs& a, void*) {
   }
   g_attn = a;
   ++g_attn_calls;
+  return 0;
+}
+
+int launch_linear_attention(const LinArgs& a, void*) {
+  if (g_fail_next) {
+    g_fail_next = 0;
+    return 1;
+  }
+  g_lin = a;
+  g_attn = a.a;  // the run table, readable through llh_last_attn
+  ++g_lin_calls;
   return 0;
 }
 
@@ -114,6 +127,21 @@ int llh_last_bwd(int64_t* ptrs /* [delta, dq, dk, dv, out, dout, lse] */) {
   ptrs[5] = int64_t(reinterpret_cast<intptr_t>(b.dout));
   ptrs[6] = int64_t(reinterpret_cast<intptr_t>(b.lse));
   return b.dk != nullptr;
+}
+
+int llh_lin_calls(void) { return ll::g_lin_calls; }
+
+// Last linear-attention launch: returns n_split; tps receives the tiles per
+// split and ptrs [part_s, part_z, st_hi, st_lo, z] as integers.
+int llh_last_lin(int32_t* tps, int64_t* ptrs) {
+  const ll::LinArgs& p = ll::g_lin;
+  *tps = p.tiles_per_split;
+  ptrs[0] = int64_t(reinterpret_cast<intptr_t>(p.part_s));
+  ptrs[1] = int64_t(reinterpret_cast<intptr_t>(p.part_z));
+  ptrs[2] = int64_t(reinterpret_cast<intptr_t>(p.st_hi));
+  ptrs[3] = int64_t(reinterpret_cast<intptr_t>(p.st_lo));
+  ptrs[4] = int64_t(reinterpret_cast<intptr_t>(p.z));
+  return p.n_split;
 }
 
 int llh_stage_calls(void) { return ll::g_stage_calls; }

@@ -1,0 +1,436 @@
+// HIP kernels for gfx950 (MI355X): linear-attention variant of the sink +
+// short-window attention call.
+//
+// LongLive: Real-time Interactive Long Video Generation, §4 "Implementation"
+// (the method was also built on a linear-attention video model, for more
+// speed; the pages give no formulation).  Reading: the softmax call's key set
+// (frame sink, resident window, current chunk) with the weights
+// w_ij = phi(q_i) . phi(k_j), phi(x) = max(x, 0), and
+// out_i = sum_j w_ij v_j / (sum_j w_ij + eps).
+// The weights factor, so the call runs in its associative form: per head
+//   S = sum_j phi(k_j) v_j^T ([D][D]),  z = sum_j phi(k_j) ([D]),
+//   out_i = phi(q_i)^T S / (phi(q_i) . z + eps),
+// O((n_keys + n_q) D^2) work instead of O(n_q n_keys D).  Three kernels:
+//   lin_state_kernel   per (key split, head): partial S and z over a range of
+//                      64-key tiles; bf16 MFMA 32x32x16 with A = phi(K)^T
+//                      (transpose reads of the row-major K tile, then max(., 0))
+//                      and B = V (rows of the transposed V tile); z is the same
+//                      product with B = ones.  Keys past a run's end read as
+//                      zero, so they add nothing and need no mask.
+//   lin_reduce_kernel  sums the partials in a fixed order (deterministic) and
+//                      stores S transposed as a bf16 pair hi + lo (hi = bf16(S),
+//                      lo = bf16(S - hi)), which keeps ~16 significant bits.
+//   lin_apply_kernel   per 256 queries of one head: O^T = S^T phi(Q)^T as two
+//                      MFMA sums (hi and lo), the normaliser phi(q) . z on the
+//                      VALU, bf16 output.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace ll {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kTile = 64;          // keys per LDS tile
+constexpr int kStateThreads = 256;  // 4 waves
+constexpr int kApplyThreads = 512;  // 8 waves x 32 queries
+constexpr int kApplyBQ = 256;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// gfx950 LDS transpose read of 4 bf16: within each group of 16 lanes, lane i
+// receives element (i & 3) of the 8 bytes addressed by lane 4*e + (i >> 2).
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// max(x, 0) of 8 bf16: a negative value (sign bit set) becomes +0.
+__device__ __forceinline__ bf16x8 relu8(bf16x8 x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned neg = (w[i] >> 15) & 0x00010001u;
+    w[i] &= ~(neg * 0xffffu);
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Column p of a transposed V tile holds key p with bits 2 and 3 swapped: the
+// order in which an MFMA k-block of 16 keys is split between the two half
+// waves (keys 0..3, 8..11 in half 0; 4..7, 12..15 in half 1).
+__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// Row-major [64][D] K tile, read by transpose reads (per 32 lanes: 4
+// consecutive rows x 4 granules).  D = 128: granule g of row r at
+// g ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3), which spreads those 16
+// (row, granule) pairs over all 64 banks.  D = 64: rows padded by 32 bytes.
+template <int D>
+struct KTile {
+  static constexpr bool kSwz = D == 128;
+  static constexpr int RB = kSwz ? D * 2 : (D + 16) * 2;
+  static constexpr int kBytes = kTile * RB;
+  static __device__ __forceinline__ int off(int row, int gran) {
+    if constexpr (kSwz) return row * RB + ((gran ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
+    else return row * RB + gran * 16;
+  }
+};
+
+// Transposed [D][64] V tile (128-byte rows, column order vt_key), read by
+// 16-byte row reads of 32 consecutive rows; granule g of row d at
+// g ^ ((d >> 1) & 7).
+template <int D>
+struct VTile {
+  static constexpr int RB = kTile * 2;
+  static constexpr int kBytes = D * RB;
+  static __device__ __forceinline__ int off(int d, int gran) { return d * RB + ((gran ^ ((d >> 1) & 7)) << 4); }
+};
+
+// ---------------------------------------------------------------------------
+// State: partial S and z of one key split
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
+  using KT = KTile<D>;
+  using VT = VTile<D>;
+  constexpr int NV = D / 8;           // 16-byte vectors per K row
+  constexpr int NB = D / 32;          // 32-wide blocks of S per dimension
+  constexpr int NPW = NB * NB / 4;    // S blocks per wave (4 waves)
+  constexpr int NL = kTile * NV / kStateThreads;  // 16-byte loads per thread per side
+  static_assert(NPW >= 1 && NL >= 1, "shape");
+  __shared__ __attribute__((aligned(16))) char ks2[2][KT::kBytes];
+  __shared__ __attribute__((aligned(16))) char vs2[2][VT::kBytes];
+  const AttnArgs& a = p.a;
+  const int split = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
+  const int d1b = (wave * NPW) / NB;           // this wave's row block of S
+  const int d2b0 = (wave * NPW) % NB;          // and its first column block
+  const bool do_z = d2b0 == 0;
+
+  // This split's tiles [tb, te) of the tile sequence over the runs.
+  int n_tiles = 0;
+  for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + kTile - 1) / kTile;
+  const int tb = split * p.tiles_per_split;
+  const int te = min(n_tiles, tb + p.tiles_per_split);
+
+  f32x16 acc[NPW], zacc;
+#pragma unroll
+  for (int i = 0; i < NPW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zacc[r] = 0.f;
+
+  if (tb < te) {
+    // A operand (phi(K)^T, rows = tile columns 32*d1b + r32): two transpose
+    // reads per 16-key step, k order 16*step + {0..3, 8..11} (half 0) or
+    // {4..7, 12..15} (half 1), the vt_key order of the V tile's columns.
+    int toff[2];
+    {
+      const int g16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
+        const int col = 32 * d1b + 16 * (g16 & 1) + 4 * (j16 & 3);
+        toff[aa] = KT::off(row, col >> 3) + (col & 7) * 2;
+      }
+    }
+    // B operand (V rows d2 = 32*d2b + r32 at columns 16*step + 8*half..+7).
+    const int vrow = r32 * VT::RB;
+    const int vx = (r32 >> 1) & 7;  // the row's granule swizzle (32*d2b keeps it)
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+
+    // The next tile's loads, held in registers from issue to LDS store.
+    u32x4 kreg[NL], vreg[NL];
+    bool vt_reg = false;
+    // Position (run, first key) of tile t in the run sequence.
+    auto locate = [&](int t, int& run, int& t0) {
+      run = 0;
+      for (;;) {
+        const int nt = (a.seg[run].len + kTile - 1) / kTile;
+        if (t < nt) break;
+        t -= nt;
+        ++run;
+      }
+      t0 = t * kTile;
+    };
+    auto issue = [&](int run, int t0) {
+      const KvSeg& sg = a.seg[run];
+      const int len = sg.len;
+      const uint32_t rs = uint32_t(sg.row_stride) * 2;
+      const auto rk = rsrc(static_cast<const char*>(sg.k) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
+      const bool vt = sg.v_tiled != 0;
+      vt_reg = vt;
+      const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
+      const auto rv = vt ? rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2,
+                                    tiles * kTile * D * 2)
+                             : rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2,
+                                    uint32_t(len) * rs);
+      const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int it = tid + i * kStateThreads;
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + it / NV) * rs + (it % NV) * 16, 0, 0);
+        // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or
+        // row-major rows with the key in the low bits of it (see stage)
+        vreg[i] = vt ? __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + (it >> 3) * 128 + (it & 7) * 16, 0, 0)
+                           : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + it % kTile) * rs + it / kTile * 16, 0, 0);
+      }
+    };
+    auto stage = [&](char* kbuf, char* vbuf) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int it = tid + i * kStateThreads;
+        *reinterpret_cast<u32x4*>(kbuf + KT::off(it / NV, it % NV)) = kreg[i];
+        if (vt_reg) {
+          *reinterpret_cast<u32x4*>(vbuf + VT::off(it >> 3, it & 7)) = vreg[i];
+        } else {
+          // one key per lane: each 2-byte store fills one 128-byte row of the
+          // transposed tile (key -> column vt_key(key))
+          const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
+          const int key = it % kTile, vv = it / kTile;
+          const int c = vt_key(key);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<__bf16*>(vbuf + VT::off(vv * 8 + e, c >> 3) + (c & 7) * 2) = b[e];
+        }
+      }
+    };
+
+    // Issue cursor: the next tile whose loads go out.
+    int run, t0;
+    locate(tb, run, t0);
+    auto issue_next = [&]() {
+      issue(run, t0);
+      t0 += kTile;
+      if (t0 >= a.seg[run].len) {
+        ++run;
+        t0 = 0;
+      }
+    };
+    issue_next();
+    stage(ks2[0], vs2[0]);
+    __syncthreads();
+    for (int t = tb; t < te; ++t) {
+      const int buf = (t - tb) & 1;
+      if (t + 1 < te) issue_next();  // tile t+1, in flight during this tile's MFMAs
+      const char* ks = ks2[buf];
+      const char* vs = vs2[buf];
+#pragma unroll
+      for (int step = 0; step < kTile / 16; ++step) {
+        const char* kb = ks + 16 * step * KT::RB;
+        const bf16x8 fa = relu8(__builtin_shufflevector(tr_read(kb + toff[0]), tr_read(kb + toff[1]),
+                                                         0, 1, 2, 3, 4, 5, 6, 7));
+        const int g = ((2 * step) ^ (vx & 6)) | (half ^ (vx & 1));
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vs + (32 * (d2b0 + i)) * VT::RB + vrow + (g << 4));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, vb, acc[i], 0, 0, 0);
+        }
+        if (do_z) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, ones, zacc, 0, 0, 0);
+      }
+      if (t + 1 < te) stage(ks2[buf ^ 1], vs2[buf ^ 1]);
+      __syncthreads();
+    }
+  }
+
+  // Partial S rows d1 = 32*d1b + 8*(r >> 2) + 4*half + (r & 3), column
+  // d2 = 32*d2b + r32; z from column 0 of zacc.
+  float* ps = p.part_s + (int64_t(split) * a.H + head) * D * D;
+#pragma unroll
+  for (int i = 0; i < NPW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d1 = 32 * d1b + 8 * (r >> 2) + 4 * half + (r & 3);
+      ps[d1 * D + 32 * (d2b0 + i) + r32] = acc[i][r];
+    }
+  if (do_z && r32 == 0) {
+    float* pz = p.part_z + (int64_t(split) * a.H + head) * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pz[32 * d1b + 8 * (r >> 2) + 4 * half + (r & 3)] = zacc[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reduce: S = sum of the partials (split order), stored transposed as bf16
+// hi + lo; z likewise in fp32.  One workgroup per 32 x 32 tile of S, one
+// element per thread: rows of the partials are read coalesced, summed, and
+// written transposed through an LDS tile so the bf16 stores are coalesced too.
+// ---------------------------------------------------------------------------
+// Sum of x(0) .. x(n-1), n <= kLinMaxSplits, in a fixed order (k ascending)
+// with every load in flight at once.
+template <typename F>
+__device__ __forceinline__ float sum_splits(int n, F x) {
+  float v[kLinMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kLinMaxSplits; ++k) v[k] = k < n ? x(k) : 0.f;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kLinMaxSplits; ++k) s += v[k];
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void lin_reduce_kernel(LinArgs p) {
+  constexpr int NB = D / 32;
+  __shared__ float t[32][33];
+  const int head = blockIdx.y;
+  const int H = p.a.H;
+  const int b1 = blockIdx.x / NB, b2 = blockIdx.x % NB;  // tile rows d1, columns d2
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 32 threads
+  {
+    const int d1 = 32 * b1 + ty, d2 = 32 * b2 + tx;
+    t[ty][tx] = sum_splits(p.n_split, [&](int k) { return p.part_s[((int64_t(k) * H + head) * D + d1) * D + d2]; });
+  }
+  __syncthreads();
+  {
+    const int d2 = 32 * b2 + ty, d1 = 32 * b1 + tx;
+    const float s = t[tx][ty];
+    const __bf16 hi = (__bf16)s;
+    const int64_t e = (int64_t(head) * D + d2) * D + d1;
+    static_cast<__bf16*>(p.st_hi)[e] = hi;
+    static_cast<__bf16*>(p.st_lo)[e] = (__bf16)(s - float(hi));
+  }
+  if (blockIdx.x == 0 && threadIdx.x < D)
+    p.z[int64_t(head) * D + threadIdx.x] =
+        sum_splits(p.n_split, [&](int k) { return p.part_z[(int64_t(k) * H + head) * D + threadIdx.x]; });
+}
+
+// ---------------------------------------------------------------------------
+// Apply: out_i = phi(q_i)^T S / (phi(q_i) . z + eps)
+// ---------------------------------------------------------------------------
+// Value held by lane l ^ 32 (v_permlane32_swap; see the attention kernels).
+__device__ __forceinline__ float partner_half(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                   __builtin_bit_cast(unsigned, x), false, false);
+  const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, lane < 32 ? pr[1] : pr[0]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kApplyThreads) void lin_apply_kernel(LinArgs p) {
+  constexpr int G = D / 8;    // 16-byte granules per row of S^T
+  constexpr int NB = D / 32;  // 32-row blocks of S^T (output column blocks)
+  constexpr int RB = D * 2;
+  // S^T rows (d2), granule g stored at g ^ (d2 mod G): 16-byte reads of
+  // consecutive rows at one granule fall in distinct banks.
+  __shared__ __attribute__((aligned(16))) char sh[D * RB];
+  __shared__ __attribute__((aligned(16))) char sl[D * RB];
+  __shared__ float zs[D];
+  const AttnArgs& a = p.a;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
+
+  const int qi = blockIdx.x * kApplyBQ + wave * 32 + r32;
+  const bool q_ok = qi < a.n_q;
+  const int64_t qrow = (int64_t(qi) * a.H + head) * D;
+  // B operand: phi(q) of the lane's query at d1 = 16j + 8*half .. +7; its
+  // loads go out first, then every load of S^T, then the LDS stores.
+  bf16x8 qf[D / 16];
+  {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0});
+  }
+  {
+    constexpr int NS = D * G / kApplyThreads;  // 16-byte loads per thread per part
+    const u32x4* gh = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.st_hi) + int64_t(head) * D * D);
+    const u32x4* gl = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.st_lo) + int64_t(head) * D * D);
+    u32x4 wh[NS], wl[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      wh[i] = gh[tid + i * kApplyThreads];
+      wl[i] = gl[tid + i * kApplyThreads];
+    }
+    const float zv = tid < D ? p.z[int64_t(head) * D + tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int it = tid + i * kApplyThreads;
+      const int row = it / G, g = it % G;
+      const int o = row * RB + ((g ^ (row & (G - 1))) << 4);
+      *reinterpret_cast<u32x4*>(sh + o) = wh[i];
+      *reinterpret_cast<u32x4*>(sl + o) = wl[i];
+    }
+    if (tid < D) zs[tid] = zv;
+  }
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) qf[j] = relu8(qf[j]);
+  __syncthreads();
+
+  // normaliser phi(q) . z: this half's 64 dims, then the other half's
+  float den = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) den = fmaf(float(qf[j][i]), zs[16 * j + 8 * half + i], den);
+  den += partner_half(den);
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int row = 32 * b + r32;
+      const int off = row * RB + (((2 * j + half) ^ (row & (G - 1))) << 4);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + off);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + off);
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[j], o[b], 0, 0, 0);
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[j], o[b], 0, 0, 0);
+    }
+
+  if (!q_ok) return;
+  const float inv = 1.f / (den + p.eps);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = 32 * b + 8 * gq + 4 * half;
+      bf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[b][4 * gq + i] * inv);
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + qrow + d0) = w;
+    }
+}
+
+template <typename K>
+int launch(K kernel, dim3 grid, dim3 block, const void* arg, void* stream) {
+  void* args[] = {const_cast<void*>(arg)};
+  return int(hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0,
+                             static_cast<hipStream_t>(stream)));
+}
+
+template <int D>
+int launch_linear_d(const LinArgs& p, void* stream) {
+  int err = launch(lin_state_kernel<D>, dim3(p.n_split, p.a.H), dim3(kStateThreads), &p, stream);
+  if (err) return err;
+  err = launch(lin_reduce_kernel<D>, dim3((D / 32) * (D / 32), p.a.H), dim3(1024), &p, stream);
+  if (err || p.a.n_q <= 0) return err;
+  return launch(lin_apply_kernel<D>, dim3((p.a.n_q + kApplyBQ - 1) / kApplyBQ, p.a.H), dim3(kApplyThreads), &p,
+                stream);
+}
+
+}  // namespace
+
+int launch_linear_attention(const LinArgs& p, void* stream) {
+  return p.a.D == 64 ? launch_linear_d<64>(p, stream) : launch_linear_d<128>(p, stream);
+}
+
+}  // namespace ll

@@ -3,6 +3,7 @@
 // Every entry point validates its arguments and the cache state first and
 // returns before enqueuing anything on error (no state change).  Host state
 // advances only after a successful launch.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -464,6 +465,64 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
   a.n_seg0 = n_sink + 1;
   if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "re-encoding attention launch");
+}
+
+ll_status ll_linear_attn_workspace_bytes(const ll_cache* cache, size_t* bytes) {
+  ll::clear_error();
+  if (!cache) return fail(LL_ERR_INVALID_ARG, "cache handle is NULL");
+  if (!bytes) return fail(LL_ERR_INVALID_ARG, "bytes is NULL");
+  const ll::Geometry& g = cache->state.geom();
+  *bytes = ll::linear_workspace_layout(g.H, g.D).total;
+  return LL_OK;
+}
+
+ll_status ll_sink_window_linear_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                     const void* k_cur, const void* v_cur, int64_t n_cur, void* out,
+                                     void* work, size_t work_bytes, ll_stream_t stream) {
+  ll::clear_error();
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  if (g.act != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "the linear-attention variant supports BF16 activations");
+  if (n_q < 0 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
+  if (n_cur != 0 && n_cur != g.ctok)
+    return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
+  if (n_q > 0 && ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK)) return st;
+  if (n_cur > 0 && ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK))
+    return st;
+  const ll::LinLayout wl = ll::linear_workspace_layout(g.H, g.D);
+  if (!work || !aligned(work, 256)) return fail(LL_ERR_INVALID_ARG, "work is NULL or not 256-byte aligned");
+  if (work_bytes < wl.total)
+    return fail(LL_ERR_BUFFER_TOO_SMALL, "work needs " + std::to_string(wl.total) + " bytes");
+  ll::LinArgs p;
+  ll::AttnArgs& a = p.a;
+  int32_t keys = 0;
+  add_cache_runs(cs, layer, a, keys);
+  if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, a, keys);
+  if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
+  if (n_q == 0) return LL_OK;
+  a.n_keys = keys;
+  a.q = q;
+  a.out = out;
+  a.n_q = int32_t(n_q);
+  a.H = g.H;
+  a.D = g.D;
+  a.act = g.act;
+  // Key splits: about 8 tiles of 64 keys each, at most kLinMaxSplits.
+  int32_t n_tiles = 0;
+  for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + 63) / 64;
+  const int32_t want = std::min<int32_t>(ll::kLinMaxSplits, std::max<int32_t>(1, (n_tiles + 7) / 8));
+  p.tiles_per_split = (n_tiles + want - 1) / want;
+  p.n_split = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  char* w = static_cast<char*>(work);
+  p.part_s = reinterpret_cast<float*>(w + wl.part_s);
+  p.part_z = reinterpret_cast<float*>(w + wl.part_z);
+  p.st_hi = w + wl.st_hi;
+  p.st_lo = w + wl.st_lo;
+  p.z = reinterpret_cast<float*>(w + wl.z);
+  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
+  return launched(ll::launch_linear_attention(p, stream), "linear attention launch");
 }
 
 ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const void* v_txt,

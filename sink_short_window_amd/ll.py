@@ -26,7 +26,9 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
 # Every function include/ll.h declares (checked against the header by the tests).
 EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
            "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
-           "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_cross_attn", "ll_cache_query", "ll_cache_layout", "ll_status_str", "ll_last_error")
+           "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_sink_window_linear_attn",
+           "ll_linear_attn_workspace_bytes", "ll_cross_attn", "ll_cache_query", "ll_cache_layout",
+           "ll_status_str", "ll_last_error")
 
 
 class ll_cache_config(ctypes.Structure):
@@ -58,6 +60,8 @@ _SIGS = {
     "ll_window_reencode_attn": (_i32, [_vp, _i32, _vp, _i64, _f32, _vp, _vp, _vp]),
     "ll_sink_window_attn_bwd": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp]),
+    "ll_sink_window_linear_attn": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "ll_linear_attn_workspace_bytes": (_i32, [_vp, _P(_sz)]),
     "ll_cross_attn": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "ll_cache_query": (_i32, [_vp, _i32, _P(_i64), _P(_i32), _P(_i32), _P(_i64)]),
     "ll_cache_layout": (_i32, [_vp, _i32, _i32, _i32, _P(_sz), _P(_i64), _P(_i64)]),
@@ -207,6 +211,25 @@ def ll_window_reencode_attn(handle, layer, q, scale, out, act_dtype, lse=None, s
         _dev_ptr(lse, "lse", "float32", True), _stream(stream, q)))
 
 
+def ll_linear_attn_workspace_bytes(handle, lib=None):
+    lib = lib or load()
+    n = _sz(0)
+    _check(lib, lib.ll_linear_attn_workspace_bytes(handle, ctypes.byref(n)))
+    return n.value
+
+
+def ll_sink_window_linear_attn(handle, layer, q, k_cur, v_cur, out, work, stream=None, lib=None):
+    """Linear-attention variant (bf16).  q, out: [n_q, H, D]; k_cur/v_cur:
+    [C_tok, H, D] or None; work: a uint8 device tensor of at least
+    ll_linear_attn_workspace_bytes."""
+    lib = lib or load()
+    n_cur = 0 if k_cur is None else k_cur.shape[0]
+    _check(lib, lib.ll_sink_window_linear_attn(
+        handle, layer, _dev_ptr(q, "q", "bfloat16"), q.shape[0],
+        _dev_ptr(k_cur, "k_cur", "bfloat16", True), _dev_ptr(v_cur, "v_cur", "bfloat16", True), n_cur,
+        _dev_ptr(out, "out", "bfloat16"), _dev_ptr(work, "work", "uint8"), work.numel(), _stream(stream, q)))
+
+
 def ll_sink_window_attn_bwd(handle, layer, q, k_cur, v_cur, scale, out, lse, dout, delta, dq,
                             dk_cur=None, dv_cur=None, stream=None, lib=None):
     """Backward of ll_sink_window_attn (bf16).  q, out, dout: [n_q, H, D] bf16;
@@ -318,6 +341,13 @@ class Cache:
 
     def reencode_attn(self, layer, q, scale, out, lse=None, stream=None):
         ll_window_reencode_attn(self.handle, layer, q, scale, out, self.cfg.act_dtype, lse, stream)
+
+    def linear_attn(self, layer, q, k_cur, v_cur, out, stream=None):
+        """Linear-attention variant; allocates (once) and reuses a workspace."""
+        if getattr(self, "_lin_work", None) is None:
+            n = ll_linear_attn_workspace_bytes(self.handle)
+            self._lin_work = _torch().empty(n, dtype=_torch().uint8, device=self.buf.device)
+        ll_sink_window_linear_attn(self.handle, layer, q, k_cur, v_cur, out, self._lin_work, stream)
 
     def reset(self):
         ll_cache_reset(self.handle)

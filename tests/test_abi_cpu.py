@@ -37,6 +37,7 @@ def libs():
     stub.llh_last_bwd.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     stub.llh_last_stage.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int64)]
+    stub.llh_last_lin.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     return stub
 
 
@@ -432,6 +433,73 @@ def test_backward_validation_and_launch(libs):
     libs.ll_cache_destroy(h2)
     h3 = create(libs, cfg())
     assert status(libs, libs.ll_sink_window_attn_bwd(h3, *args(layer=0, n_cur=0, k=None, v=None))) \
+        == "LL_ERR_BAD_STATE"
+    libs.ll_cache_destroy(h3)
+
+
+def test_linear_attention_validation_and_launch(libs):
+    """The linear-attention variant takes the softmax call's run table, splits
+    the key tiles into at most 32 ranges covering every tile once, carves its
+    workspace as documented, is bf16-only and checks every argument before
+    launching."""
+    c = cfg(L=2, T=4, C=2, S=2, W=6, H=3, D=64)
+    h = create(libs, c)
+    ct = 8
+    A = FAKE_ACT
+    need = ll.ll_linear_attn_workspace_bytes(h, lib=libs)
+    H, D, up = 3, 64, lambda x: (x + 255) // 256 * 256
+    parts = [up(32 * H * D * D * 4), up(32 * H * D * 4), up(H * D * D * 2), up(H * D * D * 2), up(H * D * 4)]
+    assert need == sum(parts)
+    W0 = FAKE_ACT + (1 << 26)
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("layer", 1), ("q", A), ("n_q", 5), ("k", A), ("v", A), ("n_cur", ct), ("out", A),
+        ("work", W0), ("work_bytes", need))] + [None]
+    call = lambda **kw: status(libs, libs.ll_sink_window_linear_attn(h, *args(**kw)))
+    for _ in range(3):
+        assert libs.ll_cache_append_chunk(h, 1, A, A, None) == 0
+    calls = libs.llh_lin_calls()
+    assert call() == "LL_OK" and libs.llh_lin_calls() == calls + 1
+    nk = ctypes.c_int64()
+    runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+    n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+    tps = ctypes.c_int32()
+    ptrs = (ctypes.c_int64 * 5)()
+    n_split = libs.llh_last_lin(ctypes.byref(tps), ptrs)
+    n_tiles = sum((runs[RUN_FIELDS * i + 5] + 63) // 64 for i in range(n_seg))
+    assert 1 <= n_split <= 32 and (n_split - 1) * tps.value < n_tiles <= n_split * tps.value
+    offs = [W0]
+    for b in parts[:-1]:
+        offs.append(offs[-1] + b)
+    assert list(ptrs) == offs
+    libs.ll_sink_window_attn(h, 1, A, 5, A, A, ct, 0.1, A, None, None)   # same key set as softmax
+    nk2 = ctypes.c_int64()
+    runs2 = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+    assert libs.llh_last_attn(ctypes.byref(nk2), runs2) == n_seg and nk.value == nk2.value
+    assert list(runs[:RUN_FIELDS * n_seg]) == list(runs2[:RUN_FIELDS * n_seg])
+    assert call(n_cur=0, k=None, v=None) == "LL_OK"
+    assert call(n_q=0) == "LL_OK"
+    for bad, code in ((dict(n_cur=ct - 1), "LL_ERR_INVALID_ARG"), (dict(q=None), "LL_ERR_INVALID_ARG"),
+                      (dict(out=A + 2), "LL_ERR_INVALID_ARG"), (dict(k=None), "LL_ERR_INVALID_ARG"),
+                      (dict(work=None), "LL_ERR_INVALID_ARG"), (dict(work=W0 + 64), "LL_ERR_INVALID_ARG"),
+                      (dict(work_bytes=need - 1), "LL_ERR_BUFFER_TOO_SMALL"), (dict(layer=2), "LL_ERR_INVALID_ARG"),
+                      (dict(n_q=-1), "LL_ERR_INVALID_ARG")):
+        calls = libs.llh_lin_calls()
+        assert call(**bad) == code, bad
+        assert libs.llh_lin_calls() == calls
+    libs.llh_fail_next_launch()
+    assert call() == "LL_ERR_HIP"
+    libs.ll_cache_destroy(h)
+    h2 = create(libs, cfg(act=ll.LL_F32, kv=ll.LL_F32))
+    assert status(libs, libs.ll_sink_window_linear_attn(h2, *args(layer=0))) == "LL_ERR_UNSUPPORTED"
+    libs.ll_cache_destroy(h2)
+    h2 = create(libs, cfg(kv=ll.LL_I8))            # int8 cache: staged, then the bf16 kernels
+    stages = libs.llh_stage_calls()
+    assert libs.ll_cache_append_chunk(h2, 0, A, A, None) == 0
+    assert status(libs, libs.ll_sink_window_linear_attn(h2, *args(layer=0))) == "LL_OK"
+    assert libs.llh_stage_calls() == stages + 1
+    libs.ll_cache_destroy(h2)
+    h3 = create(libs, cfg())
+    assert status(libs, libs.ll_sink_window_linear_attn(h3, *args(layer=0, n_cur=0, k=None, v=None))) \
         == "LL_ERR_BAD_STATE"
     libs.ll_cache_destroy(h3)
 
