@@ -20,7 +20,7 @@
 //   lin_reduce_kernel  sums the partials in a fixed order (deterministic) and
 //                      stores S transposed as a bf16 pair hi + lo (hi = bf16(S),
 //                      lo = bf16(S - hi)), which keeps ~16 significant bits.
-//   lin_apply_kernel   per 256 queries of one head: O^T = S^T phi(Q)^T as two
+//   lin_apply_kernel   per 128 queries of one head: O^T = S^T phi(Q)^T as two
 //                      MFMA sums (hi and lo), the normaliser phi(q) . z on the
 //                      VALU, bf16 output.
 
@@ -41,8 +41,8 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kTile = 64;          // keys per LDS tile
 constexpr int kStateThreads = 256;  // 4 waves
-constexpr int kApplyThreads = 512;  // 8 waves x 32 queries
-constexpr int kApplyBQ = 256;
+constexpr int kApplyThreads = 256;  // 4 waves x 32 queries (two workgroups fit a CU)
+constexpr int kApplyBQ = 128;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -325,11 +325,17 @@ __global__ __launch_bounds__(kApplyThreads) void lin_apply_kernel(LinArgs p) {
   constexpr int G = D / 8;    // 16-byte granules per row of S^T
   constexpr int NB = D / 32;  // 32-row blocks of S^T (output column blocks)
   constexpr int RB = D * 2;
+  constexpr int kWaves = kApplyThreads / 64;
+  constexpr int kSBytes = D * RB;            // one part (hi or lo) of S^T
+  constexpr int kOBytes = kWaves * 32 * RB;  // output staging, 32 rows per wave
+  constexpr int kLds = 2 * kSBytes > kOBytes ? 2 * kSBytes : kOBytes;
   // S^T rows (d2), granule g stored at g ^ (d2 mod G): 16-byte reads of
-  // consecutive rows at one granule fall in distinct banks.
-  __shared__ __attribute__((aligned(16))) char sh[D * RB];
-  __shared__ __attribute__((aligned(16))) char sl[D * RB];
+  // consecutive rows at one granule fall in distinct banks.  The same memory
+  // stages the output once every wave is done with S^T.
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ float zs[D];
+  char* const sh = lds;
+  char* const sl = lds + kSBytes;
   const AttnArgs& a = p.a;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -396,18 +402,38 @@ __global__ __launch_bounds__(kApplyThreads) void lin_apply_kernel(LinArgs p) {
       o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[j], o[b], 0, 0, 0);
     }
 
-  if (!q_ok) return;
+  // Output through LDS: the lane's 4-dim pieces of its query row go into the
+  // wave's 32-row block, which is read back as whole rows, so that each
+  // global store covers complete rows of out.  Row r keeps granule g at
+  // g ^ sw(r) and its 8-byte half s at s ^ (bit 4 of r): the writes (32
+  // rows at one granule) and the row reads are both free of bank conflicts.
   const float inv = 1.f / (den + p.eps);
+  auto sw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  char* const ob = lds + wave * 32 * RB;
+  __syncthreads();  // every wave's reads of S^T are done
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int d0 = 32 * b + 8 * gq + 4 * half;
       bf16x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[b][4 * gq + i] * inv);
-      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + qrow + d0) = w;
+      const int g = 4 * b + gq;
+      *reinterpret_cast<bf16x4*>(ob + r32 * RB + ((g ^ sw(r32)) << 4) + ((half ^ (r32 >> 4)) << 3)) = w;
     }
+  __syncthreads();
+  constexpr int RPI = 64 / G;  // rows per 64-lane read
+  const int gg = lane % G;
+  const int64_t obase = (int64_t(blockIdx.x) * kApplyBQ + wave * 32) * a.H + head;
+  const int q = blockIdx.x * kApplyBQ + wave * 32;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = k * RPI + lane / G;
+    u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * RB + ((gg ^ sw(row)) << 4));
+    if ((k * RPI) & 16) v = u32x4{v[2], v[3], v[0], v[1]};  // rows 16..31 hold their halves swapped
+    if (q + row < a.n_q)
+      *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.out) + (obase + int64_t(row) * a.H) * D + gg * 8) = v;
+  }
 }
 
 template <typename K>
