@@ -121,6 +121,7 @@ struct StageArgs {
 // max(x, 0).  The workspace pointers are parts of the caller's buffer
 // (linear_workspace_layout).
 constexpr int kLinMaxSplits = 32;
+constexpr int kComputeUnits = 256;  // MI355X (gfx950): 8 XCDs x 32 CUs
 struct LinArgs {
   AttnArgs a;                 // runs, q, out, n_q, H, D (scale and lse unused)
   float* part_s = nullptr;    // [n_split][H][D][D] fp32, [d1][d2]

@@ -14,9 +14,12 @@
 //   lin_state_kernel   per (key split, head): partial S and z over a range of
 //                      64-key tiles; bf16 MFMA 32x32x16 with A = phi(K)^T
 //                      (transpose reads of the row-major K tile, then max(., 0))
-//                      and B = V (rows of the transposed V tile); z is the same
-//                      product with B = ones.  Keys past a run's end read as
-//                      zero, so they add nothing and need no mask.
+//                      and B = V (rows of the cache's transposed V tile, or
+//                      transpose reads of a row-major V tile); z is the same
+//                      product with B = ones.  Two load waves fill a 4-stage
+//                      LDS ring by direct-to-LDS buffer loads, three tiles
+//                      ahead of the four MFMA waves.  Keys past a run's end
+//                      read as zero, so they add nothing and need no mask.
 //   lin_reduce_kernel  sums the partials in a fixed order (deterministic) and
 //                      stores S transposed as a bf16 pair hi + lo (hi = bf16(S),
 //                      lo = bf16(S - hi)), which keeps ~16 significant bits.
@@ -40,7 +43,9 @@ typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned)))
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kTile = 64;          // keys per LDS tile
-constexpr int kStateThreads = 256;  // 4 waves
+constexpr int kStateWaves = 6;      // state kernel: 4 MFMA waves + 2 load waves
+constexpr int kStateThreads = 64 * kStateWaves;
+constexpr int kStateStages = 4;     // LDS ring depth of the state kernel
 constexpr int kApplyThreads = 256;  // 4 waves x 32 queries (two workgroups fit a CU)
 constexpr int kApplyBQ = 128;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -66,27 +71,29 @@ __device__ __forceinline__ bf16x8 relu8(bf16x8 x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Column p of a transposed V tile holds key p with bits 2 and 3 swapped: the
-// order in which an MFMA k-block of 16 keys is split between the two half
-// waves (keys 0..3, 8..11 in half 0; 4..7, 12..15 in half 1).
-__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+// Key order (vt_key): column p of the cache's transposed V tiles holds key p
+// with bits 2 and 3 swapped, the order in which an MFMA k-block of 16 keys is
+// split between the two half waves (keys 0..3, 8..11 in half 0; 4..7, 12..15
+// in half 1).  The transpose reads of row-major tiles produce the same order.
 
-// Row-major [64][D] K tile, read by transpose reads (per 32 lanes: 4
-// consecutive rows x 4 granules).  D = 128: granule g of row r at
-// g ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3), which spreads those 16
-// (row, granule) pairs over all 64 banks.  D = 64: rows padded by 32 bytes.
+// Row-major [64][D] tile (K, or a row-major V), unpadded so that direct-to-LDS
+// loads can fill it, read by transpose reads (per 32 lanes: 4 consecutive
+// rows x 4 granules).  Granule g of row r sits at g ^ f(r), which spreads those
+// 16 (row, granule) pairs over all 64 banks: D = 128 (256-byte rows):
+// f(r) = ((r & 3) << 2) | ((r >> 2) & 3); D = 64 (128-byte rows, two per bank
+// sweep): f(r) = 4 * (bit 1 of r).
 template <int D>
 struct KTile {
-  static constexpr bool kSwz = D == 128;
-  static constexpr int RB = kSwz ? D * 2 : (D + 16) * 2;
+  static constexpr int RB = D * 2;
   static constexpr int kBytes = kTile * RB;
-  static __device__ __forceinline__ int off(int row, int gran) {
-    if constexpr (kSwz) return row * RB + ((gran ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
-    else return row * RB + gran * 16;
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return ((row >> 1) & 1) << 2;
   }
+  static __device__ __forceinline__ int off(int row, int gran) { return row * RB + ((gran ^ swz(row)) << 4); }
 };
 
-// Transposed [D][64] V tile (128-byte rows, column order vt_key), read by
+// Transposed [D][64] V tile (128-byte rows, columns in vt_key order), read by
 // 16-byte row reads of 32 consecutive rows; granule g of row d at
 // g ^ ((d >> 1) & 7).
 template <int D>
@@ -99,32 +106,132 @@ struct VTile {
 // ---------------------------------------------------------------------------
 // State: partial S and z of one key split
 // ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(N): this wave's oldest loads up to all but N have landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, so the
+// ring's direct-to-LDS loads stay in flight across it.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Position (run, first key) of a tile in the sequence of 64-key tiles over
+// the runs; all fields are uniform.
+struct TileCursor {
+  int run = 0, t0 = 0;
+  __device__ void seek(const AttnArgs& a, int t) {
+    run = 0;
+    for (;;) {
+      const int nt = (a.seg[run].len + kTile - 1) / kTile;
+      if (t < nt) break;
+      t -= nt;
+      ++run;
+    }
+    t0 = t * kTile;
+  }
+  __device__ void next(const AttnArgs& a) {
+    t0 += kTile;
+    if (t0 >= a.seg[run].len) {
+      ++run;
+      t0 = 0;
+    }
+  }
+};
+
+// A wave's LDS reads wait behind its own direct-to-LDS loads still in flight,
+// so the roles are split: waves 4 and 5 only load (K and V of tile j + 3 into
+// the ring stage that tile j - 1 left), waves 0..3 only read LDS and issue
+// MFMAs.  One workgroup barrier per tile both publishes tile j (each load
+// wave waits for its part of it first) and frees the stage of tile j - 1.
 template <int D>
 __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
   using KT = KTile<D>;
   using VT = VTile<D>;
-  constexpr int NV = D / 8;           // 16-byte vectors per K row
-  constexpr int NB = D / 32;          // 32-wide blocks of S per dimension
-  constexpr int NPW = NB * NB / 4;    // S blocks per wave (4 waves)
-  constexpr int NL = kTile * NV / kStateThreads;  // 16-byte loads per thread per side
-  static_assert(NPW >= 1 && NL >= 1, "shape");
-  __shared__ __attribute__((aligned(16))) char ks2[2][KT::kBytes];
-  __shared__ __attribute__((aligned(16))) char vs2[2][VT::kBytes];
+  constexpr int G = D / 8;                        // 16-byte granules per K row
+  constexpr int NB = D / 32;                      // 32-wide blocks of S per dimension
+  constexpr int NPW = NB * NB / 4;                // S blocks per MFMA wave
+  constexpr int RPI = 1024 / KT::RB;              // rows per 1 KB load
+  constexpr int NI = KT::kBytes / 1024;           // 1 KB loads per operand and tile
+  constexpr int kStage = KT::kBytes + VT::kBytes;
+  static_assert(NPW >= 1 && 2 * NI < 64 && KT::kBytes == VT::kBytes, "shape");
+  __shared__ __attribute__((aligned(16))) char ring[kStateStages * kStage];
   const AttnArgs& a = p.a;
   const int split = blockIdx.x;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int d1b = (wave * NPW) / NB;           // this wave's row block of S
-  const int d2b0 = (wave * NPW) % NB;          // and its first column block
-  const bool do_z = d2b0 == 0;
+  const int lane = tid & 63, r32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // This split's tiles [tb, te) of the tile sequence over the runs.
+  // This split's tiles [tb, tb + n_loc) of the tile sequence over the runs.
   int n_tiles = 0;
   for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + kTile - 1) / kTile;
   const int tb = split * p.tiles_per_split;
-  const int te = min(n_tiles, tb + p.tiles_per_split);
+  const int n_loc = min(n_tiles, tb + p.tiles_per_split) - tb;
 
+  if (wave >= 4) {
+    // Load wave: 4 -> K, 5 -> V.
+    if (n_loc <= 0) return;
+    const bool v_side = wave == 5;
+    TileCursor c;
+    c.seek(a, tb);
+    auto issue = [&](int st) {
+      const KvSeg& sg = a.seg[c.run];
+      const int len = sg.len;
+      const uint32_t rs = uint32_t(sg.row_stride) * 2;
+      char* dst = ring + st * kStage + (v_side ? KT::kBytes : 0);
+      if (v_side && sg.v_tiled) {
+        // the cache's [D][64] tile: 8 rows of 128 bytes per 1 KB load
+        const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
+        const auto rv = rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2,
+                             tiles * kTile * D * 2);
+        const uint32_t tbase = uint32_t(c.t0 / kTile) * kTile * D * 2;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int d = i * 8 + (lane >> 3);
+          const uint32_t off = tbase + uint32_t(d * VT::RB + (((lane & 7) ^ ((d >> 1) & 7)) << 4));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + i * 1024), 16, off, 0, 0, 0);
+        }
+      } else {
+        // row-major rows: lane -> (row, stored granule); it fetches the
+        // logical granule that belongs there (the XOR is its own inverse)
+        const void* base = v_side ? sg.v : sg.k;
+        const auto rr = rsrc(static_cast<const char*>(base) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int row = i * RPI + lane / G;
+          const uint32_t off = uint32_t(c.t0 + row) * rs + (uint32_t((lane % G) ^ KT::swz(row)) << 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + i * 1024), 16, off, 0, 0, 0);
+        }
+      }
+      c.next(a);
+    };
+    for (int j = 0; j < kStateStages - 1 && j < n_loc; ++j) issue(j);
+    for (int j = 0; j < n_loc; ++j) {
+      // tile j has landed once only the tiles issued after it are in flight
+      const int after = min(kStateStages - 2, n_loc - 1 - j);
+      if (after >= 2) wait_vmcnt<2 * NI>();
+      else if (after == 1) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+      wg_barrier();
+      if (j + kStateStages - 1 < n_loc) issue((j + kStateStages - 1) % kStateStages);
+    }
+    return;
+  }
+
+  // MFMA wave: S blocks (d1b, d2b0 .. d2b0 + NPW - 1); z with the first.
+  const int d1b = (wave * NPW) / NB;
+  const int d2b0 = (wave * NPW) % NB;
+  const bool do_z = d2b0 == 0;
   f32x16 acc[NPW], zacc;
 #pragma unroll
   for (int i = 0; i < NPW; ++i)
@@ -133,117 +240,63 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) zacc[r] = 0.f;
 
-  if (tb < te) {
-    // A operand (phi(K)^T, rows = tile columns 32*d1b + r32): two transpose
-    // reads per 16-key step, k order 16*step + {0..3, 8..11} (half 0) or
-    // {4..7, 12..15} (half 1), the vt_key order of the V tile's columns.
-    int toff[2];
-    {
+  if (n_loc > 0) {
+    // Transpose-read offsets inside a row-major tile, per 16-key step: lane
+    // r32 takes column 32*blk + r32 at keys {0..3, 8..11} (half 0) or
+    // {4..7, 12..15} (half 1), the vt_key order of the V^T tiles' columns.
+    auto tr_off = [&](int blk, int aa) {
       const int g16 = lane >> 4, j16 = lane & 15;
+      const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
+      const int col = 32 * blk + 16 * (g16 & 1) + 4 * (j16 & 3);
+      return KT::off(row, col >> 3) + (col & 7) * 2;
+    };
+    const int ka0 = tr_off(d1b, 0), ka1 = tr_off(d1b, 1);
+    int vb0[NPW], vb1[NPW];
 #pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
-        const int col = 32 * d1b + 16 * (g16 & 1) + 4 * (j16 & 3);
-        toff[aa] = KT::off(row, col >> 3) + (col & 7) * 2;
-      }
+    for (int i = 0; i < NPW; ++i) {
+      vb0[i] = tr_off(d2b0 + i, 0);
+      vb1[i] = tr_off(d2b0 + i, 1);
     }
-    // B operand (V rows d2 = 32*d2b + r32 at columns 16*step + 8*half..+7).
+    // V^T tile rows d2 = 32*d2b + r32 at columns 16*step + 8*half .. +7.
     const int vrow = r32 * VT::RB;
     const int vx = (r32 >> 1) & 7;  // the row's granule swizzle (32*d2b keeps it)
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-
-    // The next tile's loads, held in registers from issue to LDS store.
-    u32x4 kreg[NL], vreg[NL];
-    bool vt_reg = false;
-    // Position (run, first key) of tile t in the run sequence.
-    auto locate = [&](int t, int& run, int& t0) {
-      run = 0;
-      for (;;) {
-        const int nt = (a.seg[run].len + kTile - 1) / kTile;
-        if (t < nt) break;
-        t -= nt;
-        ++run;
-      }
-      t0 = t * kTile;
-    };
-    auto issue = [&](int run, int t0) {
-      const KvSeg& sg = a.seg[run];
-      const int len = sg.len;
-      const uint32_t rs = uint32_t(sg.row_stride) * 2;
-      const auto rk = rsrc(static_cast<const char*>(sg.k) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
-      const bool vt = sg.v_tiled != 0;
-      vt_reg = vt;
-      const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
-      const auto rv = vt ? rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2,
-                                    tiles * kTile * D * 2)
-                             : rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2,
-                                    uint32_t(len) * rs);
-      const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
+    TileCursor c;
+    c.seek(a, tb);
+    for (int j = 0; j < n_loc; ++j) {
+      wg_barrier();
+      const int st = j % kStateStages;
+      const char* ks = ring + st * kStage;
+      const char* vs = ks + KT::kBytes;
+      if (a.seg[c.run].v_tiled) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int it = tid + i * kStateThreads;
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + it / NV) * rs + (it % NV) * 16, 0, 0);
-        // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or
-        // row-major rows with the key in the low bits of it (see stage)
-        vreg[i] = vt ? __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + (it >> 3) * 128 + (it & 7) * 16, 0, 0)
-                           : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + it % kTile) * rs + it / kTile * 16, 0, 0);
-      }
-    };
-    auto stage = [&](char* kbuf, char* vbuf) {
+        for (int step = 0; step < kTile / 16; ++step) {
+          const char* kb = ks + 16 * step * KT::RB;
+          const bf16x8 fa = relu8(__builtin_shufflevector(tr_read(kb + ka0), tr_read(kb + ka1), 0, 1, 2, 3, 4, 5, 6, 7));
+          const int g = ((2 * step) ^ (vx & 6)) | (half ^ (vx & 1));
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int it = tid + i * kStateThreads;
-        *reinterpret_cast<u32x4*>(kbuf + KT::off(it / NV, it % NV)) = kreg[i];
-        if (vt_reg) {
-          *reinterpret_cast<u32x4*>(vbuf + VT::off(it >> 3, it & 7)) = vreg[i];
-        } else {
-          // one key per lane: each 2-byte store fills one 128-byte row of the
-          // transposed tile (key -> column vt_key(key))
-          const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
-          const int key = it % kTile, vv = it / kTile;
-          const int c = vt_key(key);
+          for (int i = 0; i < NPW; ++i) {
+            const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vs + (32 * (d2b0 + i)) * VT::RB + vrow + (g << 4));
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, vb, acc[i], 0, 0, 0);
+          }
+          if (do_z) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, ones, zacc, 0, 0, 0);
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<__bf16*>(vbuf + VT::off(vv * 8 + e, c >> 3) + (c & 7) * 2) = b[e];
+        for (int step = 0; step < kTile / 16; ++step) {
+          const char* kb = ks + 16 * step * KT::RB;
+          const char* vbp = vs + 16 * step * KT::RB;
+          const bf16x8 fa = relu8(__builtin_shufflevector(tr_read(kb + ka0), tr_read(kb + ka1), 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int i = 0; i < NPW; ++i) {
+            const bf16x8 vb = __builtin_shufflevector(tr_read(vbp + vb0[i]), tr_read(vbp + vb1[i]), 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, vb, acc[i], 0, 0, 0);
+          }
+          if (do_z) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, ones, zacc, 0, 0, 0);
         }
       }
-    };
-
-    // Issue cursor: the next tile whose loads go out.
-    int run, t0;
-    locate(tb, run, t0);
-    auto issue_next = [&]() {
-      issue(run, t0);
-      t0 += kTile;
-      if (t0 >= a.seg[run].len) {
-        ++run;
-        t0 = 0;
-      }
-    };
-    issue_next();
-    stage(ks2[0], vs2[0]);
-    __syncthreads();
-    for (int t = tb; t < te; ++t) {
-      const int buf = (t - tb) & 1;
-      if (t + 1 < te) issue_next();  // tile t+1, in flight during this tile's MFMAs
-      const char* ks = ks2[buf];
-      const char* vs = vs2[buf];
-#pragma unroll
-      for (int step = 0; step < kTile / 16; ++step) {
-        const char* kb = ks + 16 * step * KT::RB;
-        const bf16x8 fa = relu8(__builtin_shufflevector(tr_read(kb + toff[0]), tr_read(kb + toff[1]),
-                                                         0, 1, 2, 3, 4, 5, 6, 7));
-        const int g = ((2 * step) ^ (vx & 6)) | (half ^ (vx & 1));
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vs + (32 * (d2b0 + i)) * VT::RB + vrow + (g << 4));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, vb, acc[i], 0, 0, 0);
-        }
-        if (do_z) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, ones, zacc, 0, 0, 0);
-      }
-      if (t + 1 < te) stage(ks2[buf ^ 1], vs2[buf ^ 1]);
-      __syncthreads();
+      c.next(a);
     }
   }
 

@@ -509,10 +509,11 @@ ll_status ll_sink_window_linear_attn(const ll_cache* cache, int32_t layer, const
   a.H = g.H;
   a.D = g.D;
   a.act = g.act;
-  // Key splits: about 8 tiles of 64 keys each, at most kLinMaxSplits.
+  // Key splits: one state workgroup per compute unit over all heads (its
+  // 128 KB LDS ring holds one per CU), at most kLinMaxSplits and n_tiles.
   int32_t n_tiles = 0;
   for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + 63) / 64;
-  const int32_t want = std::min<int32_t>(ll::kLinMaxSplits, std::max<int32_t>(1, (n_tiles + 7) / 8));
+  const int32_t want = std::min<int32_t>({ll::kLinMaxSplits, n_tiles, std::max<int32_t>(1, ll::kComputeUnits / g.H)});
   p.tiles_per_split = (n_tiles + want - 1) / want;
   p.n_split = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   char* w = static_cast<char*>(work);
