@@ -131,19 +131,17 @@ struct TileCursor {
   int run = 0, t0 = 0;
   __device__ void seek(const AttnArgs& a, int t) {
     run = 0;
-    for (;;) {
-      const int nt = (a.seg[run].len + kTile - 1) / kTile;
-      if (t < nt) break;
-      t -= nt;
-      ++run;
-    }
     t0 = t * kTile;
+    skip(a, 0);
   }
-  __device__ void next(const AttnArgs& a) {
-    t0 += kTile;
-    if (t0 >= a.seg[run].len) {
+  // Moves k tiles on (a run's last tile may be partial).
+  __device__ void skip(const AttnArgs& a, int k) {
+    t0 += k * kTile;
+    while (run < a.n_seg) {
+      const int span = (a.seg[run].len + kTile - 1) / kTile * kTile;
+      if (t0 < span) break;
+      t0 -= span;
       ++run;
-      t0 = 0;
     }
   }
 };
@@ -172,18 +170,20 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
   const int lane = tid & 63, r32 = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // This split's tiles [tb, tb + n_loc) of the tile sequence over the runs.
+  // This split's tiles split, split + n_split, ... of the tile sequence over
+  // the runs: interleaved, so every split gets the same mix of the cache's
+  // transposed V tiles and the current chunk's row-major ones (which need
+  // more LDS reads).
   int n_tiles = 0;
   for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + kTile - 1) / kTile;
-  const int tb = split * p.tiles_per_split;
-  const int n_loc = min(n_tiles, tb + p.tiles_per_split) - tb;
+  const int n_loc = split < n_tiles ? (n_tiles - split + p.n_split - 1) / p.n_split : 0;
 
   if (wave >= 4) {
     // Load wave: 4 -> K, 5 -> V.
     if (n_loc <= 0) return;
     const bool v_side = wave == 5;
     TileCursor c;
-    c.seek(a, tb);
+    c.seek(a, split);
     auto issue = [&](int st) {
       const KvSeg& sg = a.seg[c.run];
       const int len = sg.len;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + i * 1024), 16, off, 0, 0, 0);
         }
       }
-      c.next(a);
+      c.skip(a, p.n_split);
     };
     for (int j = 0; j < kStateStages - 1 && j < n_loc; ++j) issue(j);
     for (int j = 0; j < n_loc; ++j) {
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
     TileCursor c;
-    c.seek(a, tb);
+    c.seek(a, split);
     for (int j = 0; j < n_loc; ++j) {
       wg_barrier();
       const int st = j % kStateStages;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
           if (do_z) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, ones, zacc, 0, 0, 0);
         }
       }
-      c.next(a);
+      c.skip(a, p.n_split);
     }
   }
 
