@@ -513,9 +513,9 @@ ll_status ll_sink_window_linear_attn(const ll_cache* cache, int32_t layer, const
   // 128 KB LDS ring holds one per CU), at most kLinMaxSplits and n_tiles.
   int32_t n_tiles = 0;
   for (int r = 0; r < a.n_seg; ++r) n_tiles += (a.seg[r].len + 63) / 64;
-  const int32_t want = std::min<int32_t>({ll::kLinMaxSplits, n_tiles, std::max<int32_t>(1, ll::kComputeUnits / g.H)});
-  p.tiles_per_split = (n_tiles + want - 1) / want;
-  p.n_split = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  // Split s sums tiles s, s + n_split, ... (at most tiles_per_split of them).
+  p.n_split = std::min<int32_t>({ll::kLinMaxSplits, n_tiles, std::max<int32_t>(1, ll::kComputeUnits / g.H)});
+  p.tiles_per_split = (n_tiles + p.n_split - 1) / p.n_split;
   char* w = static_cast<char*>(work);
   p.part_s = reinterpret_cast<float*>(w + wl.part_s);
   p.part_z = reinterpret_cast<float*>(w + wl.part_z);

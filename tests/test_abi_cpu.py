@@ -466,7 +466,9 @@ def test_linear_attention_validation_and_launch(libs):
     ptrs = (ctypes.c_int64 * 5)()
     n_split = libs.llh_last_lin(ctypes.byref(tps), ptrs)
     n_tiles = sum((runs[RUN_FIELDS * i + 5] + 63) // 64 for i in range(n_seg))
-    assert 1 <= n_split <= 32 and (n_split - 1) * tps.value < n_tiles <= n_split * tps.value
+    # splits: one state workgroup per CU over the heads (256 / H), at most 32
+    # and at most one per tile; split s sums tiles s, s + n_split, ...
+    assert n_split == min(32, n_tiles, max(1, 256 // H)) and tps.value == -(-n_tiles // n_split)
     offs = [W0]
     for b in parts[:-1]:
         offs.append(offs[-1] + b)

@@ -67,10 +67,11 @@ def test_linear_stream_int8_cache():
 @pytest.mark.parametrize("H,D", [(2, 128), (32, 128), (40, 64)])
 def test_linear_many_tiles_several_splits(H, D):
     """700-token chunks, 2 sink chunks and 3 ring slots: 55 ragged 64-key tiles
-    in 5 runs at the last chunk.  The key splits (about 256 / H of them) hold
-    2 tiles at H = 2 and 7 or 8 at H = 32 and 40, so the state kernel's 4-stage
-    LDS ring wraps and one split crosses runs and V layouts (the cache's
-    transposed tiles, the current chunk's rows)."""
+    in 5 runs at the last chunk.  The key splits (min(32, tiles, 256 / H) of
+    them, split s taking tiles s, s + n_split, ...) hold 1 or 2 tiles at H = 2
+    and 7 to 10 at H = 32 and 40, so the state kernel's 4-stage LDS ring wraps
+    and one split crosses runs and V layouts (the cache's transposed tiles,
+    the current chunk's rows)."""
     run_linear_stream(313 + H, 350, 2, 4, 8, H, D, 5)
 
 
