@@ -124,7 +124,7 @@ constexpr int kLinMaxSplits = 32;
 constexpr int kComputeUnits = 256;  // MI355X (gfx950): 8 XCDs x 32 CUs
 struct LinArgs {
   AttnArgs a;                 // runs, q, out, n_q, H, D (scale and lse unused)
-  float* part_s = nullptr;    // [n_split][H][D][D] fp32, [d1][d2]
+  float* part_s = nullptr;    // [n_split][H][D][D] fp32, transposed: [d2][d1]
   float* part_z = nullptr;    // [n_split][H][D] fp32
   void* st_hi = nullptr;      // [H][D][D] bf16: S transposed ([d2][d1]), high part
   void* st_lo = nullptr;      // [H][D][D] bf16: S - hi, rounded

@@ -20,9 +20,10 @@
 //                      LDS ring by direct-to-LDS buffer loads, three tiles
 //                      ahead of the four MFMA waves.  Keys past a run's end
 //                      read as zero, so they add nothing and need no mask.
-//   lin_reduce_kernel  sums the partials in a fixed order (deterministic) and
-//                      stores S transposed as a bf16 pair hi + lo (hi = bf16(S),
-//                      lo = bf16(S - hi)), which keeps ~16 significant bits.
+//   lin_reduce_kernel  sums the partials (written transposed) elementwise in a
+//                      fixed order (deterministic) and stores S^T as a bf16
+//                      pair hi + lo (hi = bf16(S), lo = bf16(S - hi)), which
+//                      keeps ~16 significant bits.
 //   lin_apply_kernel   per 128 queries of one head: O^T = S^T phi(Q)^T as two
 //                      MFMA sums (hi and lo), the normaliser phi(q) . z on the
 //                      VALU, bf16 output.
@@ -39,6 +40,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -300,15 +302,16 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
     }
   }
 
-  // Partial S rows d1 = 32*d1b + 8*(r >> 2) + 4*half + (r & 3), column
-  // d2 = 32*d2b + r32; z from column 0 of zacc.
+  // Partial S, stored transposed ([d2][d1], the layout the apply kernel
+  // reads): acc[i][4g + e] is d1 = 32*d1b + 8g + 4*half + e, d2 =
+  // 32*(d2b0 + i) + r32, so each lane stores 4 consecutive d1 at once.
   float* ps = p.part_s + (int64_t(split) * a.H + head) * D * D;
 #pragma unroll
   for (int i = 0; i < NPW; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d1 = 32 * d1b + 8 * (r >> 2) + 4 * half + (r & 3);
-      ps[d1 * D + 32 * (d2b0 + i) + r32] = acc[i][r];
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = {acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(ps + (32 * (d2b0 + i) + r32) * D + 32 * d1b + 8 * g + 4 * half) = v;
     }
   if (do_z && r32 == 0) {
     float* pz = p.part_z + (int64_t(split) * a.H + head) * D;
@@ -318,48 +321,48 @@ __global__ __launch_bounds__(kStateThreads) void lin_state_kernel(LinArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Reduce: S = sum of the partials (split order), stored transposed as bf16
-// hi + lo; z likewise in fp32.  One workgroup per 32 x 32 tile of S, one
-// element per thread: rows of the partials are read coalesced, summed, and
-// written transposed through an LDS tile so the bf16 stores are coalesced too.
+// Reduce: S^T = sum of the transposed partials in split order, stored as
+// bf16 hi + lo; z likewise in fp32.  Elementwise: each thread sums one
+// 16-byte group of 4 floats over the splits with every load in flight at once
+// (a fixed order, so the result is deterministic).
 // ---------------------------------------------------------------------------
-// Sum of x(0) .. x(n-1), n <= kLinMaxSplits, in a fixed order (k ascending)
-// with every load in flight at once.
-template <typename F>
-__device__ __forceinline__ float sum_splits(int n, F x) {
-  float v[kLinMaxSplits];
-#pragma unroll
-  for (int k = 0; k < kLinMaxSplits; ++k) v[k] = k < n ? x(k) : 0.f;
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < kLinMaxSplits; ++k) s += v[k];
-  return s;
-}
+constexpr int kReduceThreads = 128;
 
 template <int D>
-__global__ __launch_bounds__(1024) void lin_reduce_kernel(LinArgs p) {
-  constexpr int NB = D / 32;
-  __shared__ float t[32][33];
-  const int head = blockIdx.y;
+__global__ __launch_bounds__(kReduceThreads) void lin_reduce_kernel(LinArgs p) {
   const int H = p.a.H;
-  const int b1 = blockIdx.x / NB, b2 = blockIdx.x % NB;  // tile rows d1, columns d2
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 32 threads
-  {
-    const int d1 = 32 * b1 + ty, d2 = 32 * b2 + tx;
-    t[ty][tx] = sum_splits(p.n_split, [&](int k) { return p.part_s[((int64_t(k) * H + head) * D + d1) * D + d2]; });
+  const int64_t n4 = int64_t(H) * D * D / 4;  // float4 groups of S^T
+  const int64_t e = int64_t(blockIdx.x) * kReduceThreads + threadIdx.x;
+  if (e < n4) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_s) + e;
+    f32x4 v[kLinMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kLinMaxSplits; ++k)
+      if (k < p.n_split) v[k] = src[int64_t(k) * n4];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kLinMaxSplits; ++k)
+      if (k < p.n_split) s += v[k];
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = (__bf16)s[i];
+      lo[i] = (__bf16)(s[i] - float(hi[i]));
+    }
+    reinterpret_cast<bf16x4*>(p.st_hi)[e] = hi;
+    reinterpret_cast<bf16x4*>(p.st_lo)[e] = lo;
+  } else if (e < n4 + H * D) {
+    const int64_t z = e - n4;
+    float v[kLinMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kLinMaxSplits; ++k)
+      if (k < p.n_split) v[k] = p.part_z[int64_t(k) * H * D + z];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kLinMaxSplits; ++k)
+      if (k < p.n_split) s += v[k];
+    p.z[z] = s;
   }
-  __syncthreads();
-  {
-    const int d2 = 32 * b2 + ty, d1 = 32 * b1 + tx;
-    const float s = t[tx][ty];
-    const __bf16 hi = (__bf16)s;
-    const int64_t e = (int64_t(head) * D + d2) * D + d1;
-    static_cast<__bf16*>(p.st_hi)[e] = hi;
-    static_cast<__bf16*>(p.st_lo)[e] = (__bf16)(s - float(hi));
-  }
-  if (blockIdx.x == 0 && threadIdx.x < D)
-    p.z[int64_t(head) * D + threadIdx.x] =
-        sum_splits(p.n_split, [&](int k) { return p.part_z[(int64_t(k) * H + head) * D + threadIdx.x]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -500,7 +503,9 @@ template <int D>
 int launch_linear_d(const LinArgs& p, void* stream) {
   int err = launch(lin_state_kernel<D>, dim3(p.n_split, p.a.H), dim3(kStateThreads), &p, stream);
   if (err) return err;
-  err = launch(lin_reduce_kernel<D>, dim3((D / 32) * (D / 32), p.a.H), dim3(1024), &p, stream);
+  const int64_t n_red = int64_t(p.a.H) * D * D / 4 + int64_t(p.a.H) * D;
+  err = launch(lin_reduce_kernel<D>, dim3(unsigned((n_red + kReduceThreads - 1) / kReduceThreads)),
+               dim3(kReduceThreads), &p, stream);
   if (err || p.a.n_q <= 0) return err;
   return launch(lin_apply_kernel<D>, dim3((p.a.n_q + kApplyBQ - 1) / kApplyBQ, p.a.H), dim3(kApplyThreads), &p,
                 stream);
