@@ -60,7 +60,7 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g) {
   r.rows = r.sink_rows + r.ring_rows;
   // Kernels index rows and chunk tokens with 32-bit integers.
   const int64_t lim = std::numeric_limits<int32_t>::max() / 2;
-  if (r.ctok > lim || r.rows > lim || r.rows * r.D > lim)
+  if (r.ctok > lim || r.rows > lim || r.rows * r.D > lim || r.ctok * r.H * r.D > lim)
     return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit row indexing");
   r.vt = r.kv == LL_BF16;
   r.staged = r.kv == LL_I8;

@@ -936,15 +936,16 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
 // INT8 writer: one group of D/8 lanes per (head, row); each lane quantises
 // 8 values.  s = max|x| / 127 (IEEE fp32 division), q = clamp(rne(x / s)).
 __global__ __launch_bounds__(256) void quant_chunks_kernel(CopyArgs a) {
-  const int gl = a.D / 8;
-  const int64_t grp = (int64_t(blockIdx.x) * 256 + threadIdx.x) / gl;
-  const int li = threadIdx.x % gl;
-  const bool valid = grp < int64_t(a.ctok) * a.H;
+  // 32-bit indexing: the host's grid covers ctok * H groups, far below 2^31.
+  const unsigned gl = unsigned(a.D) / 8;  // 16 or 8
+  const unsigned grp = (blockIdx.x * 256u + threadIdx.x) / gl;
+  const int li = int(threadIdx.x % gl);
+  const bool valid = grp < unsigned(a.ctok) * unsigned(a.H);
   const int chunk = blockIdx.y >> 1;
   const int isv = blockIdx.y & 1;
   const int z = blockIdx.z;
-  const int row = valid ? int(grp % a.ctok) : 0;
-  const int h = valid ? int(grp / a.ctok) : 0;
+  const int row = valid ? int(grp % unsigned(a.ctok)) : 0;
+  const int h = valid ? int(grp / unsigned(a.ctok)) : 0;
   float x[8];
   if (valid) {
     const __bf16* src = static_cast<const __bf16*>(isv ? a.src_v : a.src_k) + int64_t(z) * a.src_layer_elems +
@@ -963,7 +964,7 @@ __global__ __launch_bounds__(256) void quant_chunks_kernel(CopyArgs a) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  for (int m = 1; m < gl; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  for (int m = 1; m < int(gl); m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
   if (!valid) return;
   const float s = amax / 127.0f;
   uint32_t packed[2] = {0, 0};
