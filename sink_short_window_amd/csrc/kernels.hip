@@ -802,17 +802,17 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // contiguous D-vector.
 __global__ __launch_bounds__(256) void copy_chunks_kernel(CopyArgs a) {
   constexpr int kElt = 4;  // fp32
-  const int vpr = a.D * kElt / 16;
-  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t total = int64_t(a.ctok) * a.H * vpr;
-  if (e >= total) return;
+  // 32-bit indexing: the host bounds ctok * H * D by 2^30.
+  const unsigned vpr = unsigned(a.D) * kElt / 16;  // 32 or 16
+  const unsigned e = blockIdx.x * 256u + threadIdx.x;
+  if (e >= unsigned(a.ctok) * unsigned(a.H) * vpr) return;
   const int chunk = blockIdx.y >> 1;
   const int isv = blockIdx.y & 1;
   const int z = blockIdx.z;
   const int vec = int(e % vpr);
-  const int64_t rh = e / vpr;
-  const int row = int(rh % a.ctok);
-  const int h = int(rh / a.ctok);
+  const unsigned rh = e / vpr;
+  const int row = int(rh % unsigned(a.ctok));
+  const int h = int(rh / unsigned(a.ctok));
   const char* src = static_cast<const char*>(isv ? a.src_v : a.src_k) +
                     (int64_t(z) * a.src_layer_elems + (int64_t(chunk) * a.ctok + row) * a.H * a.D +
                      int64_t(h) * a.D) * kElt + vec * 16;
