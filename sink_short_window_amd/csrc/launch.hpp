@@ -117,9 +117,9 @@ struct StageArgs {
 // Linear-attention variant (ll_sink_window_linear_attn): per head the state
 // S = sum_j phi(k_j) v_j^T ([D][D]) and z = sum_j phi(k_j) over the runs of
 // `a` are summed in n_split partial sums (split s: the 64-key tiles s,
-// s + n_split, ...; at most tiles_per_split of them), reduced, then applied: out_i = phi(q_i)^T S / (phi(q_i) . z + eps), phi(x) =
-// max(x, 0).  The workspace pointers are parts of the caller's buffer
-// (linear_workspace_layout).
+// s + n_split, ...; at most tiles_per_split of them), reduced, then applied:
+// out_i = phi(q_i)^T S / (phi(q_i) . z + eps), phi(x) = max(x, 0).  The
+// workspace pointers are parts of the caller's buffer (linear_workspace_layout).
 constexpr int kLinMaxSplits = 32;
 constexpr int kComputeUnits = 256;  // MI355X (gfx950): 8 XCDs x 32 CUs
 struct LinArgs {
