@@ -640,3 +640,71 @@ def test_int8_history_quantises_stored_chunks_only():
     cur = rng.standard_normal((2, 1, 8)).astype(np.float32)
     hk, _ = h.keys(cur, cur)
     np.testing.assert_array_equal(hk[2:], cur.astype(np.float64))
+
+
+# Exact-rational pins of the quantiser's division step.  The table's codes
+# were derived with Fractions (tests/golden/make_int8_quant_golden.py); its
+# vectors are chosen so that a division by a rounded reciprocal, or a binary64
+# division, gives different codes.
+
+def _quant_cases():
+    rows = []
+    with open(os.path.join(os.path.dirname(GOLDEN), "int8_quant_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            tag, _diff, xb, sb, codes = [c.strip() for c in line.split("|")]
+            bits = np.array([int(b, 16) for b in xb.split(",")], np.uint16)
+            x = (bits.astype(np.uint32) << 16).view(np.float32)
+            s = np.array([int(sb, 16)], np.uint32).view(np.float32)[0]
+            rows.append((tag, x, s, np.array([int(c) for c in codes.split(",")], np.int64)))
+    return rows
+
+
+def test_int8_quantiser_exact_rational_table():
+    """P9: the oracle reproduces every code and scale of the exact-rational
+    table bit for bit, including the vectors where fl32(x/s) differs from
+    x * fl32(1/s) and from a binary64 division."""
+    rows = _quant_cases()
+    tags = " ".join(t for t, *_ in rows)
+    assert "recip" in tags and "f64" in tags
+    x = np.stack([r[1] for r in rows])
+    q, s = quantize_int8(x)
+    for i, (tag, _, s_want, c_want) in enumerate(rows):
+        assert s[i].view(np.uint32) == np.float32(s_want).view(np.uint32), (i, tag)
+        np.testing.assert_array_equal(q[i].astype(np.int64), c_want, err_msg=f"row {i} ({tag})")
+
+
+def test_int8_quantiser_table_separates_the_division_variants():
+    """The table is a real pin: the two near-miss divisions, written out here
+    in float arithmetic, each miss at least one of its codes."""
+    rows = _quant_cases()
+    x = np.stack([r[1] for r in rows])
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(127)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    want = np.stack([r[3] for r in rows])
+    recip = np.clip(np.rint((x * (np.float32(1) / safe)[:, None]).astype(np.float32)), -127, 127)
+    f64 = np.clip(np.rint(x.astype(np.float64) / safe.astype(np.float64)[:, None]), -127, 127)
+    for name, got, tag in (("recip", recip, "recip"), ("f64", f64, "f64")):
+        hit = [i for i, r in enumerate(rows) if tag in r[0]]
+        assert hit and all((got[i] != want[i]).any() for i in hit), name
+
+
+def test_int8_quantiser_matches_exact_rationals_on_random_vectors():
+    """P9 on fresh draws: the oracle's codes and scales equal the
+    exact-rational quantiser on random bf16 vectors of several scales."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_int8_quant_golden", os.path.join(os.path.dirname(GOLDEN), "make_int8_quant_golden.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    quantise_exact, bf16_values, draw_bits = gen.quantise_exact, gen.bf16_values, gen.draw_bits
+    rng = np.random.default_rng(31)
+    bits = draw_bits(rng, 300)
+    x = (bits.astype(np.uint32) << 16).view(np.float32)
+    q, s = quantize_int8(x)
+    for i in range(len(bits)):
+        s_ex, codes, _, _ = quantise_exact(bf16_values(bits[i]))
+        assert float(s[i]) == float(s_ex), i
+        assert q[i].astype(int).tolist() == codes, i
