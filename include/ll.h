@@ -114,6 +114,9 @@ ll_status ll_cache_required_bytes(const ll_cache_config* cfg, size_t* bytes);
 ll_status ll_cache_create(const ll_cache_config* cfg, void* dev_buf, size_t dev_bytes,
                           ll_cache** out);
 
+/* The configuration `cache` was created with, written to *cfg (host memory). */
+ll_status ll_cache_get_config(const ll_cache* cache, ll_cache_config* cfg);
+
 /* Destroy the host handle (the device buffer is the caller's). NULL is a no-op. */
 ll_status ll_cache_destroy(ll_cache* cache);
 

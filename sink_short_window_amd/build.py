@@ -4,6 +4,9 @@
 * ``lib/libll_hoststub.so`` -- CPU test library: the same C ABI layer and
   bookkeeping linked against a launch stub that records instead of launching
   (g++ only, no HIP), so the ABI's host logic is testable without a GPU.
+* ``lib/libll_hoststub_san.so`` -- the same, built with AddressSanitizer and
+  UndefinedBehaviorSanitizer (host code only; loaded with the ASan runtime
+  preloaded, see tests/test_host_sanitizers.py).
 
 Run ``python -m sink_short_window_amd.build`` (or ``__graft_entry__.build()``).
 """
@@ -31,6 +34,9 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip", "linear_attn.hip")
 LIB_LL = os.path.join(LIB, "libll.so")
 LIB_HOSTSTUB = os.path.join(LIB, "libll_hoststub.so")
+LIB_HOSTSTUB_SAN = os.path.join(LIB, "libll_hoststub_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
 
 
 def _run(cmd):
@@ -40,16 +46,18 @@ def _run(cmd):
     return r.stdout
 
 
-def build_hoststub(verbose=False):
+def build_hoststub(verbose=False, sanitize=False):
     os.makedirs(LIB, exist_ok=True)
     cxx = shutil.which("g++") or "g++"
     srcs = [os.path.join(CSRC, f) for f in ("cache_state.cpp", "ll_api.cpp", "launch_stub.cpp")]
-    tmp = LIB_HOSTSTUB + ".tmp"
-    out = _run([cxx] + HOST_FLAGS + ["-shared", "-I", INCLUDE, "-I", CSRC] + srcs + ["-o", tmp])
-    os.replace(tmp, LIB_HOSTSTUB)
+    dst = LIB_HOSTSTUB_SAN if sanitize else LIB_HOSTSTUB
+    tmp = dst + ".tmp"
+    flags = HOST_FLAGS + (SAN_FLAGS if sanitize else [])
+    out = _run([cxx] + flags + ["-shared", "-I", INCLUDE, "-I", CSRC] + srcs + ["-o", tmp])
+    os.replace(tmp, dst)
     if verbose and out:
         print(out)
-    return LIB_HOSTSTUB
+    return dst
 
 
 def build_ll(verbose=False):
@@ -75,7 +83,7 @@ def build_ll(verbose=False):
 
 
 def build_all(verbose=False):
-    return build_ll(verbose), build_hoststub(verbose)
+    return build_ll(verbose), build_hoststub(verbose), build_hoststub(verbose, sanitize=True)
 
 
 if __name__ == "__main__":

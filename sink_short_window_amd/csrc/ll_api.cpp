@@ -187,6 +187,15 @@ ll_status ll_cache_create(const ll_cache_config* cfg, void* dev_buf, size_t dev_
   return LL_OK;
 }
 
+ll_status ll_cache_get_config(const ll_cache* cache, ll_cache_config* cfg) {
+  ll::clear_error();
+  if (!cache) return fail(LL_ERR_INVALID_ARG, "cache handle is NULL");
+  if (!cfg) return fail(LL_ERR_INVALID_ARG, "cfg is NULL");
+  const ll::Geometry& g = cache->state.geom();
+  *cfg = ll_cache_config{g.L, g.H, g.D, g.T, g.C, g.S, g.W, g.act, g.kv};
+  return LL_OK;
+}
+
 ll_status ll_cache_destroy(ll_cache* cache) {
   ll::clear_error();
   delete cache;

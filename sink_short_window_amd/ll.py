@@ -2,8 +2,10 @@
 point with the same name.  Argument marshalling only: every step of the path
 runs in the library's HIP kernels; torch supplies device memory and streams.
 
-Tensors are passed as torch tensors (device, dtype and contiguity are
-checked); the stream defaults to torch's current stream on the tensor's
+Tensors are passed as torch tensors.  Their shapes are checked against the
+cache's geometry (ll_cache_get_config) before their device, dtype and
+contiguity, and before anything reaches the library, whose C ABI sees only
+pointers and so cannot bound a buffer; the stream defaults to torch's current stream on the tensor's
 device.  A non-OK status raises :class:`LLError` with the library's message.
 If the library has not been built, loading raises instead of falling back to
 anything else.
@@ -24,7 +26,8 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
           4: "LL_ERR_BUFFER_TOO_SMALL", 5: "LL_ERR_HIP", 6: "LL_ERR_INTERNAL"}
 
 # Every function include/ll.h declares (checked against the header by the tests).
-EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
+EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_get_config", "ll_cache_destroy",
+           "ll_cache_reset",
            "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
            "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_sink_window_linear_attn",
            "ll_linear_attn_workspace_bytes", "ll_cross_attn", "ll_cache_query", "ll_cache_layout",
@@ -52,6 +55,7 @@ _P = ctypes.POINTER
 _SIGS = {
     "ll_cache_required_bytes": (_i32, [_P(ll_cache_config), _P(_sz)]),
     "ll_cache_create": (_i32, [_P(ll_cache_config), _vp, _sz, _P(_vp)]),
+    "ll_cache_get_config": (_i32, [_vp, _P(ll_cache_config)]),
     "ll_cache_destroy": (_i32, [_vp]),
     "ll_cache_reset": (_i32, [_vp]),
     "ll_cache_append_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp]),
@@ -137,6 +141,21 @@ def _stream(stream, like):
     return torch.cuda.current_stream(like.device).cuda_stream
 
 
+def _shape(t, name, shape):
+    """Raise unless tensor ``t`` (if given) has exactly ``shape``.  Checked
+    before anything reaches the library: the C ABI sees only pointers, so an
+    undersized buffer would be read or written out of bounds on the device."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if got != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+
+
+def _chunk_tokens(cfg):
+    return cfg.tokens_per_frame * cfg.frames_per_chunk
+
+
 def make_config(num_layers, num_heads, head_dim, tokens_per_frame, frames_per_chunk,
                 sink_frames, window_frames, act_dtype=LL_BF16, kv_dtype=LL_BF16):
     return ll_cache_config(num_layers, num_heads, head_dim, tokens_per_frame, frames_per_chunk,
@@ -158,10 +177,20 @@ def ll_cache_create(cfg, dev_buf, lib=None):
     """dev_buf: a uint8 device tensor of at least ll_cache_required_bytes.
     Returns the opaque handle (int)."""
     lib = lib or load()
+    if dev_buf is None or dev_buf.dim() != 1:
+        raise ValueError("dev_buf must be a 1-D uint8 tensor")
     ptr = _dev_ptr(dev_buf, "dev_buf", "uint8")
     h = _vp()
     _check(lib, lib.ll_cache_create(ctypes.byref(cfg), ptr, dev_buf.numel(), ctypes.byref(h)))
     return h.value
+
+
+def ll_cache_get_config(handle, lib=None):
+    """The ll_cache_config the handle was created with."""
+    lib = lib or load()
+    cfg = ll_cache_config()
+    _check(lib, lib.ll_cache_get_config(handle, ctypes.byref(cfg)))
+    return cfg
 
 
 def ll_cache_destroy(handle, lib=None):
@@ -176,6 +205,10 @@ def ll_cache_reset(handle, lib=None):
 
 def ll_cache_append_chunk(handle, layer, k, v, act_dtype, stream=None, lib=None):
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    shape = (_chunk_tokens(g), g.num_heads, g.head_dim)
+    _shape(k, "k", shape)
+    _shape(v, "v", shape)
     dt = _ACT[act_dtype]
     _check(lib, lib.ll_cache_append_chunk(handle, layer, _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
                                           _stream(stream, k)))
@@ -183,15 +216,38 @@ def ll_cache_append_chunk(handle, layer, k, v, act_dtype, stream=None, lib=None)
 
 def ll_cache_recache(handle, layer, k, v, n_tokens, act_dtype, stream=None, lib=None):
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    lead = (g.num_layers,) if layer == -1 else ()
+    shape = lead + (int(n_tokens), g.num_heads, g.head_dim)
+    _shape(k, "k", shape)
+    _shape(v, "v", shape)
     dt = _ACT[act_dtype]
     _check(lib, lib.ll_cache_recache(handle, layer, _dev_ptr(k, "k", dt), _dev_ptr(v, "v", dt),
                                      int(n_tokens), _stream(stream, k)))
+
+
+def _check_attn_shapes(g, q, k_cur, v_cur, out, lse=None):
+    """q, out: [n_q, H, D]; k_cur, v_cur: both [C_tok, H, D] or both None;
+    lse: [H, n_q]."""
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [n_q, H, D]")
+    n_q = q.shape[0]
+    H, D = g.num_heads, g.head_dim
+    _shape(q, "q", (n_q, H, D))
+    _shape(out, "out", (n_q, H, D))
+    _shape(lse, "lse", (H, n_q))
+    if (k_cur is None) != (v_cur is None):
+        raise ValueError("k_cur and v_cur must both be given or both be None")
+    _shape(k_cur, "k_cur", (_chunk_tokens(g), H, D))
+    _shape(v_cur, "v_cur", (_chunk_tokens(g), H, D))
 
 
 def ll_sink_window_attn(handle, layer, q, k_cur, v_cur, scale, out, act_dtype, lse=None,
                         stream=None, lib=None):
     """q, out: [n_q, H, D]; k_cur/v_cur: [C_tok, H, D] or None (cache only)."""
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    _check_attn_shapes(g, q, k_cur, v_cur, out, lse)
     dt = _ACT[act_dtype]
     n_cur = 0 if k_cur is None else k_cur.shape[0]
     _check(lib, lib.ll_sink_window_attn(
@@ -205,6 +261,8 @@ def ll_window_reencode_attn(handle, layer, q, scale, out, act_dtype, lse=None, s
                             lib=None):
     """q, out: [resident window chunks * C_tok, H, D], oldest chunk first."""
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    _check_attn_shapes(g, q, None, None, out, lse)
     dt = _ACT[act_dtype]
     _check(lib, lib.ll_window_reencode_attn(
         handle, layer, _dev_ptr(q, "q", dt), q.shape[0], float(scale), _dev_ptr(out, "out", dt),
@@ -223,6 +281,8 @@ def ll_sink_window_linear_attn(handle, layer, q, k_cur, v_cur, out, work, stream
     [C_tok, H, D] or None; work: a uint8 device tensor of at least
     ll_linear_attn_workspace_bytes."""
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    _check_attn_shapes(g, q, k_cur, v_cur, out)
     n_cur = 0 if k_cur is None else k_cur.shape[0]
     _check(lib, lib.ll_sink_window_linear_attn(
         handle, layer, _dev_ptr(q, "q", "bfloat16"), q.shape[0],
@@ -236,6 +296,15 @@ def ll_sink_window_attn_bwd(handle, layer, q, k_cur, v_cur, scale, out, lse, dou
     lse, delta: float32 [H, n_q]; dq: float32 [n_q, H, D]; k_cur/v_cur: bf16
     [C_tok, H, D] or None; dk_cur/dv_cur: float32 [C_tok, H, D] with them."""
     lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    _check_attn_shapes(g, q, k_cur, v_cur, out, lse)
+    n_q = q.shape[0]
+    _shape(dout, "dout", tuple(q.shape))
+    _shape(delta, "delta", (g.num_heads, n_q))
+    _shape(dq, "dq", tuple(q.shape))
+    if k_cur is not None:
+        _shape(dk_cur, "dk_cur", tuple(k_cur.shape))
+        _shape(dv_cur, "dv_cur", tuple(k_cur.shape))
     n_cur = 0 if k_cur is None else k_cur.shape[0]
     _check(lib, lib.ll_sink_window_attn_bwd(
         handle, layer, _dev_ptr(q, "q", "bfloat16"), q.shape[0],
@@ -249,8 +318,16 @@ def ll_sink_window_attn_bwd(handle, layer, q, k_cur, v_cur, scale, out, lse, dou
 def ll_cross_attn(q, k_txt, v_txt, scale, out, act_dtype, lse=None, stream=None, lib=None):
     """q, out: [n_q, H, D]; k_txt, v_txt: [n_txt, H, D]."""
     lib = lib or load()
-    dt = _ACT[act_dtype]
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [n_q, H, D]")
     n_q, H, D = q.shape
+    if k_txt is None or k_txt.dim() != 3:
+        raise ValueError("k_txt must be a 3-D tensor [n_txt, H, D]")
+    _shape(k_txt, "k_txt", (k_txt.shape[0], H, D))
+    _shape(v_txt, "v_txt", tuple(k_txt.shape))
+    _shape(out, "out", (n_q, H, D))
+    _shape(lse, "lse", (H, n_q))
+    dt = _ACT[act_dtype]
     _check(lib, lib.ll_cross_attn(
         _dev_ptr(q, "q", dt), n_q, _dev_ptr(k_txt, "k_txt", dt), _dev_ptr(v_txt, "v_txt", dt),
         k_txt.shape[0], H, D, act_dtype, float(scale), _dev_ptr(out, "out", dt),

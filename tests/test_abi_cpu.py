@@ -28,7 +28,8 @@ FAKE_ACT = 1 << 30
 def libs():
     if not (os.path.exists(build.LIB_LL) and os.path.exists(build.LIB_HOSTSTUB)):
         build.build_all()
-    stub = ctypes.CDLL(build.LIB_HOSTSTUB)
+    # LL_HOSTSTUB selects another build of the stub (the sanitizer build)
+    stub = ctypes.CDLL(os.environ.get("LL_HOSTSTUB", build.LIB_HOSTSTUB))
     ll.bind(stub)
     stub.llh_last_attn.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     stub.llh_last_copy.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
@@ -566,3 +567,123 @@ def test_layout_queries(libs):
     assert off_vr == off_vs + 2 * 64 * 64 * 2 and off_vs % 256 == 0
     libs.ll_cache_destroy(h)
     libs.ll_cache_destroy(h2)
+
+
+def test_get_config_round_trips(libs):
+    c = cfg(L=3, H=5, D=128, T=7, C=2, S=4, W=8, kv=ll.LL_I8)
+    h = create(libs, c)
+    got = ll.ll_cache_get_config(h, lib=libs)
+    for f, _ in ll.ll_cache_config._fields_:
+        assert getattr(got, f) == getattr(c, f), f
+    assert status(libs, libs.ll_cache_get_config(None, ctypes.byref(got))) == "LL_ERR_INVALID_ARG"
+    assert status(libs, libs.ll_cache_get_config(h, None)) == "LL_ERR_INVALID_ARG"
+    libs.ll_cache_destroy(h)
+
+
+def test_binding_rejects_mismatched_shapes_before_the_library(libs):
+    """Every wrapper checks tensor shapes against the cache geometry before it
+    touches the library (the C ABI cannot see buffer sizes).  A wrong shape
+    raises 'must have shape'; the right shapes get as far as the device check
+    (these are CPU tensors)."""
+    import torch
+    L, H, D, T, C, S, W = 2, 3, 64, 4, 2, 2, 6
+    ct = C * T
+    h = create(libs, cfg(L, H, D, T, C, S, W))
+    bf = lambda *sh: torch.zeros(sh, dtype=torch.bfloat16)
+    f32 = lambda *sh: torch.zeros(sh, dtype=torch.float32)
+
+    def shape_error(fn, *a, **kw):
+        with pytest.raises(ValueError, match="shape|3-D|both"):
+            fn(*a, **kw)
+
+    def device_error(fn, *a, **kw):
+        with pytest.raises(ValueError, match="device tensor"):
+            fn(*a, **kw)
+
+    A = ll.LL_BF16
+    # append: k, v [C_tok, H, D]
+    device_error(ll.ll_cache_append_chunk, h, 0, bf(ct, H, D), bf(ct, H, D), A, lib=libs)
+    shape_error(ll.ll_cache_append_chunk, h, 0, bf(ct - 1, H, D), bf(ct, H, D), A, lib=libs)
+    shape_error(ll.ll_cache_append_chunk, h, 0, bf(ct, H, D), bf(ct, H + 1, D), A, lib=libs)
+    # recache: [n, H, D] for one layer, [L, n, H, D] for all
+    device_error(ll.ll_cache_recache, h, 0, bf(2 * ct, H, D), bf(2 * ct, H, D), 2 * ct, A, lib=libs)
+    shape_error(ll.ll_cache_recache, h, 0, bf(ct, H, D), bf(2 * ct, H, D), 2 * ct, A, lib=libs)
+    device_error(ll.ll_cache_recache, h, -1, bf(L, ct, H, D), bf(L, ct, H, D), ct, A, lib=libs)
+    shape_error(ll.ll_cache_recache, h, -1, bf(ct, H, D), bf(ct, H, D), ct, A, lib=libs)
+    # attention: q/out [n_q, H, D], k_cur/v_cur [C_tok, H, D], lse [H, n_q]
+    n = 5
+    ok = dict(q=bf(n, H, D), k_cur=bf(ct, H, D), v_cur=bf(ct, H, D), out=bf(n, H, D), lse=f32(H, n))
+
+    def attn(**kw):
+        a = dict(ok, **kw)
+        return ll.ll_sink_window_attn(h, 0, a["q"], a["k_cur"], a["v_cur"], 0.125, a["out"], A,
+                                      lse=a["lse"], lib=libs)
+
+    device_error(attn)
+    device_error(attn, k_cur=None, v_cur=None)
+    for bad in (dict(q=bf(n, H, D + 1)), dict(q=bf(n * H * D)), dict(out=bf(n - 1, H, D)),
+                dict(k_cur=bf(ct + 1, H, D)), dict(v_cur=bf(ct, H, 2 * D)), dict(v_cur=None),
+                dict(lse=f32(H, n + 1)), dict(lse=f32(n, H))):
+        shape_error(attn, **bad)
+    # re-encoding attention, linear variant and backward share the checks
+    device_error(ll.ll_window_reencode_attn, h, 0, bf(n, H, D), 0.1, bf(n, H, D), A, lib=libs)
+    shape_error(ll.ll_window_reencode_attn, h, 0, bf(n, H, D), 0.1, bf(n + 1, H, D), A, lib=libs)
+    shape_error(ll.ll_sink_window_linear_attn, h, 0, bf(n, H, D), bf(ct, H, D), bf(ct, H, D),
+                bf(n, 1, D), torch.zeros(16, dtype=torch.uint8), lib=libs)
+
+    def bwd(**kw):
+        a = dict(q=bf(n, H, D), k=bf(ct, H, D), v=bf(ct, H, D), out=bf(n, H, D), lse=f32(H, n),
+                 dout=bf(n, H, D), delta=f32(H, n), dq=f32(n, H, D), dk=f32(ct, H, D), dv=f32(ct, H, D))
+        a.update(kw)
+        return ll.ll_sink_window_attn_bwd(h, 0, a["q"], a["k"], a["v"], 0.1, a["out"], a["lse"],
+                                          a["dout"], a["delta"], a["dq"], a["dk"], a["dv"], lib=libs)
+
+    device_error(bwd)
+    for bad in (dict(dout=bf(n, H, D - 1)), dict(delta=f32(H, n - 1)), dict(dq=f32(n, H, 1)),
+                dict(dk=f32(ct - 1, H, D)), dict(dv=f32(ct, H, D + 1))):
+        shape_error(bwd, **bad)
+    # cross-attention: q [n_q, H, D]; k_txt, v_txt [n_txt, H, D]
+    device_error(ll.ll_cross_attn, bf(n, H, D), bf(7, H, D), bf(7, H, D), 0.1, bf(n, H, D), A, lib=libs)
+    for q_, k_, v_, o_ in ((bf(n, H, D), bf(7, H + 1, D), bf(7, H, D), bf(n, H, D)),
+                           (bf(n, H, D), bf(7, H, D), bf(6, H, D), bf(n, H, D)),
+                           (bf(n, H, D), bf(7, H, D), bf(7, H, D), bf(n + 1, H, D)),
+                           (bf(n * H * D), bf(7, H, D), bf(7, H, D), bf(n, H, D))):
+        shape_error(ll.ll_cross_attn, q_, k_, v_, 0.1, o_, A, lib=libs)
+    libs.ll_cache_destroy(h)
+
+
+# The kernels index chunk elements, cache rows and transposed V tiles with
+# 32-bit integers; the geometry check bounds each product by 2^30 - 1.  Each
+# pair sits on one side of one bound.
+LIM = 2 ** 30 - 1
+
+
+@pytest.mark.parametrize("kw,ok", [
+    # C_tok * H * D: T=1024, C=1, D=128 -> H * 2^17
+    (dict(T=1024, C=1, S=0, W=2, H=8191, D=128), True),
+    (dict(T=1024, C=1, S=0, W=2, H=8192, D=128), False),
+    # rows * D with 30 ring slots: 30 * T * 128
+    (dict(T=279620, C=1, S=0, W=31, H=1, D=128, act=ll.LL_F32, kv=ll.LL_F32), True),
+    (dict(T=279621, C=1, S=0, W=31, H=1, D=128, act=ll.LL_F32, kv=ll.LL_F32), False),
+    # transposed V tiles (BF16 cache): 30 slots * ceil(T/64) * 64 * 128; T = 64k + 1
+    # pads each slot, so this bound bites before rows * D does
+    (dict(T=64 * 4368 + 1, C=1, S=0, W=31, H=1, D=128), True),
+    (dict(T=64 * 4369 + 1, C=1, S=0, W=31, H=1, D=128), False),
+    (dict(T=64 * 4369 + 1, C=1, S=0, W=31, H=1, D=128, kv=ll.LL_I8), False),
+    (dict(T=64 * 4369 + 1, C=1, S=0, W=31, H=1, D=128, act=ll.LL_F32, kv=ll.LL_F32), True),
+])
+def test_geometry_32bit_bounds(libs, kw, ok):
+    c = cfg(**{"L": 1, **kw})
+    n = ctypes.c_size_t(0)
+    st = libs.ll_cache_required_bytes(ctypes.byref(c), ctypes.byref(n))
+    T, C, H, D = kw["T"], kw["C"], kw["H"], kw["D"]
+    ct = T * C
+    rows = (kw["S"] + kw["W"] - C) * T
+    vt = (kw["S"] // C + (kw["W"] - C) // C) * -(-ct // 64) * 64 * D
+    tiled = kw.get("kv", ll.LL_BF16) != ll.LL_F32
+    assert (ct * H * D <= LIM and rows * D <= LIM and (not tiled or vt <= LIM)) == ok
+    if ok:
+        assert st == 0, libs.ll_last_error()
+    else:
+        assert status(libs, st) == "LL_ERR_UNSUPPORTED"
+        assert b"32-bit" in libs.ll_last_error()
