@@ -103,7 +103,7 @@ class Workload:
         from sink_short_window_amd import ll, synth
         self.torch, self.ll, self.synth = torch, ll, synth
         self.workload, self.kv, self.passes = workload, kv, passes
-        self.cfg_id = CFG_ID[workload] + (10 if kv == "int8" else 0)
+        self.cfg_id = CFG_ID[workload] + (10 if kv.startswith("int8") else 0)
         self.device = device
         self.scale = 1.0 / math.sqrt(D)
         gen = lambda shape, chunk, tensor: synth.to_torch(
@@ -121,9 +121,11 @@ class Workload:
         # queries of the re-encoding pass after a recache (the 2 window chunks)
         self.qwin = gen((2 * CT, H, D), POOL, synth.Q)
         self.payload = {}
-        kvcode = ll.LL_I8 if kv == "int8" else ll.LL_BF16
+        kvcode = ll.LL_I8 if kv.startswith("int8") else ll.LL_BF16
         cfg = ll.make_config(L, H, D, T, C, S, W, ll.LL_BF16, kvcode)
         self.cache = ll.Cache(cfg, device)
+        if kv == "int8-ink":   # int8 codes read inside the attention kernel
+            self.cache.set_int8_dequant(ll.LL_I8_IN_KERNEL)
         self.out = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
         self.xout = torch.empty((CT, H, D), dtype=torch.bfloat16, device=device)
         self.xwin = torch.empty((2 * CT, H, D), dtype=torch.bfloat16, device=device)
@@ -443,20 +445,58 @@ def attn_flops(n_keys):
     return 4.0 * CT * n_keys * D * H
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return [{"library": i.get("internal_api"), "version": i.get("version"),
+                 "threads": i.get("num_threads"), "file": os.path.basename(i.get("filepath", ""))}
+                for i in info], max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        return None, len(os.sched_getaffinity(0))
+
+
+def tiny_config_run():
+    """The tiny fp32 configuration through the oracle: 1 head x 64, 16 tokens
+    per frame, chunks of 1 frame, sink 1 frame, window 2 frames, 8 chunks, each
+    attending sink + window + itself and then appended.  Returns seconds."""
+    import oracle
+    from sink_short_window_amd import synth
+    t, c, s, w, h, d = 16, 1, 1, 2, 1, 64
+    g = oracle.CacheGeometry(t, c, s, w)
+    hist = oracle.LayerHistory(g)
+    t0 = time.perf_counter()
+    for j in range(8):
+        q, k, v = (synth.normal((t * c, h, d), "f32", 0, 0, j, 0, x) for x in (synth.Q, synth.K, synth.V))
+        hk, hv = hist.keys(k, v)
+        oracle.sink_window_attention(q, hk, hv, j, tokens_per_frame=t, frames_per_chunk=c,
+                                     sink_frames=s, window_frames=w, scale=1 / math.sqrt(d))
+        hist.append(k, v)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(k_steps, warmup, budget_s=20.0, passes=PASSES):
     """Time the oracle (float64 numpy, as it stands) on a bounded sample of the
     same workload and scale it to latent frames/s.
 
     Sample: one steady-state attention call (chunk 4: sink + 2 ring chunks +
     current chunk, 18720 allowed keys out of a 23400-key history), whole heads
-    at a time until ``budget_s`` is spent."""
+    at a time with the BLAS library's default threads until ``budget_s`` is
+    spent, then one head with one thread; plus the tiny fp32 configuration's
+    whole 8-chunk run."""
     import oracle
     from sink_short_window_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    blas, cores = _blas()
     g = oracle.CacheGeometry(T, C, S, W)
     hist = oracle.LayerHistory(g)
     ks = [synth.normal((CT, H, D), "bf16", 90, 0, j, 0, synth.K) for j in range(5)]
@@ -465,26 +505,49 @@ def cpu_baseline(k_steps, warmup, budget_s=20.0, passes=PASSES):
         hist.append(ks[j], vs[j])
     hk, hv = hist.keys(ks[4], vs[4])
     q = synth.normal((CT, H, D), "bf16", 90, 0, 4, 0, synth.Q)
+
+    def one_head(h):
+        hs = slice(h, h + 1)
+        oracle.sink_window_attention(q[:, hs], hk[:, hs], hv[:, hs], 4, tokens_per_frame=T,
+                                     frames_per_chunk=C, sink_frames=S, window_frames=W,
+                                     scale=1 / math.sqrt(D))
+
     heads, spent = 0, 0.0
     t0 = time.perf_counter()
     while heads < H and spent < budget_s:
-        h = slice(heads, heads + 1)
-        oracle.sink_window_attention(q[:, h], hk[:, h], hv[:, h], 4, tokens_per_frame=T,
-                                     frames_per_chunk=C, sink_frames=S, window_frames=W,
-                                     scale=1 / math.sqrt(D))
+        one_head(heads)
         heads += 1
         spent = time.perf_counter() - t0
     per_call = spent / heads * H             # one full call at a 5-chunk history
+    one_thread = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            one_head(0)
+            one_thread = (time.perf_counter() - t1) * H
+    except Exception:
+        pass
     # The oracle masks the whole history, so its cost grows with the chunk
     # index; scale each timed chunk's calls by its history length.
-    total = sum(passes * L * per_call * (c + 1) / 5.0 for c in range(warmup, warmup + k_steps))
-    return {"value": 3.0 * k_steps / total, "unit": "latent frames/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"oracle sink+window attention, {heads} of {H} heads x {CT} queries of one "
-                      f"call at chunk 4 (23400-key history, 18720 allowed) in {spent:.1f} s "
-                      f"({per_call:.1f} s per call); extrapolated to {passes}x{L} calls per chunk "
-                      f"for chunks {warmup}..{warmup + k_steps - 1} with cost scaled by history "
-                      f"length; cross-attention, append and recache not counted"}
+    scale_steps = lambda call_s: sum(passes * L * call_s * (c + 1) / 5.0 for c in range(warmup, warmup + k_steps))
+    total = scale_steps(per_call)
+    flop = attn_flops(keys_at(4))
+    res = {"value": 3.0 * k_steps / total, "unit": "latent frames/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"oracle sink+window attention, {heads} of {H} heads x {CT} queries of one "
+                     f"call at chunk 4 (23400-key history, 18720 allowed) in {spent:.1f} s "
+                     f"({per_call:.1f} s per call); extrapolated to {passes}x{L} calls per chunk "
+                     f"for chunks {warmup}..{warmup + k_steps - 1} with cost scaled by history "
+                     f"length; cross-attention, append and recache not counted",
+           "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+           "s_per_call": per_call, "gflops_per_call": flop / per_call / 1e9,
+           "tiny_fp32_8_chunks_s": tiny_config_run()}
+    if one_thread:
+        res["one_thread"] = {"s_per_call": one_thread, "gflops_per_call": flop / one_thread / 1e9,
+                             "latent_frames_per_s": 3.0 * k_steps / scale_steps(one_thread),
+                             "sample": "1 head of the same call with BLAS limited to 1 thread, x12 heads"}
+    return res
 
 
 def kernel_source_digest():
@@ -556,14 +619,80 @@ def gemm_ceiling():
     print(json.dumps({"gemm_ceiling_tflops": res, "shape": [n, n, n], "dtype": "bf16"}))
 
 
+def run_timed(wl, warmup, steps):
+    """Warmup steps (cross-attention and append launches timed there: same
+    kernels and shapes as in the timed steps), then the timed region of K
+    whole steps between HIP events.  Inside it events bracket one attention
+    launch in ATTN_EVENT_EVERY (and every rare recache) on the launch stream,
+    so the attention kernel's duration comes from the same run; events around
+    every launch would cost ~3% of the step."""
+    torch = wl.torch
+    wl.prepare(range(wl.chunk, wl.chunk + warmup + steps))
+    wl.timers, wl.timed_kinds = {}, ("cross", "append")
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    warm_timers, wl.timers = wl.timers, None
+    wl.timers, wl.timed_kinds = {}, ("attn", "recache")
+    wl.launches = {}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    first = wl.chunk
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    marks = [start]  # one event per step boundary: switch-step vs steady-step latency
+    for _ in range(steps):
+        wl.step()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks.append(e)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timers, wl.timers = wl.timers, None
+    return {"gpu_ms": start.elapsed_time(stop), "timers": timers, "warm_timers": warm_timers,
+            "marks": marks, "first": first, "wall": wall}
+
+
+def append_bytes(kv):
+    """Algorithmic HBM bytes of one layer's append: the chunk's K/V read
+    (bf16) and written in the cache's dtype (plus the int8 scales)."""
+    i8 = kv.startswith("int8")
+    return CT * H * D * 2 * 2 + CT * H * D * (1 if i8 else 2) * 2 + (CT * H * 4 * 2 if i8 else 0)
+
+
+def int8_subrun(warmup, steps, passes, kv="int8"):
+    """The same prompt-switch workload over an INT8 KV cache (per-token,
+    per-head scales), reported beside the bf16-cache line: latent frames/s,
+    the attention call (events around the whole call: the staging launch and
+    the attention for kv "int8", the attention that reads the codes itself for
+    "int8-ink") and the append rate."""
+    wl = Workload("switch", kv, passes=passes)
+    run = run_timed(wl, warmup, steps)
+    attn_ms, attn_work, attn_total = kernel_stats(run["timers"], "attn")
+    app_ms, _, _ = kernel_stats(run["warm_timers"], "append")
+    res = {"latent_frames_per_s": 3.0 * steps / (run["gpu_ms"] / 1e3),
+           "ms_per_step": run["gpu_ms"] / steps, "steps": steps, "warmup": warmup,
+           "attention_ms_per_call": attn_ms,
+           "attention_tflops": attn_work / (attn_total * 1e-3) / 1e12 if attn_ms else None,
+           "append_ms": app_ms,
+           "append_GBps": append_bytes("int8") / (app_ms * 1e-3) / 1e9 if app_ms else None}
+    wl.cache.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=76)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", choices=["switch", "stream"], default="switch")
-    ap.add_argument("--kv", choices=["bf16", "int8"], default="bf16")
+    ap.add_argument("--kv", choices=["bf16", "int8", "int8-ink"], default="bf16",
+                    help="KV cache: bf16, or int8 read through a staged bf16 copy (int8) or inside "
+                         "the attention kernel (int8-ink)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-int8-subrun", action="store_true",
+                    help="skip the INT8-cache run of the same workload that the bf16 line reports in extra")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--passes", type=int, default=PASSES,
                     help="attention passes per chunk (4 denoising; 5 adds the append pass's own attention)")
@@ -608,38 +737,9 @@ def main():
     import torch
     torch.cuda.init()
     wl = Workload(args.workload, args.kv, passes=args.passes)
-    wl.prepare(range(args.warmup + args.steps))
-    # Warmup steps; the cross-attention and append launches are timed here
-    # (same kernels and shapes as in the timed steps).
-    wl.timers, wl.timed_kinds = {}, ("cross", "append")
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
-    warm_timers, wl.timers = wl.timers, None
-
-    # Timed region: K whole steps.  HIP events bracket one attention launch in
-    # ATTN_EVENT_EVERY (and every rare recache) on the launch stream, so the
-    # attention kernel's duration comes from the same run.  Events around
-    # every launch would cost ~3% of the step, so the cheaper calls are timed
-    # during warmup.
-    wl.timers, wl.timed_kinds = {}, ("attn", "recache")
-    wl.launches = {}
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    first = wl.chunk
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    marks = [start]  # one event per step boundary: switch-step vs steady-step latency
-    for _ in range(args.steps):
-        wl.step()
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        marks.append(e)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    timers, wl.timers = wl.timers, None
-    gpu_ms = start.elapsed_time(stop)
+    run = run_timed(wl, args.warmup, args.steps)
+    gpu_ms, timers, warm_timers, marks, first, wall = (
+        run["gpu_ms"], run["timers"], run["warm_timers"], run["marks"], run["first"], run["wall"])
     ms_per_step = gpu_ms / args.steps
     frames_per_s = 3.0 * args.steps / (gpu_ms / 1e3)
 
@@ -654,10 +754,8 @@ def main():
              "timed_chunks": [first, first + args.steps - 1], "wall_s": wall}
     app_ms, _, _ = kernel_stats(warm_timers, "append")
     if app_ms:
-        elt = 1 if args.kv == "int8" else 2
-        by = CT * H * D * 2 * 2 + CT * H * D * elt * 2 + (CT * H * 4 * 2 if args.kv == "int8" else 0)
         extra["append_ms"] = app_ms
-        extra["append_GBps"] = by / (app_ms * 1e-3) / 1e9
+        extra["append_GBps"] = append_bytes(args.kv) / (app_ms * 1e-3) / 1e9
     x_ms, _, _ = kernel_stats(warm_timers, "cross")
     if x_ms:
         xf = 4.0 * CT * N_TXT * D * H
@@ -673,8 +771,8 @@ def main():
         extra["switch_steps"] = len(sw)
     rc_ms, _, _ = kernel_stats(timers, "recache")
     if rc_ms:
-        elt = 1 if args.kv == "int8" else 2
-        rc_bytes = L * 2 * (2 * CT * H * D) * (2 + elt) + (L * 2 * 2 * CT * H * 4 if args.kv == "int8" else 0)
+        i8 = args.kv.startswith("int8")
+        rc_bytes = L * 2 * (2 * CT * H * D) * (3 if i8 else 4) + (L * 2 * 2 * CT * H * 4 if i8 else 0)
         extra["recache_ms"] = rc_ms
         extra["recache_GBps"] = rc_bytes / (rc_ms * 1e-3) / 1e9
 
@@ -695,6 +793,11 @@ def main():
     extra["linear_ms_per_call"] = li_ms
     extra["linear_GBps"] = linear_bytes() / (li_ms * 1e-3) / 1e9
     extra["linear_tflops"] = linear_flops() / (li_ms * 1e-3) / 1e12
+
+    # The INT8-cache run of the same workload, reported beside this line.
+    if args.kv == "bf16" and not args.no_int8_subrun:
+        extra["int8_cache"] = int8_subrun(args.warmup, args.steps, args.passes, "int8")
+        extra["int8_cache_in_kernel"] = int8_subrun(args.warmup, args.steps, args.passes, "int8-ink")
 
     roofline = None
     if tflops:
@@ -721,7 +824,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name + (" (int8 KV cache)" if args.kv == "int8" else ""),
+        "config": {"workload": name + {"bf16": "", "int8": " (int8 KV cache, staged bf16 copy)",
+                                       "int8-ink": " (int8 KV cache read in the attention kernel)"}[args.kv],
                    "layers": L, "heads": H, "head_dim": D, "tokens_per_frame": T,
                    "chunk_frames": C, "sink_frames": S, "window_frames": W,
                    "chunk_tokens": CT, "keys_per_call": keys, "attention_passes": args.passes,

@@ -68,6 +68,9 @@ typedef enum {
 
 typedef enum { LL_F32 = 0, LL_BF16 = 1, LL_I8 = 2 } ll_dtype;
 
+/* How the attention reads an I8 cache (ll_cache_set_int8_dequant). */
+typedef enum { LL_I8_STAGED = 0, LL_I8_IN_KERNEL = 1 } ll_int8_dequant;
+
 /* Which cached tensor ll_cache_layout describes. */
 typedef enum { LL_WHICH_K = 0, LL_WHICH_V = 1, LL_WHICH_KSCALE = 2, LL_WHICH_VSCALE = 3 } ll_which;
 /* Which cache segment ll_cache_layout describes. */
@@ -120,6 +123,24 @@ ll_status ll_cache_get_config(const ll_cache* cache, ll_cache_config* cfg);
 /* Destroy the host handle (the device buffer is the caller's). NULL is a no-op. */
 ll_status ll_cache_destroy(ll_cache* cache);
 
+/*
+ * How ll_sink_window_attn and ll_window_reencode_attn read an I8 cache
+ * (INT8 KV variant; the workload definition asks for dequantisation inside
+ * the attention).  Host state only; enqueues nothing.
+ *   LL_I8_IN_KERNEL: the attention kernel reads the int8 codes and their
+ *     scales and attends over the exact values q * s: codes are converted
+ *     exactly to bf16 tiles on chip, the K scale multiplies each score in
+ *     fp32 and the V scale is folded into P before its bf16 rounding.
+ *   LL_I8_STAGED (default): one extra launch per call first writes a bf16
+ *     copy, bf16(q * s), of the layer's resident codes into the cache's
+ *     staging area, and the bf16 attention kernel reads that copy (faster on
+ *     MI355X, about 2.7x the HBM bytes, one more bf16 rounding of q * s).
+ * LL_ERR_INVALID_ARG for a mode outside the enum or a cache whose kv_dtype is
+ * not I8.  The backward and the linear-attention variant always read the
+ * staged copy.
+ */
+ll_status ll_cache_set_int8_dequant(ll_cache* cache, int32_t mode);
+
 /* Forget every appended chunk in every layer (host-only; enqueues nothing). */
 ll_status ll_cache_reset(ll_cache* cache);
 
@@ -157,11 +178,10 @@ ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const 
  *   scale:  logit scale, finite and > 0 (1/sqrt(D) in a standard DiT).
  *   lse:    nullable float [H][n_q]: natural-log sum of exp(scale * q.k).
  * Accumulation is fp32 (bf16 MFMA products for BF16 activations).  The scale
- * is folded into the queries before their bf16 rounding.  With an I8 cache
- * the call first dequantises the layer's resident codes to bf16(q * s) (s the
- * token's fp32 scale) into the cache's staging area, one extra launch on the
- * same stream, and attends over that copy; the current chunk is used as
- * given.
+ * is folded into the queries before their bf16 rounding.  An I8 cache is read
+ * as ll_cache_set_int8_dequant selects (in the attention kernel, or through a
+ * bf16 staging copy written by one extra launch on the same stream); the
+ * current chunk is used as given.
  * LL_ERR_BAD_STATE if the key set is empty.
  */
 ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,

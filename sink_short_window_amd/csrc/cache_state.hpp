@@ -35,14 +35,14 @@ struct Geometry {
   int64_t sink_rows = 0;  // S*T
   int64_t ring_rows = 0;  // R*ctok
   int64_t rows = 0;       // sink_rows + ring_rows, per head
-  // A BF16 cache keeps V transposed in 64-key tiles (the layout the attention
-  // kernel's PV operand wants): per head, nslots chunk slots (sink chunks,
-  // then ring slots) of tps tiles, each tile [D][64] with zero padding after
-  // the chunk's last key.
+  // BF16 and I8 caches keep V transposed in 64-key tiles (the layout the
+  // attention kernel's PV operand wants): per head, nslots chunk slots (sink
+  // chunks, then ring slots) of tps tiles, each tile [D][64] with zero
+  // padding after the chunk's last key.
   bool vt = false;
-  // An I8 cache is read by the attention through a bf16 staging copy of one
-  // layer's resident sink + ring in the BF16 layout (K rows, V tiles),
-  // written per call from the int8 codes and scales.
+  // An I8 cache also holds a bf16 staging area for one layer's resident sink
+  // + ring in the BF16 layout (K rows, V tiles), which the backward and the
+  // linear-attention variant read; the attention reads the int8 codes.
   bool staged = false;
   int32_t tps = 0;            // tiles per chunk slot, ceil(ctok / 64)
   int32_t nslots = 0;         // nsc + R
@@ -56,8 +56,8 @@ constexpr int kVtTileKeys = 64;
 ll_status make_geometry(const ll_cache_config* cfg, Geometry* g);
 
 // Byte layout of the device buffer.  Per layer, in order, each region
-// 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype; for a BF16
-// cache V is [H][nslots*tps][D][64] instead, see Geometry), and with I8
+// 256-byte aligned: K [H][rows][D], V [H][rows][D] (kv dtype; for BF16 and
+// I8 caches V is [H][nslots*tps][D][64] instead, see Geometry), and with I8
 // K scales [H][rows], V scales [H][rows] (fp32).  Rows [0, sink_rows) are the
 // sink; ring slot s is rows sink_rows + [s*ctok, (s+1)*ctok).  An I8 cache
 // ends with the bf16 staging area: K [H][rows][D], V [H][nslots*tps][D][64].
@@ -99,6 +99,9 @@ class CacheState {
   const LayerState& layer(int l) const { return layers_[l]; }
 
   void reset();
+  // How the attention reads an I8 cache (ll_int8_dequant).
+  int32_t int8_dequant() const { return i8_mode_; }
+  void set_int8_dequant(int32_t m) { i8_mode_ = m; }
   AppendPlan plan_append(int layer) const;
   void commit_append(int layer, const AppendPlan& p);
   // Ring slots of the resident window chunks, oldest chunk first.
@@ -111,6 +114,7 @@ class CacheState {
   Layout lay_;
   void* buf_;
   std::vector<LayerState> layers_;
+  int32_t i8_mode_ = LL_I8_STAGED;
 };
 
 }  // namespace ll

@@ -207,8 +207,9 @@ struct RunCursor {
   int tile;
   int len;
   int vt;       // V of this run in transposed 64-key tiles
+  int i8;       // int8 codes with per-key scales (rks, rvs)
   uint32_t rs;  // row stride in bytes
-  __amdgpu_buffer_rsrc_t rk, rv;
+  __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
 
   // Every field is uniform across the workgroup; readfirstlane says so to the
   // compiler, which keeps the descriptors in scalar registers (a descriptor
@@ -226,10 +227,16 @@ struct RunCursor {
     if (r >= a.n_seg) return;
     const KvSeg& s = a.seg[r];
     len = __builtin_amdgcn_readfirstlane(s.len);
-    constexpr int elt = 2;  // bf16
+    i8 = __builtin_amdgcn_readfirstlane(s.i8);
+    const int elt = i8 ? 1 : 2;  // int8 codes or bf16
     rs = __builtin_amdgcn_readfirstlane(uint32_t(s.row_stride) * elt);
     const int64_t hoff = int64_t(head) * s.head_stride * elt;
     rk = make_rsrc(uni(static_cast<const char*>(s.k) + hoff), uint32_t(len) * rs);
+    if (i8) {
+      const int64_t soff = int64_t(head) * s.s_head_stride;
+      rks = make_rsrc(uni(s.ks + soff), uint32_t(len) * 4);
+      rvs = make_rsrc(uni(s.vs + soff), uint32_t(len) * 4);
+    }
     vt = __builtin_amdgcn_readfirstlane(s.v_tiled);
     if (vt) {
       // whole zero-padded tiles; a tile is 64 rows of the cache's K row size
@@ -326,11 +333,18 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
 // Five reads ahead measured as fast as six with fewer registers spilled.
 constexpr int kAhead = 5;
 
-template <int D, bool kQK, bool kPV, bool kVT>
+struct NoExtra {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// extra(i) runs right after MFMA i is issued: other work of the same wave
+// (the int8 kernel's tile conversion) placed in the shadow of the MFMAs.
+template <int D, bool kQK, bool kPV, bool kVT, typename Extra = NoExtra>
 __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k_row, int k_x,
                                            const int (&voff)[2][D / 32], const int (&vb)[4],
                                            const bf16x8 (&qf)[D / 16], const f32x16& cinit, f32x16 (&s)[2],
-                                           f32x16 (&o)[D / 32], const bf16x8 (&pb)[4]) {
+                                           f32x16 (&o)[D / 32], const bf16x8 (&pb)[4],
+                                           const Extra& extra = Extra()) {
   using S = SwzStage<D>;
   constexpr int NK = kQK ? D / 8 : 0;          // K operand reads / QK MFMAs
   constexpr int NV = kPV ? 4 * (D / 32) : 0;   // V^T operand reads / PV MFMAs
@@ -368,6 +382,7 @@ __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k
       const int step = ii / (D / 32), db = ii % (D / 32);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[i % kAhead], pb[step], o[db], 0, 0, 0);
     }
+    extra(i);
     if (i + kAhead < N) rb[i % kAhead] = rd(i + kAhead);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -660,6 +675,450 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// INT8 cache, dequantised inside the attention.  The cache runs hold int8
+// codes c with fp32 scales per key: K = c_k * ks, V = c_v * vs (V stored
+// transposed in 64-key tiles like the bf16 cache).  Every code is an integer
+// in [-127, 127], exact in bf16, so
+//   S^T[key][q] = ks[key] * sum_d c_k[key][d] Q'[q][d]
+//     MFMA over the exact codes, then the K scale on each score column;
+//   O^T[d][q] += sum_key c_v[key][d] * (P[q][key] * vs[key])
+//     the V scale folded into P before its bf16 rounding;
+// and the row sum takes P itself.  The values attended are the exact q * s.
+//
+// Same 8-wave ping-pong as attn_pp_kernel (group A runs MFMA phase t in
+// interval 2t and softmax phase t in 2t+1, group B one interval later), with
+// this staging:
+//   * int8 tiles (K rows and V^T, 64 * D bytes each) go straight into a
+//     3-slot int8 ring (buffer_load ... lds) three tiles ahead, issued in the
+//     softmax phase: group A loads the K side and both scale vectors (into a
+//     4-slot scale ring), group B the V side;
+//   * the conversion to bf16 runs inside MFMA phases, between the MFMAs,
+//     where a wave's own VALU work hides behind its MFMAs: group A converts
+//     K(t+1) in its MFMA phase t, group B converts V(t) in its MFMA phase t.
+//     Each lane converts exactly the 16-byte pieces its own loads fetched,
+//     so a wave only waits for its own loads (vmcnt);
+//   * the caller's current chunk (bf16, row-major) goes straight into the
+//     3-stage bf16 ring two tiles ahead, as in the bf16 kernel.
+// Lifetimes: K(j) in bf16 stage j%3 is written in interval 2j-2 (converted)
+// or loaded from 2j-3 (bf16) and read in 2j, 2j+1; V(j) is written in 2j+1
+// (converted) or loaded from 2j-2 and read in 2j+2, 2j+3; int8 K(j) / V(j)
+// are loaded in 2j-5 / 2j-4 and converted in 2j-2 / 2j+1; the scales of tile
+// j are loaded in 2j-5 and read in 2j+1, 2j+2.  No write lands in a slot
+// whose previous reader runs in the same or a later interval, and every
+// interval ends with a workgroup barrier.
+// ---------------------------------------------------------------------------
+constexpr int kI8Stages = 3;
+constexpr int kScaleStages = 4;
+
+template <int D>
+struct I8Slot {
+  char k8[kBN * D];  // K rows, int8
+  char v8[kBN * D];  // V^T [D][64], int8
+};
+struct ScaleSlot {
+  float ks[kBN];
+  float vs[kBN];
+};
+
+// 8 int8 codes (two words) -> 8 bf16 holding the same integers (exact).
+__device__ __forceinline__ bf16x8 i8x8_bf16(uint32_t w0, uint32_t w1) {
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = float(int8_t(w0 >> (8 * i)));
+    f[4 + i] = float(int8_t(w1 >> (8 * i)));
+  }
+  return __builtin_convertvector(f, bf16x8);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 8].
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    default: wait_vmcnt<8>(); break;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPPThreads) void attn_i8_kernel(AttnArgs a) {
+  using S = SwzStage<D>;
+  constexpr int kLoads = 16 / S::kRowsPerLoad;       // bf16 loads per wave per tile side
+  constexpr int kI8Loads = kBN * D / (16 * 256);     // int8 loads per wave per tile side
+  static_assert(kI8Loads >= 1 && kI8Loads <= 2, "int8 tile pieces per lane");
+  __shared__ __attribute__((aligned(16))) S stage[kI8Stages];
+  __shared__ __attribute__((aligned(16))) I8Slot<D> ring[kI8Stages];
+  __shared__ __attribute__((aligned(16))) ScaleSlot sring[kScaleStages];
+
+  int head, qtile;
+  xcd_unit(head, qtile);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;
+  const int wq = wave & 3;
+  const int r32 = lane & 31;
+  const int half = lane >> 5;
+  const QueryTile qt = query_tile(a, qtile, kPPBM);
+  const int n_seg = __builtin_amdgcn_readfirstlane(qt.n_seg);
+  const int qi = qt.q0 + wave * 32 + r32;
+  const bool q_ok = qi < qt.q_end;
+  const float c = a.scale * kLog2e;
+  const int64_t qrow = (int64_t(qi) * a.H + head) * D;
+
+  u32x4 qw[D / 16];
+  {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) qw[j] = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  // Scores leave the MFMA raw (accumulators start at zero); the softmax
+  // forms s = raw * ks - m_run (log2 units) itself.
+  float m_run = 0.f;
+  f32x16 zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+  float l_run = 0.f;
+  bf16x8 pb[4];
+
+  const int k_row = r32 * S::kRowB + ((half ^ (r32 & 1)) << 4);
+  const int k_x = r32 & (S::kGran - 2);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  int voff[2][D / 32];
+#pragma unroll
+  for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
+      const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+      voff[aa][db] = v_swz<D>(row, col >> 3) + ((col & 7) << 1);
+    }
+  int vb[4];
+  {
+    const int f = (r32 >> 1) & 7;
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+      vb[step] = r32 * 128 + ((((2 * step) ^ (f & 6)) | (half ^ (f & 1))) << 4);
+  }
+
+  const int n = count_tiles(a, n_seg);
+  if (n == 0) return;
+  // tiles of the leading int8 runs (the cache; the current chunk follows)
+  int n8 = 0;
+  for (int r = 0; r < n_seg && a.seg[r].i8; ++r) n8 += (a.seg[r].len + kBN - 1) / kBN;
+  n8 = __builtin_amdgcn_readfirstlane(n8);
+  RunCursor cu;  // tile being softmaxed (masking)
+  cu.open(a, head, 0);
+  RunCursor ld;  // next tile to load (A: its K side and the scales, B: its V side)
+  ld.open(a, head, 0);
+
+  // Loads this wave issued in its last issuing phase (c1) and the one before
+  // (c2): what may still be in flight behind an older tile.
+  int c1 = 0, c2 = 0;
+  // Issuing phase p (softmax phase p; the prologue runs p = -3, -2, -1): the
+  // int8 tile p+3, or the bf16 tile p+2, of this group's side.  kMayI8: an
+  // int8 tile can be due.
+  auto issue_phase = [&](int p, auto may_i8_tag) {
+    constexpr bool kMayI8 = decltype(may_i8_tag)::value;
+    int cnt = 0;
+    if (kMayI8 && p + 3 < n8) {
+      const int j = p + 3;
+      char* dst = group == 0 ? ring[j % kI8Stages].k8 : ring[j % kI8Stages].v8;
+      const uint32_t base = uint32_t(ld.tile) * uint32_t(kBN * D);
+#pragma unroll
+      for (int i = 0; i < kI8Loads; ++i) {
+        const int idx = i * 256 + wq * 64;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(group == 0 ? ld.rk : ld.rv,
+                                                 (__attribute__((address_space(3))) void*)(dst + idx * 16), 16,
+                                                 base + uint32_t(idx + lane) * 16, 0, 0, 0);
+      }
+      cnt = kI8Loads;
+      if (group == 0 && wq < 2) {
+        float* sd = wq == 0 ? sring[j % kScaleStages].ks : sring[j % kScaleStages].vs;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wq == 0 ? ld.rks : ld.rvs,
+                                                 (__attribute__((address_space(3))) void*)(sd), 4,
+                                                 uint32_t(ld.tile * kBN + lane) * 4, 0, 0, 0);
+        ++cnt;
+      }
+      ld.advance(a, head);
+    } else if (p + 2 >= n8 && p + 2 < n) {
+      const int j = p + 2;
+      if (group == 0) dma_rows<D>(ld, false, stage[j % kI8Stages].k, 16 * wq, lane);
+      else dma_rows<D>(ld, true, stage[j % kI8Stages].v, 16 * wq, lane);
+      cnt = kLoads;
+      ld.advance(a, head);
+    }
+    c2 = c1;
+    c1 = cnt;
+  };
+
+  // Conversion of this group's side of int8 tile j (A: K rows into bf16
+  // stage j%3 in the swizzled row layout; B: V^T rows of 64 keys, 128 bytes,
+  // in the layout dma_vt gives), in pieces run between MFMAs: at i == 1 wait
+  // for the wave's own loads of the tile (vmcnt(behind): loads issued after
+  // them) and read its int8 pieces, then convert and store piece p at
+  // i == 4 + 4p.
+  struct Conv {
+    u32x4 w[2];
+  };
+  auto conv_step = [&](int i, int j, int behind, Conv& cv) {
+    const I8Slot<D>& rg = ring[j % kI8Stages];
+    if (i == 1) {
+      wait_vmcnt_dyn(behind);
+#pragma unroll
+      for (int p = 0; p < kI8Loads; ++p)
+        cv.w[p] = *reinterpret_cast<const u32x4*>((group == 0 ? rg.k8 : rg.v8) + (p * 256 + wq * 64 + lane) * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < kI8Loads; ++p) {
+      if (i != 4 + 4 * p) continue;
+      const int o = (p * 256 + wq * 64 + lane) * 16;
+      const bf16x8 lo = i8x8_bf16(cv.w[p][0], cv.w[p][1]);
+      const bf16x8 hi = i8x8_bf16(cv.w[p][2], cv.w[p][3]);
+      if (group == 0) {
+        const int row = o / D, g = (o % D) / 8;
+        char* dst = reinterpret_cast<char*>(stage[j % kI8Stages].k);
+        *reinterpret_cast<bf16x8*>(dst + k_swz<D>(row, g)) = lo;
+        *reinterpret_cast<bf16x8*>(dst + k_swz<D>(row, g + 1)) = hi;
+      } else {
+        const int d = o / kBN, g = (o % kBN) / 8;
+        char* dst = reinterpret_cast<char*>(stage[j % kI8Stages].v) + d * 128;
+        *reinterpret_cast<bf16x8*>(dst + ((g ^ ((d >> 1) & 7)) << 4)) = lo;
+        *reinterpret_cast<bf16x8*>(dst + (((g + 1) ^ ((d >> 1) & 7)) << 4)) = hi;
+      }
+    }
+  };
+  // In MFMA phase t group A converts K(t+1) (loaded in phase t-2; phase t-1
+  // issued after it), group B V(t) (loaded in phase t-3; phases t-2 and t-1
+  // after it).
+  auto conv_of_phase = [&](int t, int& j, int& behind) -> bool {
+    j = group == 0 ? t + 1 : t;
+    behind = group == 0 ? c1 : c1 + c2;
+    return j < n8;
+  };
+
+  const std::true_type scaled{}, may_i8{};
+  const std::false_type plain{}, bf16_only{};
+  // Prologue: issuing phases -3..-1 (int8 tiles 0..2 / bf16 tiles up to 1);
+  // group A converts K(0) (group B converts V(0) in its MFMA phase 0).
+  issue_phase(-3, may_i8);
+  issue_phase(-2, may_i8);
+  issue_phase(-1, may_i8);
+  if (group == 0) {
+    if (n8 > 0) {
+      Conv cv;
+      for (int i = 1; i <= 8; ++i) conv_step(i, 0, c1 + c2, cv);
+    } else {
+      wait_vmcnt_dyn(c1);  // bf16 K(0)
+    }
+  }
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    f32x8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, qw[j][i] << 16) * c;
+      f[2 * i + 1] = __builtin_bit_cast(float, qw[j][i] & 0xffff0000u) * c;
+    }
+    qf[j] = __builtin_convertvector(f, bf16x8);
+  }
+  wg_barrier();
+  if (group == 1) wg_barrier();  // group B runs one interval behind
+
+  f32x16 s[2];
+
+  // After MFMA phase t: group B makes sure a bf16 V(t) has landed (A's MFMA
+  // phase t+1 reads it); it was loaded in phase t-2, phase t-1 after it.
+  auto after_mfma = [&](int t) {
+    if (group == 1 && t >= n8 && t < n) wait_vmcnt_dyn(c1);
+  };
+
+  // Softmax phase t (kScaled: tile t is int8; kMayI8: an int8 tile can be
+  // due for loading): the loads of issuing phase t, then the online softmax
+  // of S(t); group A then makes sure a bf16 K(t+1) has landed.
+  auto softmax_phase = [&](int t, auto scaled_tag, auto may_i8_tag) {
+    constexpr bool kScaled = decltype(scaled_tag)::value;
+    issue_phase(t, may_i8_tag);
+    const int valid = min(kBN, cu.len - cu.tile * kBN);
+    cu.advance(a, head);
+    const float* ksl = sring[t % kScaleStages].ks;
+    const float* vsl = sring[t % kScaleStages].vs;
+    if constexpr (kScaled) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 k4 = *reinterpret_cast<const float4*>(ksl + kb * 32 + 8 * i + 4 * half);
+          s[kb][4 * i + 0] = fmaf(s[kb][4 * i + 0], k4.x, -m_run);
+          s[kb][4 * i + 1] = fmaf(s[kb][4 * i + 1], k4.y, -m_run);
+          s[kb][4 * i + 2] = fmaf(s[kb][4 * i + 2], k4.z, -m_run);
+          s[kb][4 * i + 3] = fmaf(s[kb][4 * i + 3], k4.w, -m_run);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= m_run;
+    }
+    if (valid < kBN) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= valid) s[kb][r] = -INFINITY;
+        }
+    }
+    auto tile_max = [&]() {
+      float mp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
+      return swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    };
+    auto shift_reference = [&](float sh, bool rescale) {
+      if (rescale) {
+        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+      m_run += sh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
+    };
+    // P = 2^s; the PV operand takes bf16(P * vs) (V scale folded in), the
+    // row sum P itself.
+    auto form_p = [&]() {
+      float ls[2] = {0.f, 0.f};
+#pragma unroll
+      for (int step = 0; step < 4; ++step) {
+        const int kb = step >> 1, r0 = 8 * (step & 1);
+        float4 v4[2];
+        if constexpr (kScaled) {
+          v4[0] = *reinterpret_cast<const float4*>(vsl + kb * 32 + 2 * r0 + 4 * half);
+          v4[1] = *reinterpret_cast<const float4*>(vsl + kb * 32 + 2 * r0 + 8 + 4 * half);
+        }
+        u32x4 pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * i]);
+          const float p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * i + 1]);
+          ls[i & 1] += p0 + p1;
+          f32x2 f = {p0, p1};
+          if constexpr (kScaled) {
+            const float4& vv = v4[i >> 1];
+            f[0] *= (i & 1) ? vv.z : vv.x;
+            f[1] *= (i & 1) ? vv.w : vv.y;
+          }
+          pw[i] = __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+        }
+        pb[step] = __builtin_bit_cast(bf16x8, pw);
+      }
+      return ls[0] + ls[1];
+    };
+    if (t == 0) shift_reference(tile_max(), false);
+    float lt = form_p();
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit))) {
+      shift_reference(fmaxf(tile_max(), 0.f), true);
+      lt = form_p();
+    }
+    l_run += lt;
+    if (group == 0 && t + 1 >= n8 && t + 1 < n) wait_vmcnt_dyn(c1);  // bf16 K(t+1)
+  };
+
+  auto kt = [&](int t) { return reinterpret_cast<const char*>(stage[t % kI8Stages].k); };
+  auto vt = [&](int t) { return reinterpret_cast<const char*>(stage[t % kI8Stages].v); };
+
+  // MFMA phase t with the conversion due in it (if any; kConv: one can be
+  // due in this phase variant) between its MFMAs.
+  auto run_mfma = [&](int t, auto qk_tag, auto pv_tag, auto vt_tag, auto conv_tag) {
+    constexpr bool kQK = decltype(qk_tag)::value, kPV = decltype(pv_tag)::value;
+    constexpr bool kVTl = decltype(vt_tag)::value, kConv = decltype(conv_tag)::value;
+    int j = 0, behind = 0;
+    const bool conv = kConv && conv_of_phase(t, j, behind);
+    Conv cv;
+    auto extra = [&](int i) {
+      if (kConv && conv) conv_step(i, j, behind, cv);
+    };
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<D, kQK, kPV, kVTl>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, zero, s, o, pb, extra);
+    __builtin_amdgcn_s_setprio(0);
+    after_mfma(t);
+  };
+
+  const std::true_type yes{};
+  const std::false_type no{};
+  run_mfma(0, yes, no, no, yes);
+  wg_barrier();
+  if (n8 > 0) softmax_phase(0, scaled, may_i8);
+  else softmax_phase(0, plain, bf16_only);
+  wg_barrier();
+  // t < n8: QK of an int8 tile, PV of an int8 tile (transposed V);
+  // t == n8: QK of the first bf16 tile, PV of the last int8 tile;
+  // t > n8: bf16 tiles, row-major V (transpose reads).
+  const int t1 = min(n8, n);
+  for (int t = 1; t < t1; ++t) {
+    run_mfma(t, yes, yes, yes, yes);
+    wg_barrier();
+    softmax_phase(t, scaled, may_i8);
+    wg_barrier();
+  }
+  if (n8 >= 1 && n8 < n) {
+    const int t = n8;
+    run_mfma(t, yes, yes, yes, no);
+    wg_barrier();
+    softmax_phase(t, plain, bf16_only);
+    wg_barrier();
+  }
+  for (int t = max(n8 + 1, 1); t < n; ++t) {
+    run_mfma(t, yes, yes, no, no);
+    wg_barrier();
+    softmax_phase(t, plain, bf16_only);
+    wg_barrier();
+  }
+  if (n - 1 < n8) run_mfma(n, no, yes, yes, no);
+  else run_mfma(n, no, yes, no, no);
+  wg_barrier();
+  wg_barrier();  // the softmax phase n does not exist; keep the two groups' barrier counts equal
+  if (group == 0) wg_barrier();
+
+  const float l_tot = swap_halves_sum(l_run);
+  if (!q_ok) return;
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = db * 32 + 8 * gq + 4 * half;
+      float4 f = make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
+                             o[db][4 * gq + 3] * inv);
+      const bf16x4 b = __builtin_convertvector(*reinterpret_cast<float __attribute__((__vector_size__(16)))*>(&f), bf16x4);
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + qrow + d0) = b;
+    }
+  if (a.lse && half == 0) a.lse[int64_t(head) * a.n_q + qi] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // fp32 activations: same run/tile walk and online softmax, fp32 MFMA 32x32x2,
 // single LDS stage (small correctness-first shapes).
 // ---------------------------------------------------------------------------
@@ -883,16 +1342,15 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(CopyArgs a) {
   }
 }
 
-// bf16 staging of an I8 layer for the attention, one workgroup per (head,
-// 64-key tile, listed chunk): every code becomes bf16(q * s) with the row's
-// fp32 scale (the fma of int8x8_dequant_bf16x8), once per call instead of
-// once per query tile.  K rows are written in place of the same rows of the
-// staging K; V goes through LDS to the transposed tile of the chunk's slot
-// (column p holds key p with bits 2 and 3 swapped; zeros past the chunk).
+// bf16 staging of an I8 layer (for the backward and the linear-attention
+// variant), one workgroup per (head, 64-key tile, listed chunk): every code
+// becomes bf16(q * s) with its key's fp32 scale.  K rows are written in place
+// of the same rows of the staging K; the V tile ([D][64], column p holding
+// key p with bits 2 and 3 swapped) goes to the same tile of the staging V,
+// zeros past the chunk.
 template <int D>
 __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
   constexpr int kG = D / 8;  // 8-code groups per row
-  __shared__ __attribute__((aligned(16))) __bf16 t[kBN][D + 8];
   const int h = blockIdx.x / a.tps;
   const int tile = blockIdx.x % a.tps;
   const int chunk = blockIdx.y;
@@ -900,84 +1358,126 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
   const int valid = min(kBN, a.ctok - tile * kBN);
   const int64_t row_base = int64_t(h) * a.rows + a.row0[chunk] + tile * kBN;  // head-major row index
   const char* kq = a.layer + a.k_off;
-  const char* vq = a.layer + a.v_off;
   const float* ks = reinterpret_cast<const float*>(a.layer + a.ks_off);
   const float* vs = reinterpret_cast<const float*>(a.layer + a.vs_off);
   __bf16* dk = reinterpret_cast<__bf16*>(a.dst_k);
 #pragma unroll
   for (int it = tid; it < kBN * kG; it += 256) {
     const int key = it / kG, g = it % kG;
-    u32x4 vw = {0, 0, 0, 0};
     if (key < valid) {
       const int64_t r = row_base + key;
       const uint2 kc = *reinterpret_cast<const uint2*>(kq + r * D + g * 8);
-      const uint2 vc = *reinterpret_cast<const uint2*>(vq + r * D + g * 8);
       *reinterpret_cast<u32x4*>(dk + r * D + g * 8) = int8x8_dequant_bf16x8(u32x2{kc.x, kc.y}, ks[r]);
-      vw = int8x8_dequant_bf16x8(u32x2{vc.x, vc.y}, vs[r]);
     }
-    *reinterpret_cast<u32x4*>(&t[key][g * 8]) = vw;
+  }
+  // the tile's V scales in column order (zero past the chunk: padding codes are 0)
+  __shared__ float vsc[kBN];
+  if (tid < kBN) {
+    const int key = (tid & ~12) | ((tid & 4) << 1) | ((tid & 8) >> 1);
+    vsc[tid] = key < valid ? vs[row_base + key] : 0.f;
   }
   __syncthreads();
-  __bf16* dst = reinterpret_cast<__bf16*>(a.dst_v) + int64_t(h) * a.vt_head_elems +
-                (int64_t(a.slot[chunk]) * a.tps + tile) * (kBN * D);
+  const int64_t vt_off = int64_t(h) * a.vt_head_elems + (int64_t(a.slot[chunk]) * a.tps + tile) * (kBN * D);
+  const char* vq = a.layer + a.v_off + vt_off;
+  __bf16* dv = reinterpret_cast<__bf16*>(a.dst_v) + vt_off;
 #pragma unroll
   for (int it = tid; it < D * (kBN / 8); it += 256) {
     const int d = it / (kBN / 8), p0 = (it % (kBN / 8)) * 8;
+    const uint2 vc = *reinterpret_cast<const uint2*>(vq + d * kBN + p0);
+    const uint32_t wv[2] = {vc.x, vc.y};
     bf16x8 o;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = p0 + j;
-      o[j] = t[(p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)][d];
-    }
-    *reinterpret_cast<bf16x8*>(dst + d * kBN + p0) = o;
+    for (int j = 0; j < 8; ++j)
+      o[j] = (__bf16)(float(int8_t(wv[j >> 2] >> (8 * (j & 3)))) * vsc[p0 + j]);
+    *reinterpret_cast<bf16x8*>(dv + d * kBN + p0) = o;
   }
 }
 
-// INT8 writer: one group of D/8 lanes per (head, row); each lane quantises
-// 8 values.  s = max|x| / 127 (IEEE fp32 division), q = clamp(rne(x / s)).
-__global__ __launch_bounds__(256) void quant_chunks_kernel(CopyArgs a) {
-  // 32-bit indexing: the host's grid covers ctok * H groups, far below 2^31.
-  const unsigned gl = unsigned(a.D) / 8;  // 16 or 8
-  const unsigned grp = (blockIdx.x * 256u + threadIdx.x) / gl;
-  const int li = int(threadIdx.x % gl);
-  const bool valid = grp < unsigned(a.ctok) * unsigned(a.H);
+// INT8 writer, one workgroup per (head, 64-token tile, chunk, K or V): each
+// token's D values of the head are quantised with s = max|x| / 127 (IEEE fp32
+// division) and q = clamp(rne(x / s), -127, 127) (s = 0, q = 0 for an
+// all-zero vector).  Thread groups of D/8 lanes hold one token (8 values per
+// lane), so max|x| is a reduction over those lanes.  K codes go to the cache
+// rows ([H][rows][D]); V codes are staged in LDS and written as the chunk
+// slot's transposed tile ([D][64], physical column p holding key p with bits
+// 2 and 3 swapped, zeros after the chunk's last key).  Scales go to the
+// [H][rows] fp32 arrays at the token's row.
+template <int D>
+__global__ __launch_bounds__(256) void quant_tile_kernel(CopyArgs a) {
+  constexpr int kG = D / 8;            // lanes per token
+  constexpr int kPer = kBN * kG / 256;  // tokens' groups per thread
+  __shared__ __attribute__((aligned(16))) uint8_t c8[kBN][D + 16];
+  const int h = blockIdx.x / a.tps;
+  const int tile = blockIdx.x % a.tps;
   const int chunk = blockIdx.y >> 1;
-  const int isv = blockIdx.y & 1;
+  const bool isv = blockIdx.y & 1;
   const int z = blockIdx.z;
-  const int row = valid ? int(grp % unsigned(a.ctok)) : 0;
-  const int h = valid ? int(grp / unsigned(a.ctok)) : 0;
-  float x[8];
-  if (valid) {
-    const __bf16* src = static_cast<const __bf16*>(isv ? a.src_v : a.src_k) + int64_t(z) * a.src_layer_elems +
-                        (int64_t(chunk) * a.ctok + row) * a.H * a.D + int64_t(h) * a.D + li * 8;
-    const uint4 w = *reinterpret_cast<const uint4*>(src);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const int tid = threadIdx.x;
+  const __bf16* src = static_cast<const __bf16*>(isv ? a.src_v : a.src_k) + int64_t(z) * a.src_layer_elems +
+                      int64_t(chunk) * a.ctok * a.H * D + int64_t(h) * D;
+  char* layer = a.dst + int64_t(z) * a.dst_layer_bytes;
+  float* scales = reinterpret_cast<float*>(layer + (isv ? a.vs_off : a.ks_off));
+  const int64_t row_base = int64_t(h) * a.rows + a.dst_row0[chunk] + tile * kBN;  // head-major row
+  const int valid = min(kBN, a.ctok - tile * kBN);
+  uint4 w[kPer];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __builtin_bit_cast(float, ww[i] << 16);
-      x[2 * i + 1] = __builtin_bit_cast(float, ww[i] & 0xffff0000u);
+  for (int i = 0; i < kPer; ++i) {
+    const int it = tid + 256 * i;
+    const int key = it / kG, g = it % kG;
+    w[i] = key < valid ? *reinterpret_cast<const uint4*>(src + int64_t(tile * kBN + key) * a.H * D + g * 8)
+                       : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int it = tid + 256 * i;
+    const int key = it / kG, g = it % kG;
+    const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, ww[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, ww[e] & 0xffff0000u);
     }
-  } else {
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int m = 1; m < kG; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float sc = amax / 127.0f;
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int qv = 0;
+      if (sc != 0.f) qv = int(fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f));
+      packed[e >> 2] |= uint32_t(qv & 0xff) << (8 * (e & 3));
+    }
+    if (key < valid) {
+      if (g == 0) scales[row_base + key] = sc;
+      if (!isv) *reinterpret_cast<uint2*>(layer + a.k_off + (row_base + key) * D + g * 8) = make_uint2(packed[0], packed[1]);
+    }
+    if (isv) *reinterpret_cast<uint2*>(&c8[key][g * 8]) = make_uint2(packed[0], packed[1]);  // zeros past the chunk
   }
-  float amax = 0.f;
+  if (!isv) return;
+  __syncthreads();
+  // [D][64] tile: thread (d, 16 columns) gathers its 16 keys' codes
+  char* dst = layer + a.v_off + int64_t(h) * a.vt_head_elems + (int64_t(a.dst_slot[chunk]) * a.tps + tile) * (kBN * D);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  for (int m = 1; m < int(gl); m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  if (!valid) return;
-  const float s = amax / 127.0f;
-  uint32_t packed[2] = {0, 0};
+  for (int it = tid; it < D * (kBN / 16); it += 256) {
+    const int d = it / (kBN / 16), p0 = (it % (kBN / 16)) * 16;
+    uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int qv = 0;
-    if (s != 0.f) qv = int(fminf(fmaxf(rintf(x[i] / s), -127.f), 127.f));
-    packed[i >> 2] |= uint32_t(qv & 0xff) << (8 * (i & 3));
+    for (int j4 = 0; j4 < 4; ++j4) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int p = p0 + 4 * j4 + b;
+        const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+        v |= uint32_t(c8[key][d]) << (8 * b);
+      }
+      o[j4] = v;
+    }
+    *reinterpret_cast<uint4*>(dst + d * kBN + p0) = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  char* base = a.dst + int64_t(z) * a.dst_layer_bytes;
-  const int64_t r = int64_t(h) * a.rows + a.dst_row0[chunk] + row;
-  *reinterpret_cast<uint2*>(base + (isv ? a.v_off : a.k_off) + r * a.D + li * 8) = make_uint2(packed[0], packed[1]);
-  if (li == 0) reinterpret_cast<float*>(base + (isv ? a.vs_off : a.ks_off))[r] = s;
 }
 
 template <typename K>
@@ -1004,6 +1504,7 @@ int launch_attention_d(const AttnArgs& args, void* stream) {
   }
   const dim3 grid(query_tiles(a, kPPBM), a.H);
   const dim3 block(kPPThreads);
+  if (a.seg[0].i8) return launch(attn_i8_kernel<D>, grid, block, &a, stream);
   if (a.n_seg == 1) return launch(attn_pp_kernel<D, true>, grid, block, &a, stream);
   return launch(attn_pp_kernel<D, false>, grid, block, &a, stream);
 }
@@ -1018,11 +1519,11 @@ int launch_attention(const AttnArgs& a, void* stream) {
 int launch_copy_chunks(const CopyArgs& a, void* stream) {
   if (a.n_chunks <= 0) return 0;
   if (a.kv == LL_I8) {
-    const int64_t threads = int64_t(a.ctok) * a.H * (a.D / 8);
-    const dim3 grid(unsigned((threads + 255) / 256), a.n_chunks * 2, a.n_layers);
-    return launch(quant_chunks_kernel, grid, dim3(256), &a, stream);
+    const dim3 grid(unsigned(a.H * a.tps), a.n_chunks * 2, a.n_layers);
+    return a.D == 64 ? launch(quant_tile_kernel<64>, grid, dim3(256), &a, stream)
+                     : launch(quant_tile_kernel<128>, grid, dim3(256), &a, stream);
   }
-  if (a.vt) {  // bf16 cache (the only one with transposed V)
+  if (a.vt) {  // bf16 cache
     const dim3 grid(unsigned(a.H * a.tps), a.n_chunks * 2, a.n_layers);
     return a.D == 64 ? launch(append_bf16_kernel<64>, grid, dim3(256), &a, stream)
                      : launch(append_bf16_kernel<128>, grid, dim3(256), &a, stream);

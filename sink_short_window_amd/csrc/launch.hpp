@@ -10,20 +10,26 @@ namespace ll {
 
 // One contiguous run of keys, addressed in place.  Element (head h, key i of
 // the run, dim d) of K lives at k + (h*head_stride + i*row_stride + d)
-// elements, and likewise V unless v_tiled.  A v_tiled run (bf16 cache) keeps
-// V transposed in 64-key tiles: element (h, i, d) at
+// elements, and likewise V unless v_tiled.  A v_tiled run (bf16 and int8
+// caches) keeps V transposed in 64-key tiles: element (h, i, d) at
 // v + h*v_head_stride + (i/64)*64*D + d*64 + p, where p is i%64 with bits 2
-// and 3 swapped (the key order of the PV operand).  Elements are of the
-// activation dtype (an I8 cache is attended through its bf16 staging copy).
+// and 3 swapped (the key order of the PV operand).  Elements are bf16 (or fp32
+// for fp32 activations), except in an i8 run: int8 codes of an INT8 cache
+// whose key i of head h has the fp32 scales ks[h*s_head_stride + i] (K) and
+// vs[h*s_head_stride + i] (V); the value it stands for is code * scale.
 struct KvSeg {
   const void* k;
   const void* v;
+  const float* ks;         // i8 runs
+  const float* vs;         // i8 runs
   int64_t head_stride;     // elements
   int64_t row_stride;      // elements
   int64_t v_head_stride;   // elements, v_tiled runs
+  int64_t s_head_stride;   // scales per head, i8 runs
   int32_t key_start;       // first key index of the run in the joint key space
   int32_t len;             // keys in the run
   int32_t v_tiled;         // 1: V in transposed 64-key tiles (see above)
+  int32_t i8;              // 1: int8 codes with per-key scales (see above)
 };
 
 constexpr int kMaxSeg = 40;
@@ -68,7 +74,9 @@ struct AttnBwdArgs {
 // (token-major [ctok][H][D]); it goes to rows dst_row0[i] .. + ctok of every
 // head in the destination layer z (cache base + z*dst_layer_bytes).  With vt,
 // V goes instead to chunk slot dst_slot[i] of the transposed tile layout
-// (tps tiles of [D][64] per slot, vt_head_elems per head, zero padding).
+// (tps tiles of [D][64] per slot, vt_head_elems per head, zero padding).  An
+// I8 cache also gets each token's K and V scales at the same rows of its
+// [H][rows] fp32 scale arrays.
 constexpr int kMaxCopyChunks = LL_MAX_RING_SLOTS + 1;
 struct CopyArgs {
   const void* src_k = nullptr;
@@ -93,11 +101,11 @@ struct CopyArgs {
 };
 
 // Each returns 0 on success or the hipError_t code of the failed launch.
-// bf16 staging copy of an I8 layer's resident chunks for the attention: each
-// listed chunk (rows row0[i] .. + ctok of every head) is dequantised to
-// bf16(q * s) into K rows [H][rows][D] at dst_k (same row index) and V tiles
-// of chunk slot slot[i] at dst_v ([H][nslots*tps][D][64], key order and zero
-// padding as the BF16 cache stores V).
+// bf16 staging copy of an I8 layer's resident chunks for the backward and the
+// linear-attention variant: each listed chunk (rows row0[i] .. + ctok of every
+// head; V tiles of chunk slot slot[i]) is dequantised to bf16(q * s) into K
+// rows [H][rows][D] at dst_k (same row index) and V tiles of the same slot at
+// dst_v ([H][nslots*tps][D][64], key order and zero padding as the cache).
 struct StageArgs {
   const char* layer = nullptr;  // I8 layer base
   int64_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0;

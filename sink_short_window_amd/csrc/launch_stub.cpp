@@ -86,14 +86,14 @@ int llh_attn_calls(void) { return ll::g_attn_calls; }
 int llh_copy_calls(void) { return ll::g_copy_calls; }
 
 // Last attention launch: n_seg, n_keys, and per run [k, v, head_stride,
-// row_stride, key_start, len, v_head_stride, v_tiled] (pointers as
-// integers).
-int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][8] */) {
+// row_stride, key_start, len, v_head_stride, v_tiled, ks, vs, i8] (pointers
+// as integers).
+int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][11] */) {
   const ll::AttnArgs& a = ll::g_attn;
   *n_keys = a.n_keys;
   for (int i = 0; i < a.n_seg; ++i) {
     const ll::KvSeg& s = a.seg[i];
-    int64_t* r = runs + 8 * i;
+    int64_t* r = runs + 11 * i;
     r[0] = int64_t(reinterpret_cast<intptr_t>(s.k));
     r[1] = int64_t(reinterpret_cast<intptr_t>(s.v));
     r[2] = s.head_stride;
@@ -102,6 +102,9 @@ int llh_last_attn(int64_t* n_keys, int64_t* runs /* [n_seg][8] */) {
     r[5] = s.len;
     r[6] = s.v_head_stride;
     r[7] = s.v_tiled;
+    r[8] = int64_t(reinterpret_cast<intptr_t>(s.ks));
+    r[9] = int64_t(reinterpret_cast<intptr_t>(s.vs));
+    r[10] = s.i8;
   }
   return a.n_seg;
 }

@@ -46,9 +46,11 @@ ll_status launched(int err, const char* what) {
 // Key runs of a layer's cache, in the order the attention kernels walk them:
 // the sink (for a BF16 or I8 cache one run per sink chunk, each with its own
 // slot of V tiles; for F32 one run), then the resident ring chunks, oldest
-// first.  An I8 cache's runs point into its bf16 staging area (see
-// stage_int8).  Appends to a.seg and keys; returns the number of sink runs.
-int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int32_t& keys) {
+// first.  An I8 cache's runs are int8 codes with their scales, or, with
+// `staged`, point into its bf16 staging area (see stage_int8).  Appends to
+// a.seg and keys; returns the number of sink runs.
+int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int32_t& keys,
+                   bool staged = false) {
   const ll::Geometry& g = cs.geom();
   const ll::Layout& lay = cs.layout();
   const char* buf = static_cast<const char*>(cs.buffer());
@@ -58,8 +60,11 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
     ll::KvSeg& s = a.seg[a.n_seg++];
     s.head_stride = g.rows * g.D;
     s.row_stride = g.D;
+    s.ks = s.vs = nullptr;
+    s.s_head_stride = 0;
+    s.i8 = 0;
     const int64_t slot = ll::slot_of_row(g, row0);
-    if (g.staged) {  // bf16 staging copy in the BF16 layout
+    if (staged && g.staged) {  // bf16 staging copy in the BF16 layout
       s.k = buf + lay.stage_k_off + size_t(row0 * g.D) * 2;
       s.v = buf + lay.stage_v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * 2;
       s.v_head_stride = g.vt_head_elems;
@@ -69,6 +74,12 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
       s.v = base + lay.v_off + size_t(slot * g.tps * ll::kVtTileKeys * g.D) * kelt;
       s.v_head_stride = g.vt_head_elems;
       s.v_tiled = 1;
+      if (g.kv == LL_I8) {
+        s.ks = reinterpret_cast<const float*>(base + lay.ks_off) + row0;
+        s.vs = reinterpret_cast<const float*>(base + lay.vs_off) + row0;
+        s.s_head_stride = g.rows;
+        s.i8 = 1;
+      }
     } else {
       s.k = base + lay.k_off + size_t(row0 * g.D) * kelt;
       s.v = base + lay.v_off + size_t(row0 * g.D) * kelt;
@@ -80,7 +91,7 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
     keys += int32_t(len);
   };
   const int64_t sink_rows = cs.sink_valid_rows(layer);
-  if (g.vt || g.staged) {
+  if (g.vt) {
     for (int64_t r0 = 0; r0 < sink_rows; r0 += g.ctok) add_cache_run(r0, g.ctok);
   } else if (sink_rows > 0) {
     add_cache_run(0, sink_rows);
@@ -90,11 +101,10 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
   return n_sink;
 }
 
-// An I8 cache is attended through a bf16 copy of the layer's resident chunks
-// (sink chunks and resident ring slots) in the staging area, dequantised to
-// bf16(q * s) by one launch per call: each code is converted once rather than
-// once per query tile, and the attention runs the bf16 kernel.  No-op for
-// other caches.
+// The backward and the linear-attention variant read an I8 cache through a
+// bf16 copy of the layer's resident chunks (sink chunks and resident ring
+// slots) in the staging area, dequantised to bf16(q * s) by one launch per
+// call.  No-op for other caches.
 int stage_int8(const ll::CacheState& cs, int32_t layer, void* stream) {
   const ll::Geometry& g = cs.geom();
   if (!g.staged) return 0;
@@ -130,10 +140,13 @@ void add_current_run(const ll::Geometry& g, const void* k_cur, const void* v_cur
   ll::KvSeg& s = a.seg[a.n_seg++];
   s.k = k_cur;
   s.v = v_cur;
+  s.ks = s.vs = nullptr;
   s.head_stride = g.D;
   s.row_stride = int64_t(g.H) * g.D;
   s.v_head_stride = 0;
+  s.s_head_stride = 0;
   s.v_tiled = 0;
+  s.i8 = 0;
   s.key_start = keys;
   s.len = int32_t(n_cur);
   keys += int32_t(n_cur);
@@ -193,6 +206,16 @@ ll_status ll_cache_get_config(const ll_cache* cache, ll_cache_config* cfg) {
   if (!cfg) return fail(LL_ERR_INVALID_ARG, "cfg is NULL");
   const ll::Geometry& g = cache->state.geom();
   *cfg = ll_cache_config{g.L, g.H, g.D, g.T, g.C, g.S, g.W, g.act, g.kv};
+  return LL_OK;
+}
+
+ll_status ll_cache_set_int8_dequant(ll_cache* cache, int32_t mode) {
+  ll::clear_error();
+  if (!cache) return fail(LL_ERR_INVALID_ARG, "cache handle is NULL");
+  if (mode != LL_I8_STAGED && mode != LL_I8_IN_KERNEL)
+    return fail(LL_ERR_INVALID_ARG, "mode must be LL_I8_STAGED or LL_I8_IN_KERNEL");
+  if (cache->state.geom().kv != LL_I8) return fail(LL_ERR_INVALID_ARG, "the cache's kv_dtype is not I8");
+  cache->state.set_int8_dequant(mode);
   return LL_OK;
 }
 
@@ -375,7 +398,8 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   }
   ll::AttnArgs a;
   int32_t keys = 0;
-  add_cache_runs(cs, layer, a, keys);
+  const bool staged = cs.int8_dequant() == LL_I8_STAGED;
+  add_cache_runs(cs, layer, a, keys, staged);
   if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, a, keys);
   if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
   if (n_q == 0) return LL_OK;
@@ -388,7 +412,7 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
   a.D = g.D;
   a.act = g.act;
   a.scale = scale;
-  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
+  if (staged && (st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "attention launch");
 }
 
@@ -418,7 +442,7 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
   }
   ll::AttnBwdArgs b;
   int32_t keys = 0;
-  add_cache_runs(cs, layer, b.a, keys);
+  add_cache_runs(cs, layer, b.a, keys, /*staged=*/true);
   if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, b.a, keys);
   if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
   b.a.n_keys = keys;
@@ -460,7 +484,8 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
   if (lse && !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   ll::AttnArgs a;
   int32_t keys = 0;
-  const int n_sink = add_cache_runs(cs, layer, a, keys);
+  const bool staged = cs.int8_dequant() == LL_I8_STAGED;
+  const int n_sink = add_cache_runs(cs, layer, a, keys, staged);
   a.n_keys = keys;
   a.q = q;
   a.out = out;
@@ -472,7 +497,7 @@ ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const vo
   a.scale = scale;
   a.q_chunk = int32_t(g.ctok);
   a.n_seg0 = n_sink + 1;
-  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
+  if (staged && (st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
   return launched(ll::launch_attention(a, stream), "re-encoding attention launch");
 }
 
@@ -507,7 +532,7 @@ ll_status ll_sink_window_linear_attn(const ll_cache* cache, int32_t layer, const
   ll::LinArgs p;
   ll::AttnArgs& a = p.a;
   int32_t keys = 0;
-  add_cache_runs(cs, layer, a, keys);
+  add_cache_runs(cs, layer, a, keys, /*staged=*/true);
   if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, a, keys);
   if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
   if (n_q == 0) return LL_OK;
@@ -557,10 +582,13 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   ll::KvSeg& s = a.seg[0];
   s.k = k_txt;
   s.v = v_txt;
+  s.ks = s.vs = nullptr;
   s.head_stride = head_dim;
   s.row_stride = int64_t(num_heads) * head_dim;
   s.v_head_stride = 0;
+  s.s_head_stride = 0;
   s.v_tiled = 0;
+  s.i8 = 0;
   s.key_start = 0;
   s.len = int32_t(n_txt);
   a.n_seg = 1;

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG, "lib", "libll.so")
 LL_F32, LL_BF16, LL_I8 = 0, 1, 2
 LL_WHICH_K, LL_WHICH_V, LL_WHICH_KSCALE, LL_WHICH_VSCALE = 0, 1, 2, 3
 LL_SEG_SINK, LL_SEG_RING = 0, 1
+LL_I8_STAGED, LL_I8_IN_KERNEL = 0, 1
 LL_MAX_RING_SLOTS = 30
 
 STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR_UNSUPPORTED",
@@ -27,7 +28,7 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
 
 # Every function include/ll.h declares (checked against the header by the tests).
 EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_get_config", "ll_cache_destroy",
-           "ll_cache_reset",
+           "ll_cache_reset", "ll_cache_set_int8_dequant",
            "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
            "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_sink_window_linear_attn",
            "ll_linear_attn_workspace_bytes", "ll_cross_attn", "ll_cache_query", "ll_cache_layout",
@@ -58,6 +59,7 @@ _SIGS = {
     "ll_cache_get_config": (_i32, [_vp, _P(ll_cache_config)]),
     "ll_cache_destroy": (_i32, [_vp]),
     "ll_cache_reset": (_i32, [_vp]),
+    "ll_cache_set_int8_dequant": (_i32, [_vp, _i32]),
     "ll_cache_append_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "ll_cache_recache": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp]),
     "ll_sink_window_attn": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
@@ -196,6 +198,12 @@ def ll_cache_get_config(handle, lib=None):
 def ll_cache_destroy(handle, lib=None):
     lib = lib or load()
     _check(lib, lib.ll_cache_destroy(handle))
+
+
+def ll_cache_set_int8_dequant(handle, mode, lib=None):
+    """LL_I8_STAGED (default) or LL_I8_IN_KERNEL for an I8 cache."""
+    lib = lib or load()
+    _check(lib, lib.ll_cache_set_int8_dequant(handle, int(mode)))
 
 
 def ll_cache_reset(handle, lib=None):
@@ -429,6 +437,9 @@ class Cache:
     def reset(self):
         ll_cache_reset(self.handle)
 
+    def set_int8_dequant(self, mode):
+        ll_cache_set_int8_dequant(self.handle, mode)
+
     def query(self, layer):
         return ll_cache_query(self.handle, layer, self.ring_slots)
 
@@ -437,12 +448,13 @@ class Cache:
         return self.cfg.tokens_per_frame * self.cfg.frames_per_chunk
 
     def v_tiled(self):
-        """True when V is stored transposed in 64-key tiles (BF16 cache)."""
-        return self.cfg.kv_dtype == LL_BF16
+        """True when V is stored transposed in 64-key tiles (BF16 and I8 caches)."""
+        return self.cfg.kv_dtype != LL_F32
 
     def tensor(self, layer, which, segment):
         """A strided view of a cached tensor inside the device buffer:
-        [H][rows][cols], or [H][tiles][D][64] for the tiled V of a BF16 cache."""
+        [H][rows][cols], or [H][tiles][D][64] for the tiled V of a BF16 or I8
+        cache."""
         torch = _torch()
         off, strides, shape = ll_cache_layout(self.handle, layer, which, segment)
         if which in (LL_WHICH_KSCALE, LL_WHICH_VSCALE):

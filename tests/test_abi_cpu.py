@@ -42,7 +42,8 @@ def libs():
     return stub
 
 
-RUN_FIELDS = 8   # llh_last_attn: k, v, head_stride, row_stride, key_start, len, v_head_stride, v_tiled
+RUN_FIELDS = 11  # llh_last_attn: k, v, head_stride, row_stride, key_start, len, v_head_stride, v_tiled,
+                 # ks, vs, i8
 VT_KEYS = 64
 
 
@@ -130,7 +131,7 @@ def test_required_bytes_matches_layout(libs, kw):
     rows = S * T + (W - C) // C * C * T
     esz = {ll.LL_F32: 4, ll.LL_BF16: 2, ll.LL_I8: 1}[c.kv_dtype]
     kb = _align(H * rows * D * esz)
-    if c.kv_dtype == ll.LL_BF16:     # V transposed in whole 64-key tiles per chunk slot
+    if c.kv_dtype != ll.LL_F32:      # V transposed in whole 64-key tiles per chunk slot
         slots = S // C + (W - C) // C
         vb = _align(H * slots * tiles_per_slot(C * T) * VT_KEYS * D * esz)
     else:
@@ -289,7 +290,7 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
                 covered = []
                 start = 0
                 for i in range(n_seg):
-                    kp, vp, hs, rs, ks, ln, vhs, vtl = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
+                    kp, vp, hs, rs, ks, ln, vhs, vtl = runs[RUN_FIELDS * i:RUN_FIELDS * i + 8]
                     assert ks == start and ln > 0
                     start += ln
                     if kp == FAKE_ACT:                 # current chunk, token-major
@@ -318,6 +319,89 @@ def test_attention_key_runs_cover_exactly_the_allowed_chunks(libs):
         libs.ll_cache_destroy(h)
 
 
+def test_int8_dequant_mode_setter(libs):
+    h = create(libs, cfg(kv=ll.LL_I8))
+    for bad in (-1, 2, 7):
+        assert status(libs, libs.ll_cache_set_int8_dequant(h, bad)) == "LL_ERR_INVALID_ARG"
+    assert libs.ll_cache_set_int8_dequant(h, ll.LL_I8_IN_KERNEL) == 0
+    assert libs.ll_cache_set_int8_dequant(h, ll.LL_I8_STAGED) == 0
+    assert status(libs, libs.ll_cache_set_int8_dequant(None, 0)) == "LL_ERR_INVALID_ARG"
+    h2 = create(libs, cfg())
+    assert status(libs, libs.ll_cache_set_int8_dequant(h2, ll.LL_I8_IN_KERNEL)) == "LL_ERR_INVALID_ARG"
+    libs.ll_cache_destroy(h)
+    libs.ll_cache_destroy(h2)
+
+
+def test_int8_attention_staged_by_default(libs):
+    """By default an I8 cache's attention launches the bf16 staging of the
+    layer's resident chunks first, and its cache runs read the staging copy
+    (bf16 K rows, bf16 V tiles), not the codes."""
+    T, C, S, W, H, D = 40, 2, 2, 8, 3, 64
+    c = cfg(L=2, T=T, C=C, S=S, W=W, H=H, D=D, kv=ll.LL_I8)
+    h = create(libs, c)
+    for _ in range(4):
+        assert libs.ll_cache_append_chunk(h, 1, FAKE_ACT, FAKE_ACT, None) == 0
+    stages = libs.llh_stage_calls()
+    assert libs.ll_sink_window_attn(h, 1, FAKE_ACT, 5, FAKE_ACT, FAKE_ACT, C * T, 0.125,
+                                    FAKE_ACT, None, None) == 0, libs.ll_last_error()
+    assert libs.llh_stage_calls() == stages + 1
+    row0 = (ctypes.c_int32 * 40)()
+    slot = (ctypes.c_int32 * 40)()
+    bases = (ctypes.c_int64 * 3)()
+    n_st = libs.llh_last_stage(row0, slot, bases)
+    nk = ctypes.c_int64()
+    runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+    n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+    assert n_st == n_seg - 1                                   # every cache run is staged
+    for i in range(n_seg - 1):
+        kp, vp, _, _, _, ln, _, vtl, ksp, vsp, i8 = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
+        assert (i8, vtl, ksp, vsp) == (0, 1, 0, 0)
+        assert kp == bases[1] + 2 * row0[i] * D and vp >= bases[2]
+    libs.ll_cache_destroy(h)
+
+
+def test_int8_attention_reads_codes_in_place(libs):
+    """With LL_I8_IN_KERNEL an I8 cache is attended in place: every cache run
+    is an int8 run whose K points at the chunk's code rows, V at its slot of
+    int8 V tiles and the scale pointers at the same rows of the K and V scale
+    arrays; the current chunk stays a bf16 run; no staging launch is
+    enqueued."""
+    T, C, S, W, H, D = 40, 2, 2, 8, 3, 64
+    c = cfg(L=2, T=T, C=C, S=S, W=W, H=H, D=D, kv=ll.LL_I8)
+    g = CacheGeometry(T, C, S, W)
+    h = create(libs, c)
+    assert libs.ll_cache_set_int8_dequant(h, ll.LL_I8_IN_KERNEL) == 0
+    sim = DequeCacheModel(g)
+    ct = g.chunk_tokens
+    tps = tiles_per_slot(ct)
+    k_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
+    v_off, st_v, _ = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
+    ks_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_KSCALE, ll.LL_SEG_SINK)
+    vs_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_VSCALE, ll.LL_SEG_SINK)
+    stages = libs.llh_stage_calls()
+    for chunk in range(6):
+        assert libs.ll_sink_window_attn(h, 1, FAKE_ACT, 5, FAKE_ACT, FAKE_ACT, ct, 0.125,
+                                        FAKE_ACT, None, None) == 0, libs.ll_last_error()
+        nk = ctypes.c_int64()
+        runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+        n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+        for i in range(n_seg - 1):
+            kp, vp, hs, rs, _, ln, vhs, vtl, ksp, vsp, i8 = runs[RUN_FIELDS * i:RUN_FIELDS * (i + 1)]
+            row = kp - FAKE_BUF - k_off                     # int8: one byte per element
+            assert row % D == 0
+            row //= D
+            assert (i8, vtl, hs, rs, vhs, ln) == (1, 1, (S * T + g.ring_slots * ct) * D, D, st_v[0], ct)
+            slot = row // ct if row < S * T else S // C + (row - S * T) // ct
+            assert vp - FAKE_BUF - v_off == slot * tps * VT_KEYS * D
+            assert ksp - FAKE_BUF - ks_off == 4 * row and vsp - FAKE_BUF - vs_off == 4 * row
+        last = runs[RUN_FIELDS * (n_seg - 1):RUN_FIELDS * n_seg]
+        assert last[0] == FAKE_ACT and last[10] == 0 and last[8] == 0
+        assert libs.ll_cache_append_chunk(h, 1, FAKE_ACT, FAKE_ACT, None) == 0
+        sim.append()
+    assert libs.llh_stage_calls() == stages
+    libs.ll_cache_destroy(h)
+
+
 @pytest.mark.parametrize("T,C,S,W,act,kv", [
     (4, 2, 2, 6, ll.LL_BF16, ll.LL_BF16), (4, 1, 0, 3, ll.LL_BF16, ll.LL_BF16),
     (3, 1, 2, 5, ll.LL_BF16, ll.LL_BF16), (4, 2, 2, 8, ll.LL_BF16, ll.LL_I8),
@@ -330,11 +414,14 @@ def test_reencode_runs_are_sink_then_window_oldest_first(libs, T, C, S, W, act, 
     c = cfg(L=2, T=T, C=C, S=S, W=W, H=3, D=64, act=act, kv=kv)
     g = CacheGeometry(T, C, S, W)
     h = create(libs, c)
+    if kv == ll.LL_I8:
+        assert libs.ll_cache_set_int8_dequant(h, ll.LL_I8_IN_KERNEL) == 0
     sim = DequeCacheModel(g)
     ct, D = g.chunk_tokens, 64
     elt = {ll.LL_BF16: 2, ll.LL_I8: 1, ll.LL_F32: 4}[kv]
     k_sink_off, _, _ = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)
     A = FAKE_ACT
+    stage_calls = libs.llh_stage_calls()
     for chunk in range(g.sink_chunks + 2 * g.ring_slots + 2):
         win = resident_window_chunks(chunk, g) if chunk > g.sink_chunks else []
         n_q = len(win) * ct
@@ -350,18 +437,10 @@ def test_reencode_runs_are_sink_then_window_oldest_first(libs, T, C, S, W, act, 
             assert libs.llh_last_attn_chunks(ctypes.byref(n_seg0)) == ct
             chunks_of_run = []
             k0, esz = FAKE_BUF + k_sink_off, elt
-            if kv == ll.LL_I8:   # runs read the bf16 staging copy the call launched first
-                row0 = (ctypes.c_int32 * 40)()
-                slot = (ctypes.c_int32 * 40)()
-                bases = (ctypes.c_int64 * 3)()
-                n_st = libs.llh_last_stage(row0, slot, bases)
-                want_rows = [j * ct for j in range(g.sink_chunks)] + \
-                    [S * T + s_ * ct for s_ in sorted(range(g.ring_slots), key=lambda x: sim.slot_chunk[x])
-                     if sim.slot_chunk[s_] >= 0]
-                assert list(row0[:n_st]) == want_rows
-                assert bases[0] == FAKE_BUF + k_sink_off and bases[1] > bases[0]
-                k0, esz = bases[1], 2
+            # in-kernel mode: an I8 cache is attended in place (int8 runs), no staging launch
+            assert libs.llh_stage_calls() == stage_calls
             for i in range(n_seg):
+                assert runs[RUN_FIELDS * i + 10] == (kv == ll.LL_I8)
                 kp, ln = runs[RUN_FIELDS * i], runs[RUN_FIELDS * i + 5]
                 row = (kp - k0) // (esz * D)
                 if row < S * T:
@@ -551,7 +630,10 @@ def test_layout_queries(libs):
     assert st_k == (rows * 64, 64, 1, 1) and sh_k == (3, 8, 64, 1)
     assert sh_kr == (3, 16, 64, 1) and off_kr == off_k + 8 * 64
     off_v, st_v, sh_v = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_SINK)
-    assert st_v == st_k and sh_v == sh_k                       # int8 V: rows, like K
+    off_vr8, st_vr8, sh_vr8 = _layout(libs, h, 1, ll.LL_WHICH_V, ll.LL_SEG_RING)
+    # int8 V: transposed 64-key tiles like the bf16 cache, 1 sink + 2 ring slots of 1 tile
+    assert st_v == st_vr8 == (3 * 64 * 64, 64 * 64, 64, 1)
+    assert sh_v == (3, 1, 64, 64) and sh_vr8 == (3, 2, 64, 64) and off_vr8 == off_v + 64 * 64
     assert st_s == (rows, 1, 1, 1) and sh_s == (3, 16, 1, 1)
     assert off_k % 256 == 0
     assert status(libs, libs.ll_cache_layout(h, 0, 9, 0, ctypes.byref(ctypes.c_size_t()),

@@ -64,10 +64,11 @@ def _replay_history(wl, layer, chunk):
     return hist
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int8-ink"])
 def test_fullsize_switch_workload_sampled(kv):
-    """bf16 cache, and the int8 cache (the oracle attends over the exactly
-    dequantised stored K/V; the current chunk stays bf16)."""
+    """bf16 cache, and the int8 cache read through the staged bf16 copy and
+    in the attention kernel (the oracle attends over the exactly dequantised
+    stored K/V; the current chunk stays bf16)."""
     wl = bench.Workload("switch", kv)
     last = max(CHUNKS)
     wl.prepare(range(last + 1))

@@ -75,12 +75,15 @@ def _check_v_padding(cache, layer, seg, chunks):
 
 
 def run_stream(cfg_id, T, C, S, W, H, D, dtype, n_chunks, int8=False, check_bytes=True,
-               n_cur_zero_at=()):
+               n_cur_zero_at=(), i8_mode=ll.LL_I8_STAGED):
     """Generate ``n_chunks`` chunks through the ABI and compare every attention
-    output with the oracle; check the cache bytes after every append."""
+    output with the oracle; check the cache bytes after every append.  An int8
+    cache is read as ``i8_mode`` selects (staged bf16 copy or in the kernel)."""
     kv = ll.LL_I8 if int8 else act_code(dtype)
     cfg = ll.make_config(1, H, D, T, C, S, W, act_code(dtype), kv)
     cache = ll.Cache(cfg)
+    if int8:
+        cache.set_int8_dequant(i8_mode)
     g = CacheGeometry(T, C, S, W)
     hist = LayerHistory(g, int8=int8)
     sim = DequeCacheModel(g)
@@ -156,11 +159,17 @@ def test_bf16_max_key_runs():
     run_stream(114, 8, 1, 8, 31, 2, 64, "bf16", 40, check_bytes=False)
 
 
-def test_int8_stream_bitexact_and_parity():
+I8_MODES = pytest.mark.parametrize("i8_mode", [ll.LL_I8_STAGED, ll.LL_I8_IN_KERNEL],
+                                   ids=["staged", "in_kernel"])
+
+
+@I8_MODES
+def test_int8_stream_bitexact_and_parity(i8_mode):
     """INT8 KV: codes and scales bit-exact vs the oracle quantiser; attention
-    vs the oracle on the identically dequantised values."""
-    run_stream(120, 50, 2, 2, 6, 2, 128, "bf16", 6, int8=True)
-    run_stream(121, 33, 1, 1, 3, 3, 64, "bf16", 5, int8=True)
+    vs the oracle on the identically dequantised values, both ways of reading
+    the codes."""
+    run_stream(120, 50, 2, 2, 6, 2, 128, "bf16", 6, int8=True, i8_mode=i8_mode)
+    run_stream(121, 33, 1, 1, 3, 3, 64, "bf16", 5, int8=True, i8_mode=i8_mode)
 
 
 def _config1_inputs(c, tensor):
@@ -381,7 +390,7 @@ def test_cross_attention(dtype, D, n_q, n_txt):
 # re-encoding attention after a KV-recache
 # --------------------------------------------------------------------------
 
-def run_reencode(cfg_id, T, C, S, W, H, D, dtype, n_chunks, check_at, int8=False):
+def run_reencode(cfg_id, T, C, S, W, H, D, dtype, n_chunks, check_at, int8=False, i8_mode=ll.LL_I8_STAGED):
     """Append ``n_chunks`` chunks; after each chunk in ``check_at`` recache the
     resident window with a fresh payload and run the re-encoding attention of
     the window chunks through the ABI, against the oracle on the same history
@@ -389,6 +398,8 @@ def run_reencode(cfg_id, T, C, S, W, H, D, dtype, n_chunks, check_at, int8=False
     kv = ll.LL_I8 if int8 else act_code(dtype)
     cfg = ll.make_config(1, H, D, T, C, S, W, act_code(dtype), kv)
     cache = ll.Cache(cfg)
+    if int8:
+        cache.set_int8_dequant(i8_mode)
     g = CacheGeometry(T, C, S, W)
     hist = LayerHistory(g, int8=int8)
     ct = g.chunk_tokens
@@ -437,8 +448,9 @@ def test_reencode_bf16_two_sink_chunks():
     run_reencode(142, 24, 1, 2, 4, 3, 128, "bf16", 7, (2, 6))
 
 
-def test_reencode_int8_cache():
-    run_reencode(143, 50, 2, 2, 6, 2, 128, "bf16", 5, (1, 4), int8=True)
+@I8_MODES
+def test_reencode_int8_cache(i8_mode):
+    run_reencode(143, 50, 2, 2, 6, 2, 128, "bf16", 5, (1, 4), int8=True, i8_mode=i8_mode)
 
 
 def test_reencode_fp32():
@@ -542,4 +554,7 @@ def test_random_geometry_stream(geom):
     streamed past the first eviction: every attention output against the
     oracle and the cache bytes after every append."""
     cfg_id, T, C, S, W, H, D, kind, n = geom
-    run_stream(cfg_id, T, C, S, W, H, D, "f32" if kind == "f32" else "bf16", n, int8=kind == "int8")
+    # the int8 geometries alternate between the two ways of reading the codes
+    mode = ll.LL_I8_IN_KERNEL if (cfg_id // 3) % 2 else ll.LL_I8_STAGED
+    run_stream(cfg_id, T, C, S, W, H, D, "f32" if kind == "f32" else "bf16", n, int8=kind == "int8",
+               i8_mode=mode)
