@@ -214,6 +214,22 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
                                   float* dq, float* dk_cur, float* dv_cur, ll_stream_t stream);
 
 /*
+ * ll_sink_window_attn_bwd without the delta workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation).  Same arguments, layouts,
+ * numerics and errors otherwise.  delta lives in a static device array of
+ * 2^20 floats that the library holds on each GPU until the process ends:
+ * num_heads * n_q must be at most 1048576 (else LL_ERR_UNSUPPORTED, nothing
+ * enqueued).  Every call on one GPU uses that GPU's array; calls that overlap
+ * on one GPU (other streams or threads) race.  Each call rewrites the part it
+ * reads, so nothing carries over between calls.  Allocates nothing.
+ */
+ll_status ll_sink_window_attn_bwd_noalloc(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                          const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                                          const void* out, const float* lse, const void* dout, float* dq,
+                                          float* dk_cur, float* dv_cur, ll_stream_t stream);
+
+/*
  * Self-attention of the re-encoding pass of a KV-recache (paper §3.1 "KV
  * recache": at a prompt switch the frames already generated are encoded again
  * with the new prompt to rebuild the cache; §3.3: the cache holds the sink and

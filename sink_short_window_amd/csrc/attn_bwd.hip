@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -503,6 +504,36 @@ int launch_bwd_d(const AttnBwdArgs& p, void* stream) {
 }
 
 }  // namespace
+
+// Workspace of the allocation-free backward (ll_sink_window_attn_bwd_noalloc):
+// delta, [H][n_q] fp32, rewritten by every call before it is read.  Each GPU
+// holds its own copy for the life of the process; calls that overlap on one
+// GPU share it and race.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+// The current device's address of `scratch`, looked up once per device (the
+// array's name is a host-side stand-in, not a device address).
+int bwd_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return int(e);
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch[dev];
+  return 0;
+}
 
 int launch_attention_bwd(const AttnBwdArgs& p, void* stream) {
   if (p.a.n_q <= 0) return 0;

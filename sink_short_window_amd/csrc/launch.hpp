@@ -160,6 +160,12 @@ inline LinLayout linear_workspace_layout(int H, int D) {
   return l;
 }
 
+// The allocation-free backward's delta workspace: a file-scope device array
+// of this many floats (4 MiB) per GPU; bwd_scratch returns the current
+// device's address of it (0 on success, else the hipError_t code).
+constexpr int64_t kBwdScratchFloats = int64_t(1) << 20;
+int bwd_scratch(float** ptr);
+
 int launch_attention(const AttnArgs& a, void* stream);
 int launch_linear_attention(const LinArgs& a, void* stream);
 int launch_stage_int8(const StageArgs& a, void* stream);

@@ -152,6 +152,65 @@ void add_current_run(const ll::Geometry& g, const void* k_cur, const void* v_cur
   keys += int32_t(n_cur);
 }
 
+// The backward of one call with its delta workspace (caller-provided or the
+// library's static one); `static_delta` replaces the caller checks of delta
+// by the size bound of the static workspace.
+ll_status attn_bwd_impl(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                        const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                        const void* out, const float* lse, const void* dout, float* delta,
+                        bool static_delta, float* dq, float* dk_cur, float* dv_cur, ll_stream_t stream) {
+  ll_status st = check_layer(cache, layer, false);
+  if (st != LL_OK) return st;
+  const ll::CacheState& cs = cache->state;
+  const ll::Geometry& g = cs.geom();
+  if (g.act != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "the backward supports BF16 activations");
+  if (n_q < 1 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q must be in [1, 2^30)");
+  if (n_cur != 0 && n_cur != g.ctok)
+    return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK ||
+      (st = check_act_ptr(dout, "dout")) != LL_OK || (st = check_act_ptr(dq, "dq")) != LL_OK)
+    return st;
+  if (!lse || !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is NULL or not 4-byte aligned");
+  if (static_delta) {
+    if (int64_t(g.H) * n_q > ll::kBwdScratchFloats)
+      return fail(LL_ERR_UNSUPPORTED, "num_heads * n_q = " + std::to_string(int64_t(g.H) * n_q) +
+                                          " exceeds the static workspace of " +
+                                          std::to_string(ll::kBwdScratchFloats) + " floats");
+  } else if (!delta || !aligned(delta, 4)) {
+    return fail(LL_ERR_INVALID_ARG, "delta is NULL or not 4-byte aligned");
+  }
+  if (n_cur > 0) {
+    if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK ||
+        (st = check_act_ptr(dk_cur, "dk_cur")) != LL_OK || (st = check_act_ptr(dv_cur, "dv_cur")) != LL_OK)
+      return st;
+  }
+  ll::AttnBwdArgs b;
+  int32_t keys = 0;
+  add_cache_runs(cs, layer, b.a, keys, /*staged=*/true);
+  if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, b.a, keys);
+  if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
+  if (static_delta && (st = launched(ll::bwd_scratch(&delta), "static workspace lookup")) != LL_OK) return st;
+  b.a.n_keys = keys;
+  b.a.q = q;
+  b.a.out = nullptr;
+  b.a.lse = nullptr;
+  b.a.n_q = int32_t(n_q);
+  b.a.H = g.H;
+  b.a.D = g.D;
+  b.a.act = g.act;
+  b.a.scale = scale;
+  b.out = out;
+  b.dout = dout;
+  b.lse = lse;
+  b.delta = delta;
+  b.dq = dq;
+  b.dk = n_cur > 0 ? dk_cur : nullptr;
+  b.dv = n_cur > 0 ? dv_cur : nullptr;
+  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
+  return launched(ll::launch_attention_bwd(b, stream), "attention backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,48 +480,17 @@ ll_status ll_sink_window_attn_bwd(const ll_cache* cache, int32_t layer, const vo
                                   const void* out, const float* lse, const void* dout, float* delta,
                                   float* dq, float* dk_cur, float* dv_cur, ll_stream_t stream) {
   ll::clear_error();
-  ll_status st = check_layer(cache, layer, false);
-  if (st != LL_OK) return st;
-  const ll::CacheState& cs = cache->state;
-  const ll::Geometry& g = cs.geom();
-  if (g.act != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "the backward supports BF16 activations");
-  if (n_q < 1 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q must be in [1, 2^30)");
-  if (n_cur != 0 && n_cur != g.ctok)
-    return fail(LL_ERR_INVALID_ARG, "n_cur must be 0 or the chunk's token count " + std::to_string(g.ctok));
-  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if ((st = check_act_ptr(q, "q")) != LL_OK || (st = check_act_ptr(out, "out")) != LL_OK ||
-      (st = check_act_ptr(dout, "dout")) != LL_OK || (st = check_act_ptr(dq, "dq")) != LL_OK)
-    return st;
-  if (!lse || !aligned(lse, 4)) return fail(LL_ERR_INVALID_ARG, "lse is NULL or not 4-byte aligned");
-  if (!delta || !aligned(delta, 4)) return fail(LL_ERR_INVALID_ARG, "delta is NULL or not 4-byte aligned");
-  if (n_cur > 0) {
-    if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK ||
-        (st = check_act_ptr(dk_cur, "dk_cur")) != LL_OK || (st = check_act_ptr(dv_cur, "dv_cur")) != LL_OK)
-      return st;
-  }
-  ll::AttnBwdArgs b;
-  int32_t keys = 0;
-  add_cache_runs(cs, layer, b.a, keys, /*staged=*/true);
-  if (n_cur > 0) add_current_run(g, k_cur, v_cur, n_cur, b.a, keys);
-  if (keys == 0) return fail(LL_ERR_BAD_STATE, "empty key set: nothing cached and n_cur == 0");
-  b.a.n_keys = keys;
-  b.a.q = q;
-  b.a.out = nullptr;
-  b.a.lse = nullptr;
-  b.a.n_q = int32_t(n_q);
-  b.a.H = g.H;
-  b.a.D = g.D;
-  b.a.act = g.act;
-  b.a.scale = scale;
-  b.out = out;
-  b.dout = dout;
-  b.lse = lse;
-  b.delta = delta;
-  b.dq = dq;
-  b.dk = n_cur > 0 ? dk_cur : nullptr;
-  b.dv = n_cur > 0 ? dv_cur : nullptr;
-  if ((st = launched(stage_int8(cs, layer, stream), "int8 staging launch")) != LL_OK) return st;
-  return launched(ll::launch_attention_bwd(b, stream), "attention backward launch");
+  return attn_bwd_impl(cache, layer, q, n_q, k_cur, v_cur, n_cur, scale, out, lse, dout, delta, false, dq,
+                       dk_cur, dv_cur, stream);
+}
+
+ll_status ll_sink_window_attn_bwd_noalloc(const ll_cache* cache, int32_t layer, const void* q, int64_t n_q,
+                                          const void* k_cur, const void* v_cur, int64_t n_cur, float scale,
+                                          const void* out, const float* lse, const void* dout, float* dq,
+                                          float* dk_cur, float* dv_cur, ll_stream_t stream) {
+  ll::clear_error();
+  return attn_bwd_impl(cache, layer, q, n_q, k_cur, v_cur, n_cur, scale, out, lse, dout, nullptr, true, dq,
+                       dk_cur, dv_cur, stream);
 }
 
 ll_status ll_window_reencode_attn(const ll_cache* cache, int32_t layer, const void* q,

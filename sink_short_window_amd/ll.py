@@ -30,7 +30,8 @@ STATUS = {0: "LL_OK", 1: "LL_ERR_INVALID_ARG", 2: "LL_ERR_BAD_STATE", 3: "LL_ERR
 EXPORTS = ("ll_cache_required_bytes", "ll_cache_create", "ll_cache_get_config", "ll_cache_destroy",
            "ll_cache_reset", "ll_cache_set_int8_dequant",
            "ll_cache_append_chunk", "ll_cache_recache", "ll_sink_window_attn",
-           "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_sink_window_linear_attn",
+           "ll_window_reencode_attn", "ll_sink_window_attn_bwd", "ll_sink_window_attn_bwd_noalloc",
+           "ll_sink_window_linear_attn",
            "ll_linear_attn_workspace_bytes", "ll_cross_attn", "ll_cache_query", "ll_cache_layout",
            "ll_status_str", "ll_last_error")
 
@@ -66,6 +67,8 @@ _SIGS = {
     "ll_window_reencode_attn": (_i32, [_vp, _i32, _vp, _i64, _f32, _vp, _vp, _vp]),
     "ll_sink_window_attn_bwd": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp]),
+    "ll_sink_window_attn_bwd_noalloc": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp,
+                                               _vp, _vp, _vp, _vp]),
     "ll_sink_window_linear_attn": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "ll_linear_attn_workspace_bytes": (_i32, [_vp, _P(_sz)]),
     "ll_cross_attn": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
@@ -321,6 +324,28 @@ def ll_sink_window_attn_bwd(handle, layer, q, k_cur, v_cur, scale, out, lse, dou
         _dev_ptr(dout, "dout", "bfloat16"), _dev_ptr(delta, "delta", "float32"),
         _dev_ptr(dq, "dq", "float32"), _dev_ptr(dk_cur, "dk_cur", "float32", n_cur == 0),
         _dev_ptr(dv_cur, "dv_cur", "float32", n_cur == 0), _stream(stream, q)))
+
+
+def ll_sink_window_attn_bwd_noalloc(handle, layer, q, k_cur, v_cur, scale, out, lse, dout, dq,
+                                    dk_cur=None, dv_cur=None, stream=None, lib=None):
+    """ll_sink_window_attn_bwd with the library's static delta workspace
+    (allocates nothing; num_heads * n_q <= 2^20)."""
+    lib = lib or load()
+    g = ll_cache_get_config(handle, lib)
+    _check_attn_shapes(g, q, k_cur, v_cur, out, lse)
+    _shape(dout, "dout", tuple(q.shape))
+    _shape(dq, "dq", tuple(q.shape))
+    if k_cur is not None:
+        _shape(dk_cur, "dk_cur", tuple(k_cur.shape))
+        _shape(dv_cur, "dv_cur", tuple(k_cur.shape))
+    n_cur = 0 if k_cur is None else k_cur.shape[0]
+    _check(lib, lib.ll_sink_window_attn_bwd_noalloc(
+        handle, layer, _dev_ptr(q, "q", "bfloat16"), q.shape[0],
+        _dev_ptr(k_cur, "k_cur", "bfloat16", True), _dev_ptr(v_cur, "v_cur", "bfloat16", True), n_cur,
+        float(scale), _dev_ptr(out, "out", "bfloat16"), _dev_ptr(lse, "lse", "float32"),
+        _dev_ptr(dout, "dout", "bfloat16"), _dev_ptr(dq, "dq", "float32"),
+        _dev_ptr(dk_cur, "dk_cur", "float32", n_cur == 0), _dev_ptr(dv_cur, "dv_cur", "float32", n_cur == 0),
+        _stream(stream, q)))
 
 
 def ll_cross_attn(q, k_txt, v_txt, scale, out, act_dtype, lse=None, stream=None, lib=None):

@@ -769,3 +769,26 @@ def test_geometry_32bit_bounds(libs, kw, ok):
     else:
         assert status(libs, st) == "LL_ERR_UNSUPPORTED"
         assert b"32-bit" in libs.ll_last_error()
+
+
+def test_noalloc_backward_validation_and_launch(libs):
+    """The allocation-free backward takes the library's static delta
+    workspace (the stub's stand-in address), bounds num_heads * n_q by its
+    size and otherwise checks and launches as the backward does."""
+    c = cfg(L=2, T=4, C=2, S=2, W=6, H=3, D=64)
+    h = create(libs, c)
+    ct = 8
+    A, F = FAKE_ACT, FAKE_ACT + (1 << 24)
+    call = lambda n_q, n_cur=ct, dq=F: status(libs, libs.ll_sink_window_attn_bwd_noalloc(
+        h, 1, A, n_q, A, A, n_cur, 0.1, A, F, A, dq, F, F, None))
+    assert call(5) == "LL_OK"
+    ptrs = (ctypes.c_int64 * 7)()
+    assert libs.llh_last_bwd(ptrs) == 1
+    assert ptrs[0] == 0x5C0000000 and ptrs[1] == F
+    assert call((1 << 20) // 3) == "LL_OK"
+    assert call((1 << 20) // 3 + 1) == "LL_ERR_UNSUPPORTED"
+    assert b"static workspace" in libs.ll_last_error()
+    assert call(0) == "LL_ERR_INVALID_ARG"
+    assert call(5, dq=None) == "LL_ERR_INVALID_ARG"
+    assert call(5, n_cur=ct - 1) == "LL_ERR_INVALID_ARG"
+    libs.ll_cache_destroy(h)
