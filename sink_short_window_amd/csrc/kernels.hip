@@ -1393,6 +1393,18 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
   }
 }
 
+// q = clamp(rne(fl32(x / s)), -127, 127) for s > 0, bit-identical to the IEEE
+// division: r = x * fl32(1/s) is within 127.5 * 3 * 2^-24 < 2.3e-5 of
+// fl32(x / s) (|x / s| <= 127.5), so both round to the same integer unless r
+// lies within that distance of a half-integer; there (rarely) the division
+// itself decides.
+__device__ __forceinline__ int quant_code(float x, float s, float inv) {
+  const float r = x * inv;
+  const float f = r - floorf(r);
+  const float q = fabsf(f - 0.5f) > 1e-4f ? rintf(r) : rintf(x / s);
+  return int(fminf(fmaxf(q, -127.f), 127.f));
+}
+
 // INT8 writer, one workgroup per (head, 64-token tile, chunk, K or V): each
 // token's D values of the head are quantised with s = max|x| / 127 (IEEE fp32
 // division) and q = clamp(rne(x / s), -127, 127) (s = 0, q = 0 for an
@@ -1404,9 +1416,10 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
 // [H][rows] fp32 arrays at the token's row.
 template <int D>
 __global__ __launch_bounds__(256) void quant_tile_kernel(CopyArgs a) {
-  constexpr int kG = D / 8;            // lanes per token
+  constexpr int kG = D / 8;             // lanes per token
   constexpr int kPer = kBN * kG / 256;  // tokens' groups per thread
-  __shared__ __attribute__((aligned(16))) uint8_t c8[kBN][D + 16];
+  constexpr int kRowW = D / 4 + 1;      // staged code row in words (odd: conflict-free column reads)
+  __shared__ uint32_t c8[kBN * kRowW];
   const int h = blockIdx.x / a.tps;
   const int tile = blockIdx.x % a.tps;
   const int chunk = blockIdx.y >> 1;
@@ -1445,38 +1458,43 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(CopyArgs a) {
     for (int m = 1; m < kG; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     const float sc = amax / 127.0f;
     uint32_t packed[2] = {0, 0};
+    if (sc != 0.f) {
+      const float inv = 1.0f / sc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int qv = 0;
-      if (sc != 0.f) qv = int(fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f));
-      packed[e >> 2] |= uint32_t(qv & 0xff) << (8 * (e & 3));
+      for (int e = 0; e < 8; ++e) packed[e >> 2] |= uint32_t(quant_code(x[e], sc, inv) & 0xff) << (8 * (e & 3));
     }
     if (key < valid) {
       if (g == 0) scales[row_base + key] = sc;
       if (!isv) *reinterpret_cast<uint2*>(layer + a.k_off + (row_base + key) * D + g * 8) = make_uint2(packed[0], packed[1]);
     }
-    if (isv) *reinterpret_cast<uint2*>(&c8[key][g * 8]) = make_uint2(packed[0], packed[1]);  // zeros past the chunk
+    if (isv) {  // zeros past the chunk
+      c8[key * kRowW + 2 * g] = packed[0];
+      c8[key * kRowW + 2 * g + 1] = packed[1];
+    }
   }
   if (!isv) return;
   __syncthreads();
-  // [D][64] tile: thread (d, 16 columns) gathers its 16 keys' codes
+  // [D][64] tile: thread (4 dims, 8 columns) reads one word (4 dims) of each
+  // of its 8 keys and transposes the 8 x 4 bytes into 4 rows of 8 columns.
   char* dst = layer + a.v_off + int64_t(h) * a.vt_head_elems + (int64_t(a.dst_slot[chunk]) * a.tps + tile) * (kBN * D);
+  if (tid < D / 4 * 8) {
+    const int d4 = tid / 8, p0 = (tid % 8) * 8;
+    uint32_t in[8];
 #pragma unroll
-  for (int it = tid; it < D * (kBN / 16); it += 256) {
-    const int d = it / (kBN / 16), p0 = (it % (kBN / 16)) * 16;
-    uint32_t o[4];
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int p = p0 + 4 * j4 + b;
-        const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-        v |= uint32_t(c8[key][d]) << (8 * b);
-      }
-      o[j4] = v;
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j;
+      const int key = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+      in[j] = c8[key * kRowW + d4];
     }
-    *reinterpret_cast<uint4*>(dst + d * kBN + p0) = make_uint4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // byte i of in[0..3] -> word lo, of in[4..7] -> word hi
+      const uint32_t s01 = __builtin_amdgcn_perm(in[1], in[0], 0x0c0c0400u + 0x0101u * i);
+      const uint32_t s23 = __builtin_amdgcn_perm(in[3], in[2], 0x04000c0cu + 0x01010000u * i);
+      const uint32_t s45 = __builtin_amdgcn_perm(in[5], in[4], 0x0c0c0400u + 0x0101u * i);
+      const uint32_t s67 = __builtin_amdgcn_perm(in[7], in[6], 0x04000c0cu + 0x01010000u * i);
+      *reinterpret_cast<uint2*>(dst + (4 * d4 + i) * kBN + p0) = make_uint2(s01 | s23, s45 | s67);
+    }
   }
 }
 

@@ -20,7 +20,8 @@ import pytest
 import torch
 
 import bench
-from oracle import CacheGeometry, LayerHistory, sink_window_attention, cross_attention
+from oracle import (CacheGeometry, LayerHistory, sink_window_attention, cross_attention, frame_mask,
+                    masked_attention)
 from sink_short_window_amd import synth
 from gpu_util import need_gpu, say, check_out
 
@@ -50,7 +51,7 @@ def _replay_history(wl, layer, chunk):
     """The layer's history as the oracle defines it, through chunk-1, with the
     recache of chunk ``chunk`` (if it is a switch) applied."""
     g = CacheGeometry(bench.T, bench.C, bench.S, bench.W)
-    hist = LayerHistory(g, int8=wl.kv == "int8")
+    hist = LayerHistory(g, int8=wl.kv.startswith("int8"))
     for c in range(chunk + 1):
         if bench.is_switch(c):
             i = bench.recache_index(bench.switches_before(c), layer)
@@ -96,6 +97,14 @@ def test_fullsize_switch_workload_sampled(kv):
                                         frames_per_chunk=bench.C, sink_frames=bench.S,
                                         window_frames=bench.W, scale=scale)
         check_out(got[c][(p, layer, "attn")][rows], want, "bf16", f"chunk {c} pass {p} layer {layer}")
+        if c == max(CHUNKS):
+            # every query row at the last chunk (after all six switches): the
+            # oracle attends the keys its frame mask allows in the full history
+            mask = frame_mask(hk.shape[0], c, tokens_per_frame=bench.T, frames_per_chunk=bench.C,
+                              sink_frames=bench.S, window_frames=bench.W)
+            say(f"[fullsize {kv}] all rows at chunk {c}: {int(mask.sum())} allowed keys")
+            want_all, _ = masked_attention(q, hk[mask], hv[mask], None, scale)
+            check_out(got[c][(p, layer, "attn")], want_all, "bf16", f"chunk {c} all rows")
         j = bench.txt_index(bench.switches_before(c), layer)
         kt = _pool(wl, (bench.N_TXT, bench.H, bench.D), j, synth.K_TXT)
         vt = _pool(wl, (bench.N_TXT, bench.H, bench.D), j, synth.V_TXT)
