@@ -1342,15 +1342,17 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(CopyArgs a) {
   }
 }
 
-// bf16 staging of an I8 layer (for the backward and the linear-attention
-// variant), one workgroup per (head, 64-key tile, listed chunk): every code
-// becomes bf16(q * s) with its key's fp32 scale.  K rows are written in place
-// of the same rows of the staging K; the V tile ([D][64], column p holding
-// key p with bits 2 and 3 swapped) goes to the same tile of the staging V,
-// zeros past the chunk.
+// bf16 staging of an I8 layer (the attention's default INT8 mode, the backward
+// and the linear-attention variant), one workgroup per (head, 64-key tile,
+// listed chunk): every code becomes bf16(q * s) with its key's fp32 scale.  K
+// rows are written in place of the same rows of the staging K; the V tile
+// ([D][64], column p holding key p with bits 2 and 3 swapped) goes to the same
+// tile of the staging V, zeros past the chunk.
 template <int D>
 __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
-  constexpr int kG = D / 8;  // 8-code groups per row
+  constexpr int kG = D / 8;                   // 8-code groups per row
+  constexpr int kKPer = kBN * kG / 256;       // K groups per thread
+  constexpr int kVPer = D * (kBN / 8) / 256;  // V^T groups (8 columns of one dim) per thread
   const int h = blockIdx.x / a.tps;
   const int tile = blockIdx.x % a.tps;
   const int chunk = blockIdx.y;
@@ -1360,31 +1362,48 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
   const char* kq = a.layer + a.k_off;
   const float* ks = reinterpret_cast<const float*>(a.layer + a.ks_off);
   const float* vs = reinterpret_cast<const float*>(a.layer + a.vs_off);
-  __bf16* dk = reinterpret_cast<__bf16*>(a.dst_k);
-#pragma unroll
-  for (int it = tid; it < kBN * kG; it += 256) {
-    const int key = it / kG, g = it % kG;
-    if (key < valid) {
-      const int64_t r = row_base + key;
-      const uint2 kc = *reinterpret_cast<const uint2*>(kq + r * D + g * 8);
-      *reinterpret_cast<u32x4*>(dk + r * D + g * 8) = int8x8_dequant_bf16x8(u32x2{kc.x, kc.y}, ks[r]);
-    }
-  }
-  // the tile's V scales in column order (zero past the chunk: padding codes are 0)
-  __shared__ float vsc[kBN];
-  if (tid < kBN) {
-    const int key = (tid & ~12) | ((tid & 4) << 1) | ((tid & 8) >> 1);
-    vsc[tid] = key < valid ? vs[row_base + key] : 0.f;
-  }
-  __syncthreads();
   const int64_t vt_off = int64_t(h) * a.vt_head_elems + (int64_t(a.slot[chunk]) * a.tps + tile) * (kBN * D);
   const char* vq = a.layer + a.v_off + vt_off;
+  // All loads first (keys past the chunk read the last valid key, in bounds,
+  // and are dropped), so their latencies overlap.  Column p of the V tile
+  // holds key p with bits 2 and 3 swapped; its scale goes to LDS in column
+  // order, zero past the chunk (the padding codes are 0 too).
+  const int pcol = tid & (kBN - 1);
+  const int pkey = (pcol & ~12) | ((pcol & 4) << 1) | ((pcol & 8) >> 1);
+  const float vsl = vs[row_base + min(pkey, valid - 1)];
+  uint2 kc[kKPer];
+  float ksl[kKPer];
+#pragma unroll
+  for (int i = 0; i < kKPer; ++i) {
+    const int it = tid + 256 * i;
+    const int64_t r = row_base + min(it / kG, valid - 1);
+    kc[i] = *reinterpret_cast<const uint2*>(kq + r * D + (it % kG) * 8);
+    ksl[i] = ks[r];
+  }
+  uint2 vc[kVPer];
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const int it = tid + 256 * i;
+    vc[i] = *reinterpret_cast<const uint2*>(vq + (it / (kBN / 8)) * kBN + (it % (kBN / 8)) * 8);
+  }
+  __shared__ float vsc[kBN];
+  if (tid < kBN) vsc[tid] = pkey < valid ? vsl : 0.f;
+  __bf16* dk = reinterpret_cast<__bf16*>(a.dst_k);
+#pragma unroll
+  for (int i = 0; i < kKPer; ++i) {
+    const int it = tid + 256 * i;
+    const int key = it / kG;
+    if (key < valid)
+      *reinterpret_cast<u32x4*>(dk + (row_base + key) * D + (it % kG) * 8) =
+          int8x8_dequant_bf16x8(u32x2{kc[i].x, kc[i].y}, ksl[i]);
+  }
+  __syncthreads();
   __bf16* dv = reinterpret_cast<__bf16*>(a.dst_v) + vt_off;
 #pragma unroll
-  for (int it = tid; it < D * (kBN / 8); it += 256) {
+  for (int i = 0; i < kVPer; ++i) {
+    const int it = tid + 256 * i;
     const int d = it / (kBN / 8), p0 = (it % (kBN / 8)) * 8;
-    const uint2 vc = *reinterpret_cast<const uint2*>(vq + d * kBN + p0);
-    const uint32_t wv[2] = {vc.x, vc.y};
+    const uint32_t wv[2] = {vc[i].x, vc[i].y};
     bf16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -1393,16 +1412,57 @@ __global__ __launch_bounds__(256) void stage_int8_kernel(StageArgs a) {
   }
 }
 
-// q = clamp(rne(fl32(x / s)), -127, 127) for s > 0, bit-identical to the IEEE
-// division: r = x * fl32(1/s) is within 127.5 * 3 * 2^-24 < 2.3e-5 of
-// fl32(x / s) (|x / s| <= 127.5), so both round to the same integer unless r
-// lies within that distance of a half-integer; there (rarely) the division
-// itself decides.
-__device__ __forceinline__ int quant_code(float x, float s, float inv) {
-  const float r = x * inv;
-  const float f = r - floorf(r);
-  const float q = fabsf(f - 0.5f) > 1e-4f ? rintf(r) : rintf(x / s);
-  return int(fminf(fmaxf(q, -127.f), 127.f));
+// Max over aligned groups of G = 8 or 16 lanes (one DPP row or half-row), in
+// every lane of the group: quad swaps (xor 1, xor 2), then the half-row mirror
+// (lane i <-> 7 - i) and, for 16, the row mirror (i <-> 15 - i).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                                 0xf, 0xf, false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  if constexpr (G == 16) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+  return v;
+}
+
+// The 8 codes of one lane, q = clamp(rne(fl32(x / s)), -127, 127), bit-identical
+// to the IEEE division.  For s > 0, r = x * rcp(s) (rcp within 1 ulp) lies
+// within 127.5 * 1.5 * 2^-23 + 2^-18 < 3e-5 of fl32(x / s) (|x / s| <= 127.5),
+// so rne(r) is the code unless r is within that distance of a half-integer,
+// i.e. |r - rne(r)| > 0.5 - 1e-4 (or r is not finite, from a subnormal s).
+// Such codes are rare (about 2e-4 of them); if any lane of the wave has one,
+// the flagged codes take the division itself, so the common path costs a
+// multiply, a rounding and a compare per code.  s == 0 (an all-zero vector)
+// gives r = 0, q = 0.
+__device__ __forceinline__ u32x2 quant_codes8(const float (&x)[8], float s) {
+  constexpr float kNearHalf = 0.5f - 1e-4f;
+  const float inv = s != 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
+  float q[8];
+  uint64_t tie = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float r = x[e] * inv;
+    q[e] = rintf(r);
+    tie |= __builtin_amdgcn_ballot_w64(!(fabsf(r - q[e]) < kNearHalf));
+  }
+  if (tie != 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = x[e] * inv;
+      if (!(fabsf(r - q[e]) < kNearHalf)) q[e] = rintf(x[e] / s);
+    }
+  }
+  u32x2 packed = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = int(fminf(fmaxf(q[e], -127.f), 127.f));
+    packed[e >> 2] |= uint32_t(c & 0xff) << (8 * (e & 3));
+  }
+  return packed;
 }
 
 // INT8 writer, one workgroup per (head, 64-token tile, chunk, K or V): each
@@ -1432,14 +1492,20 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(CopyArgs a) {
   float* scales = reinterpret_cast<float*>(layer + (isv ? a.vs_off : a.ks_off));
   const int64_t row_base = int64_t(h) * a.rows + a.dst_row0[chunk] + tile * kBN;  // head-major row
   const int valid = min(kBN, a.ctok - tile * kBN);
+  // Every load is issued before any is used: keys past the chunk read the
+  // last valid key (in bounds) and are zeroed afterwards, so no load sits in
+  // a branch of its own with a wait behind it.
   uint4 w[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int it = tid + 256 * i;
     const int key = it / kG, g = it % kG;
-    w[i] = key < valid ? *reinterpret_cast<const uint4*>(src + int64_t(tile * kBN + key) * a.H * D + g * 8)
-                       : make_uint4(0, 0, 0, 0);
+    w[i] = *reinterpret_cast<const uint4*>(src + int64_t(tile * kBN + min(key, valid - 1)) * a.H * D + g * 8);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of any use
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if ((tid + 256 * i) / kG >= valid) w[i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int it = tid + 256 * i;
@@ -1454,15 +1520,9 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(CopyArgs a) {
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-    for (int m = 1; m < kG; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    amax = group_max<kG>(amax);
     const float sc = amax / 127.0f;
-    uint32_t packed[2] = {0, 0};
-    if (sc != 0.f) {
-      const float inv = 1.0f / sc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) packed[e >> 2] |= uint32_t(quant_code(x[e], sc, inv) & 0xff) << (8 * (e & 3));
-    }
+    const u32x2 packed = quant_codes8(x, sc);
     if (key < valid) {
       if (g == 0) scales[row_base + key] = sc;
       if (!isv) *reinterpret_cast<uint2*>(layer + a.k_off + (row_base + key) * D + g * 8) = make_uint2(packed[0], packed[1]);
