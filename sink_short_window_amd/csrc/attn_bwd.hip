@@ -408,23 +408,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
 
   for (int q0 = 0; q0 < a.n_q; q0 += kTile) {
     __syncthreads();
+    {
+      // every load of the tile in flight at once: rows past n_q read the
+      // last query (in bounds) and are zeroed after the loads
+      constexpr int NL = kTile * NV / kBwdThreads;
+      u32x4 wq[NL], wg[NL];
 #pragma unroll
-    for (int it = tid; it < kTile * NV; it += kBwdThreads) {
-      const int row = it / NV, vec = it % NV;
-      const int qi = q0 + row;
-      u32x4 wq = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
-      if (qi < a.n_q) {
-        const int64_t e = (int64_t(qi) * a.H + head) * D + vec * 8;
-        wq = *reinterpret_cast<const u32x4*>(q + e);
-        wg = *reinterpret_cast<const u32x4*>(g + e);
+      for (int i = 0; i < NL; ++i) {
+        const int it = tid + i * kBwdThreads;
+        const int qi = min(q0 + it / NV, a.n_q - 1);
+        const int64_t e = (int64_t(qi) * a.H + head) * D + (it % NV) * 8;
+        wq[i] = *reinterpret_cast<const u32x4*>(q + e);
+        wg[i] = *reinterpret_cast<const u32x4*>(g + e);
       }
-      *reinterpret_cast<bf16x8*>(qs + QT::off(row, vec)) = scale_bf16x8(wq, c);
-      *reinterpret_cast<u32x4*>(gs + QT::off(row, vec)) = wg;
-    }
-    if (tid < kTile) {
-      const int qi = q0 + tid;
-      lse2s[tid] = qi < a.n_q ? p.lse[int64_t(head) * a.n_q + qi] * kLog2e : INFINITY;
-      dls[tid] = qi < a.n_q ? p.delta[int64_t(head) * a.n_q + qi] : 0.f;
+      const int ql = min(q0 + (tid & (kTile - 1)), a.n_q - 1);
+      const float lsel = p.lse[int64_t(head) * a.n_q + ql];
+      const float dll = p.delta[int64_t(head) * a.n_q + ql];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int it = tid + i * kBwdThreads;
+        const int row = it / NV, vec = it % NV;
+        const bool ok = q0 + row < a.n_q;
+        const u32x4 z = {0, 0, 0, 0};
+        *reinterpret_cast<bf16x8*>(qs + QT::off(row, vec)) = scale_bf16x8(ok ? wq[i] : z, c);
+        *reinterpret_cast<u32x4*>(gs + QT::off(row, vec)) = ok ? wg[i] : z;
+      }
+      if (tid < kTile) {
+        const bool ok = q0 + tid < a.n_q;
+        lse2s[tid] = ok ? lsel * kLog2e : INFINITY;
+        dls[tid] = ok ? dll : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll
