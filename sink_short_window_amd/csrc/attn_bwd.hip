@@ -187,6 +187,23 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
   }
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2: XCD x gets a contiguous, head-major range of (head,
+// tile) units, so the workgroups that share a head's K/V (dQ) or Q/dO (dK/dV)
+// run on the same XCD.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_unit(int& head, int& tile) {
+  const int nt = gridDim.x;
+  const int total = nt * gridDim.y;
+  const int lin = blockIdx.y * nt + blockIdx.x;
+  const int xcd = lin % kXcds;
+  const int slot = lin / kXcds;
+  const int per = total / kXcds, extra = total % kXcds;
+  const int unit = xcd * per + min(xcd, extra) + slot;
+  head = unit / nt;
+  tile = unit % nt;
+}
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
@@ -199,10 +216,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
   __shared__ __attribute__((aligned(16))) char ks2[2][KT::kBytes];
   __shared__ __attribute__((aligned(16))) char vs2[2][VT::kBytes];  // [d][column], column p = key vt_key(p)
   const AttnArgs& a = p.a;
-  const int head = blockIdx.y;
+  int head, qtile;
+  xcd_unit(head, qtile);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int qi = blockIdx.x * kBwdBQ + wave * 32 + r32;
+  const int qi = qtile * kBwdBQ + wave * 32 + r32;
   const bool q_ok = qi < a.n_q;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
@@ -377,10 +395,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   __shared__ __attribute__((aligned(16))) float dls[kTile];
   const AttnArgs& a = p.a;
   const KvSeg& cur = a.seg[a.n_seg - 1];
-  const int head = blockIdx.y;
+  int head, ktile;
+  xcd_unit(head, ktile);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int key = blockIdx.x * kBwdBK + wave * 32 + r32;
+  const int key = ktile * kBwdBK + wave * 32 + r32;
   const bool k_ok = key < cur.len;
   const float c = a.scale * kLog2e;
 
