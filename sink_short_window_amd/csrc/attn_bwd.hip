@@ -349,13 +349,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
       }
+      if (valid < kTile) {  // keys past the run's end: P = 0
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) s[e] = -INFINITY;
+      }
       float ds[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const float pr = key < valid ? __builtin_amdgcn_exp2f(s[e] - lse2) : 0.f;
-        ds[e] = pr * (dp[e] - dl);
-      }
+      for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(s[e] - lse2) * (dp[e] - dl);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 b = pack8(ds, s2);
