@@ -104,8 +104,9 @@ typedef struct {
 } ll_cache_config;
 
 /* Device bytes the cache needs for `cfg` (all layers), written to *bytes.  An
- * I8 cache also holds one layer's bf16 staging area, which every attention
- * call on the cache rewrites from the layer's codes before reading it. */
+ * I8 cache also holds one layer's bf16 staging area, which the staged
+ * attention mode, the backward and the linear-attention variant rewrite from
+ * the layer's codes before reading it. */
 ll_status ll_cache_required_bytes(const ll_cache_config* cfg, size_t* bytes);
 
 /*
@@ -125,8 +126,7 @@ ll_status ll_cache_destroy(ll_cache* cache);
 
 /*
  * How ll_sink_window_attn and ll_window_reencode_attn read an I8 cache
- * (INT8 KV variant; the workload definition asks for dequantisation inside
- * the attention).  Host state only; enqueues nothing.
+ * (INT8 KV variant).  Host state only; enqueues nothing.
  *   LL_I8_IN_KERNEL: the attention kernel reads the int8 codes and their
  *     scales and attends over the exact values q * s: codes are converted
  *     exactly to bf16 tiles on chip, the K scale multiplies each score in
@@ -134,7 +134,8 @@ ll_status ll_cache_destroy(ll_cache* cache);
  *   LL_I8_STAGED (default): one extra launch per call first writes a bf16
  *     copy, bf16(q * s), of the layer's resident codes into the cache's
  *     staging area, and the bf16 attention kernel reads that copy (faster on
- *     MI355X, about 2.7x the HBM bytes, one more bf16 rounding of q * s).
+ *     MI355X; about 3.4x the call's algorithmic HBM bytes against 1.6x in the
+ *     kernel, and one more bf16 rounding of q * s).
  * LL_ERR_INVALID_ARG for a mode outside the enum or a cache whose kv_dtype is
  * not I8.  The backward and the linear-attention variant always read the
  * staged copy.
