@@ -31,9 +31,11 @@
 //                            read (ds_read_b64_tr_b16).
 // The two halves of the workgroup alternate between an MFMA phase and a
 // softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
-// direct-to-LDS buffer loads.  An int8 cache is read through a bf16 staging
-// copy in the bf16 cache's layout (stage_int8_kernel, one launch per call:
-// every code becomes bf16(q * s) once, not once per query tile).
+// direct-to-LDS buffer loads.  An int8 cache is read either through a bf16
+// staging copy in the bf16 cache's layout (stage_int8_kernel, one launch per
+// call: every code becomes bf16(q * s) once, not once per query tile), or by
+// attn_i8_kernel, which converts the codes to bf16 on chip and applies the
+// scales to the scores and to P (details above it).
 // fp32 activations use a plainer kernel with the fp32 MFMA 32x32x2.
 
 #include <hip/hip_runtime.h>
