@@ -101,10 +101,11 @@ int add_cache_runs(const ll::CacheState& cs, int32_t layer, ll::AttnArgs& a, int
   return n_sink;
 }
 
-// The backward and the linear-attention variant read an I8 cache through a
-// bf16 copy of the layer's resident chunks (sink chunks and resident ring
-// slots) in the staging area, dequantised to bf16(q * s) by one launch per
-// call.  No-op for other caches.
+// The staged attention mode (the default), the backward and the
+// linear-attention variant read an I8 cache through a bf16 copy of the
+// layer's resident chunks (sink chunks and resident ring slots) in the
+// staging area, dequantised to bf16(q * s) by one launch per call.  No-op for
+// other caches.
 int stage_int8(const ll::CacheState& cs, int32_t layer, void* stream) {
   const ll::Geometry& g = cs.geom();
   if (!g.staged) return 0;
