@@ -92,19 +92,20 @@ __device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1)
 // (per 32 lanes: 4 consecutive rows x 4 granules).  For D = 128 rows are 256
 // bytes and granule g of row r is stored at g ^ f(r), f(r) = ((r & 3) << 2) |
 // ((r >> 2) & 3), a rotation of r mod 16: both patterns then cover 16
-// distinct granules, i.e. all 64 banks.  Otherwise (D = 64, or a kernel
-// whose registers cannot spare the per-read address arithmetic) rows are
-// padded by 32 bytes, to a stride of 8 (mod 64) dwords, which keeps the
-// transpose reads conflict-free within 16 lanes.
+// distinct granules, i.e. all 64 banks.  Otherwise (D = 64, or the dK/dV
+// kernel, whose registers cannot spare the XOR's per-read address arithmetic)
+// rows are padded by 64 bytes and skewed: granule g of row r is stored at
+// granule g + ((r >> 2) & 3).  16 rows at one granule, and the 4 rows x 4
+// granules of a 32-lane transpose read, then fall in distinct bank groups.
 template <int D, bool kSwzOn = true>
 struct RowTile {
   static constexpr bool kSwz = kSwzOn && D == 128;
-  static constexpr int RB = kSwz ? D * 2 : (D + 16) * 2;
+  static constexpr int RB = kSwz ? D * 2 : (D + 32) * 2;
   static constexpr int kBytes = kTile * RB;
   static __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
   static __device__ __forceinline__ int off(int row, int gran) {
     if constexpr (kSwz) return row * RB + ((gran ^ swz(row)) << 4);
-    else return row * RB + gran * 16;
+    else return row * RB + ((gran + ((row >> 2) & 3)) << 4);
   }
 };
 
@@ -136,7 +137,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
       const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
       const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
       if constexpr (T::kSwz) off[aa][db] = T::off(row, col >> 3) + (col & 7) * 2;
-      else off[aa][db] = row * T::RB + col * 2;  // (this form keeps the compiler from spilling)
+      else off[aa][db] = row * T::RB + (((col >> 3) + ((row >> 2) & 3)) << 4) + (col & 7) * 2;
     }
 }
 
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
-  using QT = RowTile<D, false>;  // padded: the swizzle's address arithmetic spills here
+  using QT = RowTile<D, false>;  // padded and skewed: the XOR swizzle's address arithmetic spills here
   constexpr int NV = D / 8;
   __shared__ __attribute__((aligned(16))) char qs[QT::kBytes];   // Q' rows
   __shared__ __attribute__((aligned(16))) char gs[QT::kBytes];   // dO rows
