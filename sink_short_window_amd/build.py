@@ -8,7 +8,7 @@
   UndefinedBehaviorSanitizer (host code only; loaded with the ASan runtime
   preloaded, see tests/test_host_sanitizers.py).
 
-Run ``python -m sink_short_window_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python -m sink_short_window_amd.build``.
 """
 
 import os
