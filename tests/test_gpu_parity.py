@@ -530,7 +530,7 @@ def test_window_sweep_shapes_sampled(S, W):
 # random small geometries (fixed draw)
 # --------------------------------------------------------------------------
 
-def _random_geometries(n=12, seed=2026):
+def _random_geometries(n=24, seed=2026):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
