@@ -67,3 +67,47 @@ def test_graph_replay_matches_eager(kv):
         del graph
     finally:
         cache.close()
+
+
+def test_graph_replay_of_the_allocation_free_backward():
+    """The training step's forward and its allocation-free backward (whose
+    delta workspace is the library's static device array) captured in one
+    graph: three replays equal the eager calls bit for bit.  The first eager
+    call looks up the array's address; inside the capture only kernels are
+    launched."""
+    T, C, S, W, H, D = 100, 1, 1, 3, 4, 128
+    cfg = ll.make_config(1, H, D, T, C, S, W, ll.LL_BF16, ll.LL_BF16)
+    cache = ll.Cache(cfg, "cuda")
+    try:
+        g = lambda c, t: dev(synth.normal((T, H, D), "bf16", 171, 0, c, 0, t), "bf16")
+        for c in range(3):
+            cache.append_chunk(0, g(c, K), g(c, V))
+        q, kc, vc, dout = g(3, Q), g(3, K), g(3, V), g(4, Q)
+        scale = 1.0 / math.sqrt(D)
+        out = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        dq, dk, dv = (torch.empty((T, H, D), dtype=torch.float32, device="cuda") for _ in range(3))
+
+        def step():
+            cache.attn(0, q, kc, vc, scale, out, lse)
+            ll.ll_sink_window_attn_bwd_noalloc(cache.handle, 0, q, kc, vc, scale, out, lse, dout, dq, dk, dv)
+
+        step()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (out, lse, dq, dk, dv)]
+        say("[graph bwd] capture")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for rep in range(3):
+            for t in (out, lse, dq, dk, dv):
+                t.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for name, got, ref in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk, dv), want):
+                assert torch.equal(got, ref), f"replay {rep}: {name} differs from the eager call"
+        say("[graph bwd] 3 replays equal the eager calls")
+        del graph
+    finally:
+        cache.close()
