@@ -29,8 +29,8 @@
 // are written in fp32 (token-major [n][H][D]).
 //
 // Tiles reach LDS through registers, in layouts (RowTile, VtTile) whose XOR
-// swizzles keep both the 16-byte row reads and the transpose reads free of
-// bank conflicts.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
+// swizzles or skewed padding keep both the 16-byte row reads and the
+// transpose reads free of bank conflicts.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
 // as the bf16 cache stores it; the caller's row-major current chunk is
 // transposed while staged) and its rows are read back with transpose reads.
 
