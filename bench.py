@@ -798,6 +798,11 @@ def main():
     if args.kv == "bf16" and not args.no_int8_subrun:
         extra["int8_cache"] = int8_subrun(args.warmup, args.steps, args.passes, "int8")
         extra["int8_cache_in_kernel"] = int8_subrun(args.warmup, args.steps, args.passes, "int8-ink")
+        # The staged call is the staging launch plus the bf16 kernel, inside one C
+        # call; its extra time over this line's bf16 call estimates the staging.
+        st = extra["int8_cache"].get("attention_ms_per_call")
+        if st and extra.get("attention_ms_per_call"):
+            extra["int8_cache"]["staging_ms_vs_bf16_call"] = st - extra["attention_ms_per_call"]
 
     roofline = None
     if tflops:
