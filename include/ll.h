@@ -162,8 +162,10 @@ ll_status ll_cache_append_chunk(ll_cache* cache, int32_t layer, const void* k, c
  * oldest to newest, from k, v: [n_tokens][H][D] of act_dtype, where n_tokens
  * must equal (resident ring chunks) * C_tok.  layer == -1 rewrites all layers
  * in one launch from k, v: [num_layers][n_tokens][H][D]; every layer must then
- * hold the same number of resident ring chunks.  The sink is never rewritten.
- * LL_ERR_BAD_STATE if no window chunk is resident.
+ * hold the same resident ring slots in the same oldest-to-newest order (as
+ * layers that have appended equally many chunks do).  The sink is never
+ * rewritten.  LL_ERR_BAD_STATE if no window chunk is resident or the layers'
+ * rings differ.
  */
 ll_status ll_cache_recache(ll_cache* cache, int32_t layer, const void* k, const void* v,
                            int64_t n_tokens, ll_stream_t stream);

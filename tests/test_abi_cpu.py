@@ -792,3 +792,97 @@ def test_noalloc_backward_validation_and_launch(libs):
     assert call(5, dq=None) == "LL_ERR_INVALID_ARG"
     assert call(5, n_cur=ct - 1) == "LL_ERR_INVALID_ARG"
     libs.ll_cache_destroy(h)
+
+
+# --------------------------------------------------------------------------
+# random operation sequences against the oracle's cache model
+# --------------------------------------------------------------------------
+
+from hypothesis import HealthCheck, given, settings, strategies as hst  # noqa: E402
+
+# appends dominate, so that sequences run well past the first evictions
+_OPS = hst.lists(hst.tuples(hst.sampled_from(["append"] * 8 + ["recache", "recache_all", "attn",
+                                                               "attn_cache_only", "reset"]),
+                            hst.integers(0, 1)), min_size=1, max_size=60)
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(T=hst.integers(1, 9), C=hst.integers(1, 3), nsc=hst.integers(0, 3), R=hst.integers(0, 4), ops=_OPS)
+def test_state_machine_matches_the_cache_model_under_random_operations(libs, T, C, nsc, R, ops):
+    """Any interleaving of appends (two layers, out of step), recaches of one
+    or all layers (all layers only when their rings hold the same slots in
+    the same order), attention calls with and without the current chunk and
+    resets: after every operation ll_cache_query equals the oracle's FIFO
+    model, a recache rewrites exactly the resident window chunks oldest
+    first, and an attention call's run table covers exactly the chunks the
+    frame rule allows, each once, ending with the current chunk."""
+    S, W = nsc * C, (R + 1) * C
+    L, H, D = 2, 2, 64
+    g = CacheGeometry(T, C, S, W)
+    h = create(libs, cfg(L=L, T=T, C=C, S=S, W=W, H=H, D=D))
+    ct = g.chunk_tokens
+    sims = [DequeCacheModel(g) for _ in range(L)]
+    k_sink_off = _layout(libs, h, 0, ll.LL_WHICH_K, ll.LL_SEG_SINK)[0]
+    layer_bytes = _layout(libs, h, 1, ll.LL_WHICH_K, ll.LL_SEG_SINK)[0] - k_sink_off
+    try:
+        for op, layer in ops:
+            n = sims[layer].appended
+            if op == "append":
+                assert libs.ll_cache_append_chunk(h, layer, FAKE_ACT, FAKE_ACT, None) == 0
+                sims[layer].append()
+            elif op == "reset":
+                assert libs.ll_cache_reset(h) == 0
+                sims = [DequeCacheModel(g) for _ in range(L)]
+            elif op in ("recache", "recache_all"):
+                target = -1 if op == "recache_all" else layer
+                chunks = resident_window_chunks(n, g)
+
+                def slots(sim):
+                    return [sim.slot_chunk.index(ch) for ch in resident_window_chunks(sim.appended, g)]
+
+                # all layers at once needs one ring arrangement: the same slots, oldest first
+                same_ring = all(slots(s) == slots(sims[layer]) for s in sims)
+                st = libs.ll_cache_recache(h, target, FAKE_ACT, FAKE_ACT, len(chunks) * ct, None)
+                if not chunks or (target == -1 and not same_ring):
+                    assert status(libs, st) == "LL_ERR_BAD_STATE"
+                else:
+                    assert st == 0, libs.ll_last_error()
+                    nl = ctypes.c_int32()
+                    rows = (ctypes.c_int32 * 40)()
+                    k = libs.llh_last_copy(ctypes.byref(nl), rows)
+                    assert nl.value == (L if target == -1 else 1)
+                    assert list(rows[:k]) == [S * T + sims[layer].slot_chunk.index(ch) * ct for ch in chunks]
+            else:
+                n_cur = ct if op == "attn" else 0
+                st = libs.ll_sink_window_attn(h, layer, FAKE_ACT, 3, FAKE_ACT, FAKE_ACT, n_cur, 0.125,
+                                              FAKE_ACT, None, None)
+                ok = allowed_frames(n, frames_per_chunk=C, sink_frames=S, window_frames=W)
+                want = {f // C for f in ok if n_cur or f // C != n}
+                if not want:
+                    assert status(libs, st) == "LL_ERR_BAD_STATE"
+                    continue
+                assert st == 0, libs.ll_last_error()
+                nk = ctypes.c_int64()
+                runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
+                n_seg = libs.llh_last_attn(ctypes.byref(nk), runs)
+                covered, start = [], 0
+                for i in range(n_seg):
+                    kp, _vp, _hs, _rs, ks, ln = runs[RUN_FIELDS * i:RUN_FIELDS * i + 6]
+                    assert ks == start and ln == ct
+                    start += ln
+                    if kp == FAKE_ACT:
+                        assert i == n_seg - 1
+                        covered.append(n)
+                        continue
+                    row = (kp - FAKE_BUF - k_sink_off - layer * layer_bytes) // (2 * D)
+                    covered.append(row // ct if row < S * T else sims[layer].slot_chunk[(row - S * T) // ct])
+                assert nk.value == start
+                assert sorted(covered) == sorted(want)
+                assert len(covered) == len(set(covered))
+            for lay in range(L):
+                q = query(libs, h, lay, g.ring_slots)
+                assert q["chunks_appended"] == sims[lay].appended
+                assert q["slot_chunk"] == sims[lay].slot_chunk
+                assert q["ring_valid"] == len(sims[lay].fifo)
+    finally:
+        libs.ll_cache_destroy(h)
