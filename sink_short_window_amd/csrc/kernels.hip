@@ -14,21 +14,23 @@
 // read as zero.
 //
 // bf16 kernel (attn_pp_kernel), per workgroup: 8 waves x 32 queries of one
-// head.  Per 64-key tile:
-//   S^T[key][q] = K Q^T      bf16 MFMA 32x32x16, A = K rows from LDS, B = the
-//                            wave's Q fragment kept in registers.  Each lane
-//                            owns one query and 16 keys per 32-key block, so
-//                            row max / row sum are lane-local plus one swap
-//                            between the two 32-lane halves.
+// head, each wave's queries in two blocks of 16.  Per 64-key tile:
+//   S^T[key][q] = K Q^T      bf16 MFMA 16x16x32, A = K rows from LDS (each
+//                            read serves both query blocks), B = the wave's Q
+//                            fragments kept in registers.  Each lane owns two
+//                            queries and 16 of the 64 keys of each, so row
+//                            max / row sum are lane-local plus two swaps.
 //   online softmax in the log2 domain against a reference that the first
 //   tile sets to its max and that moves only when a tile's P would leave the
 //   safe fp32/bf16 range (exact: any reference gives the same softmax).
-//   O^T[d][q] += V^T P^T     bf16 MFMA; B = P straight from the S^T
+//   O^T[d][q] += V^T P^T     bf16 MFMA 16x16x32; B = P straight from the S^T
 //                            accumulators; A = V^T: for the bf16 cache, whose
 //                            V is stored transposed in 64-key tiles, a plain
 //                            16-byte LDS read; for row-major V (the caller's
 //                            current chunk, text K/V) the gfx950 transpose
 //                            read (ds_read_b64_tr_b16).
+// The 16x16x32 shape moves half the accumulator data per flop of the
+// 32x32x16 one; under the chip's power limit that buys more MFMA throughput.
 // The two halves of the workgroup alternate between an MFMA phase and a
 // softmax phase (details above attn_pp_kernel); K/V tiles reach LDS by
 // direct-to-LDS buffer loads.  An int8 cache is read either through a bf16
@@ -87,6 +89,15 @@ __device__ __forceinline__ float partner_half(float x) {
   const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   return __builtin_bit_cast(float, lane < 32 ? p[1] : p[0]);
 }
+// Value held by lane l^16, via v_permlane16_swap: with operands (x, x) the
+// first result holds, in every lane, the value of the lane with bit 4 clear
+// and the second the value of the lane with bit 4 set.
+__device__ __forceinline__ float partner_row(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, (lane & 16) ? p[0] : p[1]);
+}
 __device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, partner_half(x)); }
 __device__ __forceinline__ float swap_halves_sum(float x) { return x + partner_half(x); }
 
@@ -142,8 +153,8 @@ __device__ __forceinline__ QueryTile query_tile(const AttnArgs& a, int qtile, in
 // group A: while one wave of a SIMD issues MFMAs the other runs its softmax.
 //
 // K/V tiles live in a 4-stage LDS ring, rows unpadded, with the 16-byte
-// granules of row r XOR-swizzled by (r mod granules-per-row) so the MFMA
-// operand reads of 32 consecutive rows spread over the banks.  bf16 tiles are
+// granules of each row XOR-swizzled by a function of the row so that the
+// rows one MFMA operand read touches spread over the banks.  bf16 tiles are
 // loaded straight from memory into LDS (buffer_load ... lds): at the start of
 // its softmax phase t group A loads K(t+3) and group B V(t+3), three tiles
 // ahead.
@@ -182,6 +193,27 @@ __device__ __forceinline__ int k_swz(int r, int g) {
 template <int D>
 __device__ __forceinline__ int v_swz(int r, int g) {
   return r * SwzStage<D>::kRowB + (v_swz_gran<D>(r, g) << 4);
+}
+
+// Swizzles of the bf16 kernel's tiles, whose operands are read for the MFMA
+// 16x16x32 (granule g of row r is stored at g ^ mask(r)).  K: the 16 rows
+// that one 16-lane group reads together differ in bits 0-2 and 4 of the row
+// (see mfma_phase16); their masks are distinct (D = 128: 16 granules per
+// row) or distinct per row parity (D = 64: two rows per bank line).  V, read
+// by ds_read_b64_tr_b16: the 8 rows that 32 lanes read together differ in
+// bits 0-2 and get distinct masks on the granule pair.  Neither mask looks
+// at bits 3 and 5, which the key blocks and key steps add.
+template <int D>
+__device__ __forceinline__ int k16_mask(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return (r & 7) | (((r >> 4) & 1) << 3);
+  else return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int v16_mask(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return (r & 7) << 1;
+  else return ((r >> 1) & 3) << 1;
 }
 
 // Workgroup barrier that waits only for this wave's LDS operations; global
@@ -255,7 +287,7 @@ struct RunCursor {
 };
 
 // LDS-DMA load of rows [row_lo, row_lo + 16) of a tile (bf16 runs).
-template <int D>
+template <int D, bool kMfma16 = false>
 __device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16* tile_base, int row_lo,
                                          int lane) {
   using S = SwzStage<D>;
@@ -264,7 +296,9 @@ __device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16
   for (int r0 = 0; r0 < 16; r0 += S::kRowsPerLoad) {
     const int row = row_lo + r0 + lane / S::kGran;
     const int pg = lane % S::kGran;
-    const int lg = v_side ? v_swz_gran<D>(row, pg) : k_swz_gran<D>(row, pg);  // XOR: its own inverse
+    // XOR swizzles are their own inverse
+    const int lg = kMfma16 ? pg ^ (v_side ? v16_mask<D>(row) : k16_mask<D>(row))
+                           : (v_side ? v_swz_gran<D>(row, pg) : k_swz_gran<D>(row, pg));
     // row stride is a multiple of the (power-of-two) row size, so OR-ing in
     // the granule offset is exact and keeps the address a 32-bit value
     const uint32_t voff = (uint32_t(row0 + row) * c.rs) | (uint32_t(lg) << 4);
@@ -327,11 +361,13 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
   qtile = unit % nq;
 }
 
-// One MFMA phase of a wave: S(t) = K(t) Q^T (kQK) and O += V(t-1)^T P(t-1)^T
-// (kPV), as 16 + 16 MFMAs 32x32x16.  The operand reads are software
-// pipelined by hand: kAhead LDS reads are in flight ahead of the MFMA that
-// consumes them, and sched_barrier keeps the compiler from regrouping them
-// (left alone it waits for every pair of reads before each pair of MFMAs).
+// One MFMA phase of a wave of the int8 kernel: S(t) = K(t) Q^T (kQK) and
+// O += V(t-1)^T P(t-1)^T (kPV), as 16 + 16 MFMAs 32x32x16 (the bf16 kernel's
+// 16x16x32 phase, mfma_phase16, is built the same way).  The operand reads
+// are software pipelined by hand: kAhead LDS reads are in flight ahead of the
+// MFMA that consumes them, and sched_barrier keeps the compiler from
+// regrouping them (left alone it waits for every pair of reads before each
+// pair of MFMAs).
 // Five reads ahead measured as fast as six with fewer registers spilled.
 constexpr int kAhead = 5;
 
@@ -390,6 +426,68 @@ __device__ __forceinline__ void mfma_phase(const char* kt, const char* vt, int k
   __builtin_amdgcn_sched_barrier(0);
 }
 
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// One MFMA phase of a wave of the bf16 kernel: S(t) = K(t) Q'^T (kQK) and
+// O += V(t-1)^T P(t-1)^T (kPV) as MFMA 16x16x32 bf16, two per operand read:
+// the wave's two 16-query blocks share every K and V^T operand.  Operand i:
+// K (d-step kd = i/4, key block kb = i%4), then V^T (key step ks, 16-dim
+// block db).  A-row 4m + i of key block kb is the key
+//   32 (kb >> 1) + 16 (m >> 1) + 8 (kb & 1) + 4 (m & 1) + i,
+// so lane group g holds, in the S^T accumulators of blocks 2ks and 2ks + 1,
+// the keys 32 ks + swap23(8g + j), j = 0..7 (swap23 exchanges bits 2 and 3):
+// the keys of granule g of key step ks in a cached V^T tile, whose column p
+// holds key swap23(p).  That is the B operand of the PV MFMA as it stands.
+template <int D, bool kQK, bool kPV, bool kVT>
+__device__ __forceinline__ void mfma_phase16(const char* kt, const char* vt, const int (&koff)[D / 32],
+                                             const int (&voff)[D / 16], const int (&vb)[2],
+                                             const bf16x8 (&qf)[2][D / 32], const f32x4 (&cinit)[2],
+                                             f32x4 (&s)[2][4], f32x4 (&o)[2][D / 16], const bf16x8 (&pb)[2][2]) {
+  constexpr int kRowB = D * 2;
+  constexpr int NK = kQK ? 4 * (D / 32) : 0;
+  constexpr int NV = kPV ? 2 * (D / 16) : 0;
+  constexpr int N = NK + NV;
+  static_assert(N >= kAhead, "phase shorter than the read-ahead");
+  auto rd = [&](int i) -> bf16x8 {
+    if (i < NK) {
+      const int kd = i >> 2, kb = i & 3;
+      return *reinterpret_cast<const bf16x8*>(kt + koff[kd] + (32 * (kb >> 1) + 8 * (kb & 1)) * kRowB);
+    }
+    const int ii = i - NK;
+    const int ks = ii / (D / 16), db = ii % (D / 16);
+    if constexpr (kVT) {  // transposed tile: one 16-byte read of row 16 db + lane % 16
+      return *reinterpret_cast<const bf16x8*>(vt + vb[ks] + db * 16 * 128);
+    } else {  // row-major: the lane's keys 0..3 and 4..7 (8 rows apart), by two transpose reads
+      const char* base = vt + 32 * ks * kRowB + voff[db];
+      const bf16x4 lo = tr_read(reinterpret_cast<const __bf16*>(base));
+      const bf16x4 hi = tr_read(reinterpret_cast<const __bf16*>(base + 8 * kRowB));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  bf16x8 rb[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) rb[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < NK) {
+      const int kd = i >> 2, kb = i & 3;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[i % kAhead], qf[qb][kd],
+                                                            kd == 0 ? cinit[qb] : s[qb][kb], 0, 0, 0);
+    } else {
+      const int ii = i - NK;
+      const int ks = ii / (D / 16), db = ii % (D / 16);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[i % kAhead], pb[qb][ks], o[qb][db], 0, 0, 0);
+    }
+    if (i + kAhead < N) rb[i % kAhead] = rd(i + kAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, bool kOneRun>
 __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   using S = SwzStage<D>;
@@ -404,68 +502,81 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave >> 2;
   const int wq = wave & 3;
-  const int r32 = lane & 31;
-  const int half = lane >> 5;
+  // MFMA 16x16x32 lane roles: r16 = lane % 16 is the query column of each
+  // 16-query block, g = lane / 16 the 8-wide slice of the contraction and the
+  // 4-row slice of the result.
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
   const QueryTile qt = query_tile(a, qtile, kPPBM);
   const int n_seg = __builtin_amdgcn_readfirstlane(qt.n_seg);
-  const int qi = qt.q0 + wave * 32 + r32;
-  const bool q_ok = qi < qt.q_end;
-  const float c = a.scale * kLog2e;
-  const int64_t qrow = (int64_t(qi) * a.H + head) * D;
-
-  // The wave's queries, raw; converted to the MFMA fragment once the first
-  // K/V tiles' loads are in flight, so the two memory latencies overlap.
-  // (They are issued before any LDS-DMA load, so every vmcnt wait below that
-  // covers a tile also covers them.)
-  u32x4 qw[D / 16];
-  {
-    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
+  int qi[2];
+  bool q_ok[2];
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) qw[j] = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
+  for (int qb = 0; qb < 2; ++qb) {
+    qi[qb] = qt.q0 + wave * 32 + qb * 16 + r16;
+    q_ok[qb] = qi[qb] < qt.q_end;
+  }
+  const float c = a.scale * kLog2e;
+
+  // The lane's slices of its two queries, raw; converted to the MFMA
+  // fragment once the first K/V tiles' loads are in flight, so the two
+  // memory latencies overlap.  (They are issued before any LDS-DMA load, so
+  // every vmcnt wait below that covers a tile also covers them.)
+  u32x4 qw[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) +
+                                                    (int64_t(qi[qb]) * a.H + head) * D);
+#pragma unroll
+    for (int kd = 0; kd < D / 32; ++kd) qw[qb][kd] = q_ok[qb] ? q[4 * kd + g] : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 o[D / 32];
+  f32x4 o[2][D / 16];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  // Running reference max in log2 units; the S accumulators start at -m_run
-  // (cinit), so the MFMA output is already c*q.k - m_run.
-  float m_run = 0.f;
-  f32x16 cinit;
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cinit[r] = 0.f;
-  float l_run = 0.f;
-  bf16x8 pb[4];  // P of the last softmaxed tile, one bf16x8 per 16-key step
+      for (int r = 0; r < 4; ++r) o[qb][db][r] = 0.f;
+  // Running reference max per query in log2 units; the S accumulators start
+  // at -m_run (cinit), so the MFMA output is already c*q.k - m_run.
+  float m_run[2] = {0.f, 0.f};
+  f32x4 cinit[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cinit[qb][r] = 0.f;
+  float l_run[2] = {0.f, 0.f};
+  bf16x8 pb[2][2];  // P of the last softmaxed tile per query block and 32-key step
 
   // Byte offsets of this lane's operand reads.
-  // K (A of S^T): row kb*32 + r32, logical granule 2j + half, i.e. physical
-  // granule (2j ^ (r32 & ~1 & mask)) | (half ^ (r32 & 1)), formed per j.
-  const int k_row = r32 * S::kRowB + ((half ^ (r32 & 1)) << 4);
-  const int k_x = r32 & (S::kGran - 2);
-  // V (transpose reads): 16-lane group g16, lane j16 reads 4 elements of row
-  // 16*step + 8*a + 4*(g16 >> 1) + (j16 >> 2) at column
-  // 32*db + 16*(g16 & 1) + 4*(j16 & 3); the lane then holds V[4 keys][d].
-  const int g16 = lane >> 4, j16 = lane & 15;
-  int voff[2][D / 32];
-#pragma unroll
-  for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
-      const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
-      voff[aa][db] = v_swz<D>(row, col >> 3) + ((col & 7) << 1);
-    }
-  // V^T tiles (128-byte rows, see dma_vt): lane (r32, half) reads row
-  // 32*db + r32 at logical granule 2*step + half, stored at granule
-  // (2*step + half) ^ ((r32 >> 1) & 7).
-  int vb[4];
+  // K (A of S^T): key row 16 (m >> 1) + 4 (m & 1) + i, m = r16 >> 2,
+  // i = r16 & 3, of block 0 (the other blocks add 8 or 32 rows, which keep
+  // the mask), granule 4 kd + g.
+  int koff[D / 32];
   {
-    const int f = (r32 >> 1) & 7;
+    const int row = 16 * ((r16 >> 3) & 1) + 4 * ((r16 >> 2) & 1) + (r16 & 3);
 #pragma unroll
-    for (int step = 0; step < 4; ++step)
-      vb[step] = r32 * 128 + ((((2 * step) ^ (f & 6)) | (half ^ (f & 1))) << 4);
+    for (int kd = 0; kd < D / 32; ++kd) koff[kd] = row * S::kRowB + (((4 * kd + g) ^ k16_mask<D>(row)) << 4);
   }
+  // Row-major V (transpose reads): lane r16 of group g addresses row
+  // 16 (g >> 1) + 4 (g & 1) + (r16 >> 2) (+8 for the upper four keys, +32
+  // per key step; neither changes the mask) at column 16 db + 4 (r16 & 3);
+  // after the transpose it holds column 16 db + r16 of four consecutive rows.
+  int voff[D / 16];
+  {
+    const int row = 16 * (g >> 1) + 4 * (g & 1) + (r16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int col = 16 * db + 4 * (r16 & 3);
+      voff[db] = row * S::kRowB + (((col >> 3) ^ v16_mask<D>(row)) << 4) + ((col & 7) << 1);
+    }
+  }
+  // V^T tiles (128-byte rows, see dma_vt): row 16 db + r16, logical granule
+  // 4 ks + g, stored at granule (4 ks + g) ^ ((r16 >> 1) & 7).
+  int vb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) vb[ks] = r16 * 128 + (((4 * ks + g) ^ ((r16 >> 1) & 7)) << 4);
 
   // Tiles in the key set; the host never launches an empty one.
   const int n = kOneRun ? (a.seg[0].len + kBN - 1) / kBN : count_tiles(a, n_seg);
@@ -484,9 +595,9 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   {
     const int pre = min(n, 3);
     for (int j = 0; j < pre; ++j) {
-      if (group == 0) dma_rows<D>(ld, false, stage[j].k, 16 * wq, lane);
+      if (group == 0) dma_rows<D, true>(ld, false, stage[j].k, 16 * wq, lane);
       else if (ld.vt) dma_vt<D>(ld, stage[j].v, wq, lane);
-      else dma_rows<D>(ld, true, stage[j].v, 16 * wq, lane);
+      else dma_rows<D, true>(ld, true, stage[j].v, 16 * wq, lane);
       ld.advance(a, head);
     }
     if (group == 0) {
@@ -495,23 +606,28 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
       else wait_vmcnt<0>();
     }
   }
-  // Q fragment with the logit scale folded in: Q' = bf16(Q * scale * log2 e),
+  // Q fragments with the logit scale folded in: Q' = bf16(Q * scale * log2 e),
   // so the MFMA yields scores in log2 units.
-  bf16x8 qf[D / 16];
+  bf16x8 qf[2][D / 32];
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    f32x8 f;
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __builtin_bit_cast(float, qw[j][i] << 16) * c;
-      f[2 * i + 1] = __builtin_bit_cast(float, qw[j][i] & 0xffff0000u) * c;
+    for (int kd = 0; kd < D / 32; ++kd) {
+      f32x8 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_bit_cast(float, qw[qb][kd][i] << 16) * c;
+        f[2 * i + 1] = __builtin_bit_cast(float, qw[qb][kd][i] & 0xffff0000u) * c;
+      }
+      qf[qb][kd] = __builtin_convertvector(f, bf16x8);
     }
-    qf[j] = __builtin_convertvector(f, bf16x8);
-  }
   wg_barrier();
   if (group == 1) wg_barrier();  // group B runs one interval behind
 
-  f32x16 s[2];
+  // S^T accumulators: block kb of query block qb; element i of lane (r16, g)
+  // is key 32 (kb >> 1) + 16 (g >> 1) + 8 (kb & 1) + 4 (g & 1) + i against
+  // query 16 qb + r16.
+  f32x4 s[2][4];
 
   // Each group keeps three tiles of its side (A: K, B: V) in flight, issuing
   // tile t+3 at the start of its softmax phase t.  Group B makes sure V(t)
@@ -530,20 +646,22 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // Softmax phase t: online softmax of S(t) -> P(t).
   auto softmax_phase = [&](int t) {
     if (t + 3 < n) {  // A: K(t+3), B: V(t+3), straight into LDS
-      if (group == 0) dma_rows<D>(ld, false, stage[(t + 3) % kPPStages].k, 16 * wq, lane);
+      if (group == 0) dma_rows<D, true>(ld, false, stage[(t + 3) % kPPStages].k, 16 * wq, lane);
       else if (ld.vt) dma_vt<D>(ld, stage[(t + 3) % kPPStages].v, wq, lane);
-      else dma_rows<D>(ld, true, stage[(t + 3) % kPPStages].v, 16 * wq, lane);
+      else dma_rows<D, true>(ld, true, stage[(t + 3) % kPPStages].v, 16 * wq, lane);
       ld.advance(a, head);
     }
     const int valid = min(kBN, cu.len - cu.tile * kBN);
     cu.advance(a, head);
     if (valid < kBN) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= valid) s[kb][r] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int key = 32 * (kb >> 1) + 16 * (g >> 1) + 8 * (kb & 1) + 4 * (g & 1) + i;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (key >= valid) s[qb][kb][i] = -INFINITY;
         }
     }
     // Scores are relative to the reference m_run (cinit).  The first tile
@@ -552,61 +670,81 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     // (a score more than ~2^60 above the reference, or an overflow to inf)
     // takes the slow path that raises the reference and redoes P.  Any
     // reference gives the same softmax; the bound keeps P, the row sum and O
-    // finite in fp32 and bf16.
-    auto tile_max = [&]() {
-      float mp[4];
+    // finite in fp32 and bf16.  A query's keys are spread over the four
+    // lanes r16 + 16g, which reduce with two swaps.
+    auto tile_max = [&](float (&mx)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mp[i] = fmaxf(s[i >> 1][8 * (i & 1)], s[i >> 1][8 * (i & 1) + 1]);
+      for (int qb = 0; qb < 2; ++qb) {
+        float mp[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 2; r < 8; ++r) mp[i] = fmaxf(mp[i], s[i >> 1][8 * (i & 1) + r]);
-      return swap_halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-    };
-    // Move the reference up by sh (all lanes; sh = 0 leaves a lane as is).
-    auto shift_reference = [&](float sh, bool rescale) {
-      if (rescale) {
-        const float alpha = __builtin_amdgcn_exp2f(-sh);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        for (int kb = 0; kb < 4; ++kb) mp[kb] = fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3]));
+        const float m4 = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+        mx[qb] = swap_halves_max(fmaxf(m4, partner_row(m4)));
       }
-      m_run += sh;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cinit[r] = -m_run;
     };
-    // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand; the
-    // row sum adds exactly these rounded values, two per dot2.  s is kept.
-    auto form_p = [&]() {
-      float ls[2] = {0.f, 0.f};
+    // Move the reference of query block qb up by sh[qb] (sh = 0 leaves it).
+    auto shift_reference = [&](const float (&sh)[2], bool rescale) {
 #pragma unroll
-      for (int step = 0; step < 4; ++step) {
-        u32x4 pw;
+      for (int qb = 0; qb < 2; ++qb) {
+        if (rescale) {
+          const float alpha = __builtin_amdgcn_exp2f(-sh[qb]);
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x2 f = {__builtin_amdgcn_exp2f(s[step >> 1][8 * (step & 1) + 2 * i]),
-                           __builtin_amdgcn_exp2f(s[step >> 1][8 * (step & 1) + 2 * i + 1])};
-          const bf16x2 b = __builtin_convertvector(f, bf16x2);
-          pw[i] = __builtin_bit_cast(unsigned, b);
-          ls[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[i & 1], false);
+          for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[qb][db][r] *= alpha;
         }
-        pb[step] = __builtin_bit_cast(bf16x8, pw);
+        m_run[qb] += sh[qb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[qb][kb][r] -= sh[qb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cinit[qb][r] = -m_run[qb];
       }
-      return ls[0] + ls[1];
     };
-    if (t == 0) shift_reference(tile_max(), false);
-    float lt = form_p();
-    if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit))) {
-      shift_reference(fmaxf(tile_max(), 0.f), true);
-      lt = form_p();
+    // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand: key
+    // step ks takes blocks 2ks (keys 0..3 of the lane's eight) and 2ks + 1
+    // (keys 4..7).  The row sum adds exactly these rounded values, two per
+    // dot2.  s is kept.
+    auto form_p = [&](float (&lt)[2]) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 pw;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x4& src = s[qb][2 * ks + (w >> 1)];
+            const int i0 = 2 * (w & 1);
+            const f32x2 f = {__builtin_amdgcn_exp2f(src[i0]), __builtin_amdgcn_exp2f(src[i0 + 1])};
+            const bf16x2 b = __builtin_convertvector(f, bf16x2);
+            pw[w] = __builtin_bit_cast(unsigned, b);
+            ls[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[w & 1], false);
+          }
+          pb[qb][ks] = __builtin_bit_cast(bf16x8, pw);
+        }
+        lt[qb] = ls[0] + ls[1];
+      }
+    };
+    if (t == 0) {
+      float mx[2];
+      tile_max(mx);
+      shift_reference(mx, false);
     }
-    l_run += lt;
+    float lt[2];
+    form_p(lt);
+    if (__builtin_amdgcn_ballot_w64(!(lt[0] <= kTileSumLimit) || !(lt[1] <= kTileSumLimit))) {
+      float mx[2];
+      tile_max(mx);
+      mx[0] = fmaxf(mx[0], 0.f);
+      mx[1] = fmaxf(mx[1], 0.f);
+      shift_reference(mx, true);
+      form_p(lt);
+    }
+    l_run[0] += lt[0];
+    l_run[1] += lt[1];
     // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
     if (group == 0) {
       if (t + 3 < n) wait_vmcnt<2 * kLoads>();
@@ -622,7 +760,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // and softmax phase t, each closed by a workgroup barrier; the first and
   // last MFMA phases are peeled so the steady one is one straight-line block.
   __builtin_amdgcn_s_setprio(1);
-  mfma_phase<D, true, false, false>(kt(0), vt(0), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+  mfma_phase16<D, true, false, false>(kt(0), vt(0), koff, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(0);
   wg_barrier();
@@ -635,7 +773,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int t1 = min(n_vt + 1, n);
   for (int t = 1; t < t1; ++t) {  // PV of tile t-1 < n_vt: transposed V
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase<D, true, true, true>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+    mfma_phase16<D, true, true, true>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -644,7 +782,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   }
   for (int t = t1; t < n; ++t) {  // row-major V: transpose reads
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase<D, true, true, false>(kt(t), vt(t - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+    mfma_phase16<D, true, true, false>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -652,28 +790,30 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     wg_barrier();
   }
   __builtin_amdgcn_s_setprio(1);
-  if (n - 1 < n_vt) mfma_phase<D, false, true, true>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
-  else mfma_phase<D, false, true, false>(kt(n), vt(n - 1), k_row, k_x, voff, vb, qf, cinit, s, o, pb);
+  if (n - 1 < n_vt) mfma_phase16<D, false, true, true>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
+  else mfma_phase16<D, false, true, false>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(n);
   wg_barrier();
   wg_barrier();  // the softmax phase n does not exist; keep the two groups' barrier counts equal
   if (group == 0) wg_barrier();
 
-  const float l_tot = swap_halves_sum(l_run);
-  if (!q_ok) return;
-  const float inv = 1.f / l_tot;
+  // O^T accumulators: element i of lane (r16, g) in block (qb, db) is
+  // dimension 16 db + 4g + i of query 16 qb + r16.
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l4 = l_run[qb] + partner_row(l_run[qb]);
+    const float l_tot = swap_halves_sum(l4);
+    if (!q_ok[qb]) continue;
+    const float inv = 1.f / l_tot;
+    __bf16* orow = static_cast<__bf16*>(a.out) + (int64_t(qi[qb]) * a.H + head) * D;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d0 = db * 32 + 8 * gq + 4 * half;
-      float4 f = make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                             o[db][4 * gq + 3] * inv);
-      const bf16x4 b = __builtin_convertvector(*reinterpret_cast<float __attribute__((__vector_size__(16)))*>(&f), bf16x4);
-      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + qrow + d0) = b;
+    for (int db = 0; db < D / 16; ++db) {
+      const f32x4 f = o[qb][db] * inv;
+      *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g) = __builtin_convertvector(f, bf16x4);
     }
-  if (a.lse && half == 0) a.lse[int64_t(head) * a.n_q + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (a.lse && g == 0) a.lse[int64_t(head) * a.n_q + qi[qb]] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------------------
