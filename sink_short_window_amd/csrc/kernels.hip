@@ -71,7 +71,8 @@ constexpr float kRescaleLog2 = 8.0f;   // fp32 kernel: rescale when the max grow
 // above the reference, or inf) makes the softmax raise its reference.
 constexpr float kTileSumLimit = 0x1p60f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr bf16x8 kOnes8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                           (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -705,12 +706,15 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     };
     // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand: key
     // step ks takes blocks 2ks (keys 0..3 of the lane's eight) and 2ks + 1
-    // (keys 4..7).  The row sum adds exactly these rounded values, two per
-    // dot2.  s is kept.
+    // (keys 4..7).  s is kept.  The tile's row sums of exactly these rounded
+    // values come from two MFMAs per query block with an all-ones A operand
+    // (every result row is the sum over the 64 keys), not from VALU adds:
+    // while the other wave of the SIMD streams MFMAs this wave gets about one
+    // VALU issue per MFMA, so the softmax phase is priced in VALU
+    // instructions.  Each lane then holds its queries' full tile sums.
     auto form_p = [&](float (&lt)[2]) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float ls[2] = {0.f, 0.f};
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           u32x4 pw;
@@ -719,13 +723,16 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
             const f32x4& src = s[qb][2 * ks + (w >> 1)];
             const int i0 = 2 * (w & 1);
             const f32x2 f = {__builtin_amdgcn_exp2f(src[i0]), __builtin_amdgcn_exp2f(src[i0 + 1])};
-            const bf16x2 b = __builtin_convertvector(f, bf16x2);
-            pw[w] = __builtin_bit_cast(unsigned, b);
-            ls[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, kOnes2, ls[w & 1], false);
+            pw[w] = __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
           }
           pb[qb][ks] = __builtin_bit_cast(bf16x8, pw);
         }
-        lt[qb] = ls[0] + ls[1];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][0], sum, 0, 0, 0);
+        sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][1], sum, 0, 0, 0);
+        lt[qb] = sum[0];
       }
     };
     if (t == 0) {
@@ -802,8 +809,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // dimension 16 db + 4g + i of query 16 qb + r16.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l4 = l_run[qb] + partner_row(l_run[qb]);
-    const float l_tot = swap_halves_sum(l4);
+    const float l_tot = l_run[qb];  // already summed over the 4 lanes of the query
     if (!q_ok[qb]) continue;
     const float inv = 1.f / l_tot;
     __bf16* orow = static_cast<__bf16*>(a.out) + (int64_t(qi[qb]) * a.H + head) * D;
