@@ -362,6 +362,23 @@ __device__ __forceinline__ void xcd_unit(int& head, int& qtile) {
   qtile = unit % nq;
 }
 
+// Chunk-causal query tiles (the re-encoding call): the tiles of window chunk
+// r attend one chunk more than those of chunk r-1, so their work grows with
+// r.  The workgroups are numbered chunk-major, latest chunk first, head-major
+// inside a chunk, and keep the hardware's round-robin dealing of linear ids
+// to the XCDs: every XCD then gets the same mix of sizes and starts its
+// largest units first, so no CU runs two of the largest back to back while
+// others idle.  (The K/V of a head are then read on every XCD, which the
+// prefetch three tiles ahead hides; the call stays MFMA-bound.)
+__device__ __forceinline__ void chunk_major_unit(const AttnArgs& a, int& head, int& qtile) {
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int per_chunk = gridDim.y * a.q_tiles;  // heads x query tiles of one chunk
+  const int n_chunks = gridDim.x / a.q_tiles;
+  const int rem = lin % per_chunk;
+  head = rem / a.q_tiles;
+  qtile = (n_chunks - 1 - lin / per_chunk) * a.q_tiles + rem % a.q_tiles;
+}
+
 // One MFMA phase of a wave of the int8 kernel: S(t) = K(t) Q^T (kQK) and
 // O += V(t-1)^T P(t-1)^T (kPV), as 16 + 16 MFMAs 32x32x16 (the bf16 kernel's
 // 16x16x32 phase, mfma_phase16, is built the same way).  The operand reads
@@ -496,7 +513,8 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) S stage[kPPStages];
 
   int head, qtile;
-  xcd_unit(head, qtile);
+  if (a.q_chunk == 0) xcd_unit(head, qtile);
+  else chunk_major_unit(a, head, qtile);
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // group's branches and the buffer descriptors scalar
@@ -905,7 +923,8 @@ __global__ __launch_bounds__(kPPThreads) void attn_i8_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) ScaleSlot sring[kScaleStages];
 
   int head, qtile;
-  xcd_unit(head, qtile);
+  if (a.q_chunk == 0) xcd_unit(head, qtile);
+  else chunk_major_unit(a, head, qtile);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave >> 2;
