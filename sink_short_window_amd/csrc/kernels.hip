@@ -287,7 +287,9 @@ struct RunCursor {
   }
 };
 
-// LDS-DMA load of rows [row_lo, row_lo + 16) of a tile (bf16 runs).
+// LDS-DMA load of rows [row_lo, row_lo + 16) of a tile (bf16 runs), in the
+// swizzle of the kernel that reads it: kMfma16 for the bf16 kernel's
+// 16x16x32 operand reads (k16_mask / v16_mask), else the int8 kernel's.
 template <int D, bool kMfma16 = false>
 __device__ __forceinline__ void dma_rows(const RunCursor& c, bool v_side, __bf16* tile_base, int row_lo,
                                          int lane) {
