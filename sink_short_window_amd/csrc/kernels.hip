@@ -530,6 +530,11 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int g = lane >> 4;
   const QueryTile qt = query_tile(a, qtile, kPPBM);
   const int n_seg = __builtin_amdgcn_readfirstlane(qt.n_seg);
+  // A wave whose 32 queries all lie past the tile's end (the ragged last
+  // query tile of a head) skips its MFMAs and softmax arithmetic, but still
+  // loads its share of every K/V tile and meets every wait and barrier: the
+  // power it does not draw goes to the other waves' clock.
+  const bool idle = __builtin_amdgcn_readfirstlane(qt.q0 + wave * 32) >= qt.q_end;
   int qi[2];
   bool q_ok[2];
 #pragma unroll
@@ -674,104 +679,106 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     }
     const int valid = min(kBN, cu.len - cu.tile * kBN);
     cu.advance(a, head);
-    if (valid < kBN) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 32 * (kb >> 1) + 16 * (g >> 1) + 8 * (kb & 1) + 4 * (g & 1) + i;
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            if (key >= valid) s[qb][kb][i] = -INFINITY;
-        }
-    }
-    // Scores are relative to the reference m_run (cinit).  The first tile
-    // sets the reference to its max.  Later tiles skip the max: P = 2^s is
-    // formed and summed first, and only a tile whose sum leaves the safe range
-    // (a score more than ~2^60 above the reference, or an overflow to inf)
-    // takes the slow path that raises the reference and redoes P.  Any
-    // reference gives the same softmax; the bound keeps P, the row sum and O
-    // finite in fp32 and bf16.  A query's keys are spread over the four
-    // lanes r16 + 16g, which reduce with two swaps.
-    auto tile_max = [&](float (&mx)[2]) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mp[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mp[kb] = fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3]));
-        const float m4 = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-        mx[qb] = swap_halves_max(fmaxf(m4, partner_row(m4)));
-      }
-    };
-    // Move the reference of query block qb up by sh[qb] (sh = 0 leaves it).
-    auto shift_reference = [&](const float (&sh)[2], bool rescale) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (rescale) {
-          const float alpha = __builtin_amdgcn_exp2f(-sh[qb]);
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[qb][db][r] *= alpha;
-        }
-        m_run[qb] += sh[qb];
+    if (!idle) {  // the loads and the cursor above, and group A's wait below, run in every wave
+      if (valid < kBN) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[qb][kb][r] -= sh[qb];
+          for (int i = 0; i < 4; ++i) {
+            const int key = 32 * (kb >> 1) + 16 * (g >> 1) + 8 * (kb & 1) + 4 * (g & 1) + i;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cinit[qb][r] = -m_run[qb];
-      }
-    };
-    // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand: key
-    // step ks takes blocks 2ks (keys 0..3 of the lane's eight) and 2ks + 1
-    // (keys 4..7).  s is kept.  The tile's row sums of exactly these rounded
-    // values come from two MFMAs per query block with an all-ones A operand
-    // (every result row is the sum over the 64 keys), not from VALU adds:
-    // while the other wave of the SIMD streams MFMAs this wave gets about one
-    // VALU issue per MFMA, so the softmax phase is priced in VALU
-    // instructions.  Each lane then holds its queries' full tile sums.
-    auto form_p = [&](float (&lt)[2]) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4 pw;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f32x4& src = s[qb][2 * ks + (w >> 1)];
-            const int i0 = 2 * (w & 1);
-            const f32x2 f = {__builtin_amdgcn_exp2f(src[i0]), __builtin_amdgcn_exp2f(src[i0 + 1])};
-            pw[w] = __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+            for (int qb = 0; qb < 2; ++qb)
+              if (key >= valid) s[qb][kb][i] = -INFINITY;
           }
-          pb[qb][ks] = __builtin_bit_cast(bf16x8, pw);
-        }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-        sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][0], sum, 0, 0, 0);
-        sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][1], sum, 0, 0, 0);
-        lt[qb] = sum[0];
       }
-    };
-    if (t == 0) {
-      float mx[2];
-      tile_max(mx);
-      shift_reference(mx, false);
-    }
-    float lt[2];
-    form_p(lt);
-    if (__builtin_amdgcn_ballot_w64(!(lt[0] <= kTileSumLimit) || !(lt[1] <= kTileSumLimit))) {
-      float mx[2];
-      tile_max(mx);
-      mx[0] = fmaxf(mx[0], 0.f);
-      mx[1] = fmaxf(mx[1], 0.f);
-      shift_reference(mx, true);
+      // Scores are relative to the reference m_run (cinit).  The first tile
+      // sets the reference to its max.  Later tiles skip the max: P = 2^s is
+      // formed and summed first, and only a tile whose sum leaves the safe range
+      // (a score more than ~2^60 above the reference, or an overflow to inf)
+      // takes the slow path that raises the reference and redoes P.  Any
+      // reference gives the same softmax; the bound keeps P, the row sum and O
+      // finite in fp32 and bf16.  A query's keys are spread over the four
+      // lanes r16 + 16g, which reduce with two swaps.
+      auto tile_max = [&](float (&mx)[2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float mp[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) mp[kb] = fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3]));
+          const float m4 = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+          mx[qb] = swap_halves_max(fmaxf(m4, partner_row(m4)));
+        }
+      };
+      // Move the reference of query block qb up by sh[qb] (sh = 0 leaves it).
+      auto shift_reference = [&](const float (&sh)[2], bool rescale) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (rescale) {
+            const float alpha = __builtin_amdgcn_exp2f(-sh[qb]);
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[qb][db][r] *= alpha;
+          }
+          m_run[qb] += sh[qb];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[qb][kb][r] -= sh[qb];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cinit[qb][r] = -m_run[qb];
+        }
+      };
+      // P = 2^s as bf16 pairs (one 32-bit word each) for the PV operand: key
+      // step ks takes blocks 2ks (keys 0..3 of the lane's eight) and 2ks + 1
+      // (keys 4..7).  s is kept.  The tile's row sums of exactly these rounded
+      // values come from two MFMAs per query block with an all-ones A operand
+      // (every result row is the sum over the 64 keys), not from VALU adds:
+      // while the other wave of the SIMD streams MFMAs this wave gets about one
+      // VALU issue per MFMA, so the softmax phase is priced in VALU
+      // instructions.  Each lane then holds its queries' full tile sums.
+      auto form_p = [&](float (&lt)[2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            u32x4 pw;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const f32x4& src = s[qb][2 * ks + (w >> 1)];
+              const int i0 = 2 * (w & 1);
+              const f32x2 f = {__builtin_amdgcn_exp2f(src[i0]), __builtin_amdgcn_exp2f(src[i0 + 1])};
+              pw[w] = __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+            }
+            pb[qb][ks] = __builtin_bit_cast(bf16x8, pw);
+          }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+          sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][0], sum, 0, 0, 0);
+          sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pb[qb][1], sum, 0, 0, 0);
+          lt[qb] = sum[0];
+        }
+      };
+      if (t == 0) {
+        float mx[2];
+        tile_max(mx);
+        shift_reference(mx, false);
+      }
+      float lt[2];
       form_p(lt);
+      if (__builtin_amdgcn_ballot_w64(!(lt[0] <= kTileSumLimit) || !(lt[1] <= kTileSumLimit))) {
+        float mx[2];
+        tile_max(mx);
+        mx[0] = fmaxf(mx[0], 0.f);
+        mx[1] = fmaxf(mx[1], 0.f);
+        shift_reference(mx, true);
+        form_p(lt);
+      }
+      l_run[0] += lt[0];
+      l_run[1] += lt[1];
     }
-    l_run[0] += lt[0];
-    l_run[1] += lt[1];
     // group A: K(t+1) must be in LDS before M(t+1); K(t+2), K(t+3) may fly on
     if (group == 0) {
       if (t + 3 < n) wait_vmcnt<2 * kLoads>();
@@ -787,7 +794,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   // and softmax phase t, each closed by a workgroup barrier; the first and
   // last MFMA phases are peeled so the steady one is one straight-line block.
   __builtin_amdgcn_s_setprio(1);
-  mfma_phase16<D, true, false, false>(kt(0), vt(0), koff, voff, vb, qf, cinit, s, o, pb);
+  if (!idle) mfma_phase16<D, true, false, false>(kt(0), vt(0), koff, voff, vb, qf, cinit, s, o, pb);
   __builtin_amdgcn_s_setprio(0);
   after_mfma(0);
   wg_barrier();
@@ -800,7 +807,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   const int t1 = min(n_vt + 1, n);
   for (int t = 1; t < t1; ++t) {  // PV of tile t-1 < n_vt: transposed V
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase16<D, true, true, true>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
+    if (!idle) mfma_phase16<D, true, true, true>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -809,7 +816,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
   }
   for (int t = t1; t < n; ++t) {  // row-major V: transpose reads
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase16<D, true, true, false>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
+    if (!idle) mfma_phase16<D, true, true, false>(kt(t), vt(t - 1), koff, voff, vb, qf, cinit, s, o, pb);
     __builtin_amdgcn_s_setprio(0);
     after_mfma(t);
     wg_barrier();
@@ -817,8 +824,10 @@ __global__ __launch_bounds__(kPPThreads) void attn_pp_kernel(AttnArgs a) {
     wg_barrier();
   }
   __builtin_amdgcn_s_setprio(1);
-  if (n - 1 < n_vt) mfma_phase16<D, false, true, true>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
-  else mfma_phase16<D, false, true, false>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
+  if (!idle) {
+    if (n - 1 < n_vt) mfma_phase16<D, false, true, true>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
+    else mfma_phase16<D, false, true, false>(kt(n), vt(n - 1), koff, voff, vb, qf, cinit, s, o, pb);
+  }
   __builtin_amdgcn_s_setprio(0);
   after_mfma(n);
   wg_barrier();
