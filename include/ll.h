@@ -202,9 +202,12 @@ ll_status ll_sink_window_attn(const ll_cache* cache, int32_t layer, const void* 
  *   q, out, dout: [n_q][H][D] bf16 (out and lse from the forward call);
  *   lse:   float [H][n_q], required;
  *   delta: float [H][n_q] device workspace, overwritten with rowsum(dout*out);
- *   dq:    float [n_q][H][D], written;
+ *   dq:    float [n_q][H][D], written; when dk_cur/dv_cur are asked for, the
+ *          call first uses its first n_q*H*D*2 bytes as scratch for a bf16
+ *          copy of the scaled queries, so dq must not overlap any input;
  *   dk_cur, dv_cur: float [C_tok][H][D], written when n_cur == C_tok (ignored
- *          when n_cur == 0).
+ *          when n_cur == 0).  With them, (n_q + 64) * H * D * 2 must be below
+ *          4 GiB (else LL_ERR_UNSUPPORTED).
  * Gradients are fp32, accumulated in fp32 from bf16 MFMA products of bf16
  * operands (P and dS rounded to bf16); P is recomputed from the forward's lse.
  * BF16 activations only (else LL_ERR_UNSUPPORTED); with an I8 cache the

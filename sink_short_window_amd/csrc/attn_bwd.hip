@@ -13,24 +13,28 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  delta = rowsum(dO O),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // Three kernels on the stream:
-//   bwd_delta_kernel  delta[h][i] = dO_i . O_i (fp32).
+//   bwd_delta_kernel  delta[h][i] = dO_i . O_i (fp32); when dK/dV are asked
+//                     for, also Q' (below) as bf16 into the first half of dq.
+//   bwd_dkv_kernel    per 256 keys of the current chunk: loop over 64-query
+//                     tiles; S = Q' K^T, dP = dO V^T (K/V fragments in
+//                     registers), then dV^T += dO^T P and dK^T += Q'^T dS with
+//                     dO^T and Q'^T from transpose reads.  The Q' and dO
+//                     tiles stream straight into a 3-stage LDS ring (LDS-DMA),
+//                     two tiles ahead.
 //   bwd_dq_kernel     per 256 queries of one head (8 waves x 32): walk every
 //                     64-key tile of every run; S^T = K Q'^T and dP^T = V dO^T
 //                     (bf16 MFMA 32x32x16, K/V rows from LDS, Q' and dO in
 //                     registers), P = 2^(S^T - lse2) from the forward's
 //                     log-sum-exp, dS^T in fp32 rounded to bf16, then
 //                     dQ^T += K^T dS^T with K^T from gfx950 transpose reads.
-//   bwd_dkv_kernel    per 256 keys of the current chunk: loop over 64-query
-//                     tiles; S = Q' K^T, dP = dO V^T (K/V fragments in
-//                     registers), then dV^T += dO^T P and dK^T += Q'^T dS with
-//                     dO^T and Q'^T from transpose reads.
+//                     It runs last: it overwrites the Q' copy in dq.
 // Q' = bf16(Q * scale * log2 e) exactly as the forward kernel forms it, so P is
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
 //
-// Tiles reach LDS through registers, in layouts (RowTile, VtTile) whose XOR
-// swizzles or skewed padding keep both the 16-byte row reads and the
-// transpose reads free of bank conflicts.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
+// Tiles sit in LDS in layouts (RowTile, VtTile) whose XOR swizzles or skewed
+// padding keep both the 16-byte row reads and the transpose reads free of
+// bank conflicts; the dQ kernel stages its tiles through registers.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
 // as the bf16 cache stores it; the caller's row-major current chunk is
 // transposed while staged) and its rows are read back with transpose reads.
 
@@ -165,7 +169,10 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int s2) {
 }
 
 // ---------------------------------------------------------------------------
-// delta[h][i] = sum_d dO[i][h][d] * O[i][h][d]
+// delta[h][i] = sum_d dO[i][h][d] * O[i][h][d]; and, when the dK/dV kernel
+// runs, Q' = bf16(Q * scale * log2 e) ([n_q][H][D] bf16) in the first half of
+// dq, which that kernel streams into LDS as it is.  The dQ kernel runs last
+// and overwrites dq.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
@@ -177,6 +184,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(AttnBwdArgs p) {
   if (row < rows) {
     const u32x4 o = reinterpret_cast<const u32x4*>(p.out)[row * kLanes + part];
     const u32x4 g = reinterpret_cast<const u32x4*>(p.dout)[row * kLanes + part];
+    if (p.dk) {
+      const u32x4 q = reinterpret_cast<const u32x4*>(p.a.q)[row * kLanes + part];
+      reinterpret_cast<bf16x8*>(p.dq)[row * kLanes + part] = scale_bf16x8(q, p.a.scale * kLog2e);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc += bf_lo(o[i]) * bf_lo(g[i]) + bf_hi(o[i]) * bf_hi(g[i]);
   }
@@ -387,14 +398,44 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
 // ---------------------------------------------------------------------------
 // dK, dV of the current chunk (the last run)
 // ---------------------------------------------------------------------------
+// The tile ring: Q' rows and dO rows in the padded, skewed RowTile layout,
+// plus the tile's forward log-sum-exp and delta.  Three stages, each its own
+// __shared__ variable so that the compiler can tell a stage being filled by
+// LDS-DMA from the stage being read and does not wait for the fill.
+template <int D>
+struct DkvStage {
+  char q[RowTile<D, false>::kBytes];
+  char g[RowTile<D, false>::kBytes];
+  float lse[kTile];
+  float dl[kTile];
+};
+
+// s_waitcnt vmcnt(N) (N <= 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations; LDS-DMA
+// loads stay in flight (their waits are explicit).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   using QT = RowTile<D, false>;  // padded and skewed: the XOR swizzle's address arithmetic spills here
-  constexpr int NV = D / 8;
-  __shared__ __attribute__((aligned(16))) char qs[QT::kBytes];   // Q' rows
-  __shared__ __attribute__((aligned(16))) char gs[QT::kBytes];   // dO rows
-  __shared__ __attribute__((aligned(16))) float lse2s[kTile];
-  __shared__ __attribute__((aligned(16))) float dls[kTile];
+  constexpr int G = QT::RB / 16;  // 16-byte slots per LDS row, padding included
+  constexpr int NI = G / 4;       // 1 KB LDS-DMA loads per wave per tile side (4 waves per side)
+  static_assert(G % 4 == 0, "tile side splits over four waves");
+  __shared__ __attribute__((aligned(16))) DkvStage<D> st0;
+  __shared__ __attribute__((aligned(16))) DkvStage<D> st1;
+  __shared__ __attribute__((aligned(16))) DkvStage<D> st2;
   const AttnArgs& a = p.a;
   const KvSeg& cur = a.seg[a.n_seg - 1];
   int head, ktile;
@@ -403,7 +444,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
   const int key = ktile * kBwdBK + wave * 32 + r32;
   const bool k_ok = key < cur.len;
-  const float c = a.scale * kLog2e;
 
   // B operands: K and V of the lane's key, d = 16j + 8*half .. +7.
   bf16x8 kf[D / 16], vf[D / 16];
@@ -424,54 +464,56 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
   int toff[2][D / 32];
   tr_offsets<D, QT>(lane, toff);
-  const __bf16* q = static_cast<const __bf16*>(a.q);
-  const __bf16* g = static_cast<const __bf16*>(p.dout);
 
-  for (int q0 = 0; q0 < a.n_q; q0 += kTile) {
-    __syncthreads();
-    {
-      // every load of the tile in flight at once: rows past n_q read the
-      // last query (in bounds) and are zeroed after the loads
-      constexpr int NL = kTile * NV / kBwdThreads;
-      u32x4 wq[NL], wg[NL];
+  // Tile loads, straight into LDS.  Waves 0-3 fill the Q' side (the delta
+  // kernel's bf16(Q c) copy at the start of dq), waves 4-7 the dO side; wave
+  // 0 also loads the tile's lse and wave 4 its delta.  Slot s of a side (one
+  // lane of instruction s / 64) is LDS row s / G, slot s % G, which holds
+  // granule (s % G) - skew(row) of that query row; the padding slots take a
+  // duplicate of an in-row granule and are never read.  Query rows past n_q
+  // lie past the end of every buffer range and load as zeros: Q' = dO = 0
+  // and lse = delta = 0 give P = 1 and dS = 0, and a zero dO row, so those
+  // rows add nothing to dK or dV.
+  const int side = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
+  const uint32_t row_bytes = uint32_t(a.H) * D * 2;  // one query's row of all heads
+  const uint32_t side_bytes = uint32_t(a.n_q) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rside = rsrc(side ? p.dout : static_cast<const void*>(p.dq), side_bytes);
+  const __amdgpu_buffer_rsrc_t rvec = rsrc(side ? static_cast<const void*>(p.delta + int64_t(head) * a.n_q)
+                                                : static_cast<const void*>(p.lse + int64_t(head) * a.n_q),
+                                           uint32_t(a.n_q) * 4);
+  auto issue = [&](DkvStage<D>& s, int t) {
+    // The lane's slot addresses are recomputed per tile from an opaque copy of
+    // the lane id, so the compiler does not keep them in registers across the
+    // loop (the MFMA accumulators and K/V fragments fill the register file).
+    int ln = lane;
+    __asm__ __volatile__("" : "+v"(ln));
+    const uint32_t t0 = uint32_t(t) * kTile * row_bytes + uint32_t(head) * (D * 2);
+    char* dst = side ? s.g : s.q;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int it = tid + i * kBwdThreads;
-        const int qi = min(q0 + it / NV, a.n_q - 1);
-        const int64_t e = (int64_t(qi) * a.H + head) * D + (it % NV) * 8;
-        wq[i] = *reinterpret_cast<const u32x4*>(q + e);
-        wg[i] = *reinterpret_cast<const u32x4*>(g + e);
-      }
-      const int ql = min(q0 + (tid & (kTile - 1)), a.n_q - 1);
-      const float lsel = p.lse[int64_t(head) * a.n_q + ql];
-      const float dll = p.delta[int64_t(head) * a.n_q + ql];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int it = tid + i * kBwdThreads;
-        const int row = it / NV, vec = it % NV;
-        const bool ok = q0 + row < a.n_q;
-        const u32x4 z = {0, 0, 0, 0};
-        *reinterpret_cast<bf16x8*>(qs + QT::off(row, vec)) = scale_bf16x8(ok ? wq[i] : z, c);
-        *reinterpret_cast<u32x4*>(gs + QT::off(row, vec)) = ok ? wg[i] : z;
-      }
-      if (tid < kTile) {
-        const bool ok = q0 + tid < a.n_q;
-        lse2s[tid] = ok ? lsel * kLog2e : INFINITY;
-        dls[tid] = ok ? dll : 0.f;
-      }
+    for (int k = 0; k < NI; ++k) {
+      const int sl = (wq * NI + k) * 64 + ln;
+      const int row = sl / G;
+      const int gran = min(max(sl % G - ((row >> 2) & 3), 0), D / 8 - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rside, (__attribute__((address_space(3))) void*)(dst + (wq * NI + k) * 1024),
+                                               16, t0 + uint32_t(row) * row_bytes + uint32_t(gran) * 16, 0, 0, 0);
     }
-    __syncthreads();
+    if (wq == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rvec, (__attribute__((address_space(3))) void*)(side ? s.dl : s.lse),
+                                               4, uint32_t(t * kTile + ln) * 4, 0, 0, 0);
+  };
+
+  auto compute = [&](const DkvStage<D>& s) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s, dp;
+      f32x16 sc, dp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 qa = row_read<QT>(qs, qb * 32 + r32, 2 * j + half);
-        const bf16x8 ga = row_read<QT>(gs, qb * 32 + r32, 2 * j + half);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[j], s, 0, 0, 0);
+        const bf16x8 qa = row_read<QT>(s.q, qb * 32 + r32, 2 * j + half);
+        const bf16x8 ga = row_read<QT>(s.g, qb * 32 + r32, 2 * j + half);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[j], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[j], dp, 0, 0, 0);
       }
       // rows of the accumulators: queries qb*32 + 8*(e >> 2) + 4*half + (e & 3)
@@ -479,14 +521,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int q4 = qb * 32 + 8 * g4 + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(&lse2s[q4]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&dls[q4]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&s.lse[q4]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[q4]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g4 + i;
-          pr[e] = __builtin_amdgcn_exp2f(s[e] - lv[i]);
+          pr[e] = __builtin_amdgcn_exp2f(fmaf(-lv[i], kLog2e, sc[e]));  // scores are in log2 units
           ds[e] = pr[e] * (dp[e] - dv4[i]);
         }
       }
@@ -496,11 +538,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
         const bf16x8 db8 = pack8(ds, s2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(gs, 2 * qb + s2, toff, db), pb, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(qs, 2 * qb + s2, toff, db), db8, dk[db], 0, 0, 0);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(s.g, 2 * qb + s2, toff, db), pb, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(s.q, 2 * qb + s2, toff, db), db8, dk[db], 0, 0, 0);
         }
       }
     }
+  };
+
+  // Tile t sits in stage t mod 3.  Step t: wait for this wave's loads of tile
+  // t (tile t+1's may stay in flight), one barrier (every wave's tile t has
+  // landed and every wave is done with tile t-1), then load tile t+2 into the
+  // stage tile t-1 used, and compute tile t.
+  const int nt = (a.n_q + kTile - 1) / kTile;
+  issue(st0, 0);
+  if (nt > 1) issue(st1, 1);
+  auto step = [&](const DkvStage<D>& cur_st, DkvStage<D>& next2, int t) {
+    if (t + 1 < nt) {
+      if (wq == 0) wait_vmcnt<NI + 1>();
+      else wait_vmcnt<NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wg_barrier();
+    if (t + 2 < nt) issue(next2, t + 2);
+    compute(cur_st);
+  };
+  for (int t = 0; t < nt; t += 3) {
+    step(st0, st2, t);
+    if (t + 1 < nt) step(st1, st0, t + 1);
+    if (t + 2 < nt) step(st2, st1, t + 2);
   }
   if (!k_ok) return;
   // dK = scale dS^T Q = (dS^T Q') / log2 e
@@ -532,10 +598,12 @@ int launch_bwd_d(const AttnBwdArgs& p, void* stream) {
   const int64_t lanes = int64_t(a.n_q) * a.H * (D / 8);
   int err = launch(bwd_delta_kernel<D>, dim3(unsigned((lanes + 255) / 256)), dim3(256), &p, stream);
   if (err) return err;
-  err = launch(bwd_dq_kernel<D>, dim3((a.n_q + kBwdBQ - 1) / kBwdBQ, a.H), dim3(kBwdThreads), &p, stream);
-  if (err || !p.dk) return err;
-  const int len = a.seg[a.n_seg - 1].len;
-  return launch(bwd_dkv_kernel<D>, dim3((len + kBwdBK - 1) / kBwdBK, a.H), dim3(kBwdThreads), &p, stream);
+  if (p.dk) {  // before the dQ kernel, which overwrites the Q' copy in dq
+    const int len = a.seg[a.n_seg - 1].len;
+    err = launch(bwd_dkv_kernel<D>, dim3((len + kBwdBK - 1) / kBwdBK, a.H), dim3(kBwdThreads), &p, stream);
+    if (err) return err;
+  }
+  return launch(bwd_dq_kernel<D>, dim3((a.n_q + kBwdBQ - 1) / kBwdBQ, a.H), dim3(kBwdThreads), &p, stream);
 }
 
 }  // namespace

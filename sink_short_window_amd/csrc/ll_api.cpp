@@ -185,6 +185,11 @@ ll_status attn_bwd_impl(const ll_cache* cache, int32_t layer, const void* q, int
     if ((st = check_act_ptr(k_cur, "k_cur")) != LL_OK || (st = check_act_ptr(v_cur, "v_cur")) != LL_OK ||
         (st = check_act_ptr(dk_cur, "dk_cur")) != LL_OK || (st = check_act_ptr(dv_cur, "dv_cur")) != LL_OK)
       return st;
+    // The dK/dV kernel addresses the bf16 queries and dout with 32-bit byte
+    // offsets, rounded up to whole 64-query tiles.
+    if ((n_q + 64) * int64_t(g.H) * g.D * 2 >= (int64_t(1) << 32))
+      return fail(LL_ERR_UNSUPPORTED, "with dk_cur/dv_cur, (n_q + 64) * num_heads * head_dim * 2 bytes must be "
+                                      "below 4 GiB");
   }
   ll::AttnBwdArgs b;
   int32_t keys = 0;

@@ -499,6 +499,13 @@ def test_backward_validation_and_launch(libs):
         calls = libs.llh_bwd_calls()
         assert call(**bad) == "LL_ERR_INVALID_ARG", bad
         assert libs.llh_bwd_calls() == calls
+    # the dK/dV kernel's 32-bit offsets: (n_q + 64) * H * D * 2 < 2^32 (H=3, D=64: 384 bytes a query)
+    n_max = (1 << 32) // 384 - 64
+    assert call(n_q=n_max) == "LL_OK"
+    calls = libs.llh_bwd_calls()
+    assert call(n_q=n_max + 1) == "LL_ERR_UNSUPPORTED" and b"4 GiB" in libs.ll_last_error()
+    assert libs.llh_bwd_calls() == calls
+    assert call(n_q=n_max + 1, n_cur=0, dk=None, dv=None, k=None, v=None) == "LL_OK"  # dQ alone
     libs.llh_fail_next_launch()
     assert call() == "LL_ERR_HIP"
     libs.ll_cache_destroy(h)
