@@ -27,21 +27,24 @@
 //                     registers), P = 2^(S^T - lse2) from the forward's
 //                     log-sum-exp, dS^T in fp32 rounded to bf16, then
 //                     dQ^T += K^T dS^T with K^T from gfx950 transpose reads.
-//                     It runs last: it overwrites the Q' copy in dq.
+//                     The K/V tiles stream straight into a 2-stage LDS ring
+//                     (LDS-DMA), one tile ahead.  It runs last: it
+//                     overwrites the Q' copy in dq.
 // Q' = bf16(Q * scale * log2 e) exactly as the forward kernel forms it, so P is
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
 //
 // Tiles sit in LDS in layouts (RowTile, VtTile) whose XOR swizzles or skewed
 // padding keep both the 16-byte row reads and the transpose reads free of
-// bank conflicts; the dQ kernel stages its tiles through registers.  In the dQ kernel V stays transposed ([D][64] per 64 keys,
-// as the bf16 cache stores it; the caller's row-major current chunk is
-// transposed while staged) and its rows are read back with transpose reads.
+// bank conflicts.  In the dQ kernel the cache's V stays transposed ([D][64]
+// per 64 keys, as the bf16 cache stores it) and its rows are read back with
+// transpose reads; the caller's row-major current chunk is read as rows.
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "launch.hpp"
 
@@ -56,7 +59,11 @@ typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned)))
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kBwdThreads = 512;  // 8 waves
-constexpr int kBwdBQ = 256;       // queries per dq workgroup (8 waves x 32)
+// Waves of 32 queries per dq workgroup.  (Four, i.e. two workgroups per CU
+// whose waves are not barrier-locked to each other, measured 4% slower for
+// the whole backward: each workgroup streams every K/V tile, so the LDS-DMA
+// traffic per flop doubles.)
+constexpr int kBwdDqWaves = 8;
 constexpr int kBwdBK = 256;       // current-chunk keys per dk/dv workgroup (8 waves x 32)
 constexpr int kTile = 64;         // keys (dq) or queries (dk/dv) per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -87,9 +94,9 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(u32x4 w, float c) {
   return __builtin_convertvector(f, bf16x8);
 }
 
-// Column p of a transposed V tile holds key p with bits 2 and 3 swapped (the
-// involution the forward kernel's PV operand order asks for).
-__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+// Column p of a transposed V tile of the cache holds key p with bits 2 and 3
+// swapped (the involution the forward kernel's PV operand order asks for);
+// the dQ kernel's transpose-read offsets undo it.
 
 // Row-major [kTile][D] bf16 LDS tile (K, Q' or dO), read both as rows
 // (16-byte reads, 16 consecutive rows at one granule) and by transpose reads
@@ -216,23 +223,90 @@ __device__ __forceinline__ void xcd_unit(int& head, int& tile) {
   tile = unit % nt;
 }
 
+// s_waitcnt vmcnt(N) (N <= 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations; LDS-DMA
+// loads stay in flight (their waits are explicit).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Stage of the dQ kernel's LDS ring: one K tile (RowTile rows) and one V tile,
+// either a transposed [D][64] tile (cache runs) or row-major rows in the K
+// tile's layout (the caller's current chunk).
+template <int D>
+struct DqStage {
+  static constexpr int kVBytes =
+      RowTile<D, true>::kBytes > VtTile<D>::kBytes ? RowTile<D, true>::kBytes : VtTile<D>::kBytes;
+  char k[RowTile<D, true>::kBytes];
+  char v[kVBytes];
+};
+
+// LDS-DMA load `ins` (1 KB: 64 lanes x 16 bytes) of a RowTile: slot
+// s = 64 ins + lane is LDS row s / G, slot s % G, which holds granule
+// slot ^ swz(row) (XOR layout, an involution) or slot - skew(row) (padded
+// layout; padding slots take a duplicate in-row granule and are never read)
+// of tile row `row`, i.e. source row row0 + row at byte stride rs.  Rows
+// past the buffer range load as zeros.
+template <int D, typename T>
+__device__ __forceinline__ void dma_rowtile(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t rs, uint32_t row0, int ins,
+                                            int lane) {
+  constexpr int G = T::RB / 16;
+  const int s = ins * 64 + lane;
+  const int row = s / G, sg = s % G;
+  int gran;
+  if constexpr (T::kSwz) gran = sg ^ T::swz(row);
+  else gran = min(max(sg - ((row >> 2) & 3), 0), D / 8 - 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + ins * 1024), 16,
+                                           (row0 + uint32_t(row)) * rs + uint32_t(gran) * 16, 0, 0, 0);
+}
+
+// LDS-DMA load `ins` of a transposed [D][64] V tile stored at byte offset
+// `tile` of the buffer: slot s is row d = s / 8, slot s % 8, holding granule
+// slot ^ (((d >> 1) & 1) << 2) (VtTile's layout, an involution).
+template <int D>
+__device__ __forceinline__ void dma_vttile(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t tile, int ins, int lane) {
+  const int s = ins * 64 + lane;
+  const int d = s >> 3, sg = s & 7;
+  const int gran = sg ^ (((d >> 1) & 1) << 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + ins * 1024), 16,
+                                           tile + uint32_t(d) * 128 + uint32_t(gran) * 16, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
+// W waves of 32 queries each.  Tiles reach LDS by LDS-DMA into a two-stage
+// ring, one tile ahead: the first W/2 waves load the K tile, the others the V
+// tile.  Each stage is its own __shared__ variable and the loops are unrolled
+// by two, so the compiler can tell the stage being filled from the stage
+// being read and inserts no wait for the fill before the reads.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
   using KT = RowTile<D, true>;
   using VT = VtTile<D>;
-  constexpr int NV = D / 8;        // 16-byte vectors per row
-  // two LDS buffers: tile t is read from one while tile t+1 is written to the other
-  __shared__ __attribute__((aligned(16))) char ks2[2][KT::kBytes];
-  __shared__ __attribute__((aligned(16))) char vs2[2][VT::kBytes];  // [d][column], column p = key vt_key(p)
+  constexpr int BQ = 32 * W;           // queries per workgroup
+  constexpr int HW = W / 2;            // waves per tile side
+  constexpr int NKL = (KT::RB / 16) / HW;  // 1 KB loads per wave: K tile, or row-major V rows
+  constexpr int NVL = (D / 8) / HW;        // 1 KB loads per wave: transposed V tile
+  static_assert((KT::RB / 16) % HW == 0 && (D / 8) % HW == 0, "tile loads split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) DqStage<D> st0;
+  __shared__ __attribute__((aligned(16))) DqStage<D> st1;
   const AttnArgs& a = p.a;
   int head, qtile;
   xcd_unit(head, qtile);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int qi = qtile * kBwdBQ + wave * 32 + r32;
+  const int qi = qtile * BQ + wave * 32 + r32;
   const bool q_ok = qi < a.n_q;
   const float c = a.scale * kLog2e;
   const int64_t qrow = (int64_t(qi) * a.H + head) * D;
@@ -261,13 +335,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
   int toff[2][D / 32];
   tr_offsets<D, KT>(lane, toff);
-  // V rows (A of dP^T: key 32*kb + r32, d = 16j + 8*half + 0..7) from the
+  // V rows (A of dP^T: key 32*kb + r32, d = 16j + 8*half + 0..7) from a
   // transposed tile by two transpose reads: the address lane (e = j16 >> 2,
   // m = j16 & 3) of a 16-lane group points at row d = 16j + 8*half + 4*aa + e,
   // at the column holding keys 32*kb + 16*(g16 & 1) + 4m .. +3, i.e. column
   // 32*kb + 16*(g16 & 1) + 4*swap(m) where swap exchanges m's two bits.  The
   // swizzle depends on (d >> 1) & 1 = (e >> 1) & 1 only, so 16j is a plain
-  // offset.
+  // offset.  (Row-major V rows are read like K rows.)
   int voff[2][2];
   {
     const int g16 = lane >> 4, j16 = lane & 15, m = j16 & 3;
@@ -280,109 +354,118 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(AttnBwdArgs p) {
       }
   }
 
-  // Loads of one 64-key tile, held in registers from issue to LDS write.
-  constexpr int NL = kTile * NV / kBwdThreads;  // 16-byte loads per thread per side
-  u32x4 kreg[NL], vreg[NL];
-  bool vt_reg = false;
-  auto issue = [&](int run, int t0) {
+  const int side = __builtin_amdgcn_readfirstlane(wave / HW);
+  const int wq = __builtin_amdgcn_readfirstlane(wave % HW);
+  // The loads of key tile (run, t0) into stage s.  Rows past the run's end
+  // lie past the end of its buffer range and load as zeros (their scores are
+  // masked below).
+  auto issue = [&](DqStage<D>& s, int run, int t0) __attribute__((always_inline)) {
     const KvSeg& sg = a.seg[run];
     const int len = sg.len;
     const uint32_t rs = uint32_t(sg.row_stride) * 2;
-    const auto rk = rsrc(static_cast<const char*>(sg.k) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
-    vt_reg = sg.v_tiled != 0;
-    const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
-    const auto rv = vt_reg ? rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2,
-                                  tiles * kTile * D * 2)
-                           : rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
-    const uint32_t tbase = uint32_t(t0 / kTile) * kTile * D * 2;
+    if (side == 0) {
+      const auto rk = rsrc(static_cast<const char*>(sg.k) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int it = tid + i * kBwdThreads;
-      const int row = it / NV, vec = it % NV;
-      // K rows (rows past the run read as zero)
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(t0 + row) * rs + vec * 16, 0, 0);
-      // V: a stored [D][64] tile (row d = it / 8, granule it % 8), or
-      // row-major rows with the key in the low bits of it (see stage)
-      vreg[i] = vt_reg ? __builtin_amdgcn_raw_buffer_load_b128(rv, tbase + (it >> 3) * 128 + (it & 7) * 16, 0, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b128(rv, uint32_t(t0 + it % kTile) * rs + it / kTile * 16, 0, 0);
-    }
-  };
-  auto stage = [&](char* kbuf, char* vbuf) {
+      for (int k = 0; k < NKL; ++k) dma_rowtile<D, KT>(rk, s.k, rs, uint32_t(t0), wq * NKL + k, lane);
+    } else if (sg.v_tiled) {
+      const uint32_t tiles = uint32_t(len + kTile - 1) / kTile;
+      const auto rv = rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.v_head_stride * 2, tiles * kTile * D * 2);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int it = tid + i * kBwdThreads;
-      const int row = it / NV, vec = it % NV;
-      *reinterpret_cast<u32x4*>(kbuf + KT::off(row, vec)) = kreg[i];
-      if (vt_reg) {  // columns already in vt_key order: copy
-        *reinterpret_cast<u32x4*>(vbuf + VT::off(it >> 3, it & 7)) = vreg[i];
-      } else {
-        // Row-major V (the current chunk): the 64 lanes of a wave hold the 64
-        // keys of one 16-byte column (dims 8*vv .. 8*vv+7), so each 2-byte
-        // store below fills one whole 128-byte row d of the transposed tile
-        // (key -> column vt_key(key)) without bank conflicts.
-        const bf16x8 b = __builtin_bit_cast(bf16x8, vreg[i]);
-        const int key = it % kTile, vv = it / kTile;
-        const int p = vt_key(key);
+      for (int k = 0; k < NVL; ++k) dma_vttile<D>(rv, s.v, uint32_t(t0) * D * 2, wq * NVL + k, lane);
+    } else {
+      const auto rv = rsrc(static_cast<const char*>(sg.v) + int64_t(head) * sg.head_stride * 2, uint32_t(len) * rs);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<__bf16*>(vbuf + VT::off(vv * 8 + e, p >> 3) + (p & 7) * 2) = b[e];
-      }
+      for (int k = 0; k < NKL; ++k) dma_rowtile<D, KT>(rv, s.v, rs, uint32_t(t0), wq * NKL + k, lane);
     }
   };
 
-  // Tiles in run order; runs are never empty.  Tile t is computed from
-  // buffer t & 1 while tile t+1's loads are in flight, then written to the
-  // other buffer; one barrier per tile.
-  int run = 0, t0 = 0;
-  issue(0, 0);
-  stage(ks2[0], vs2[0]);
-  __syncthreads();
-  for (int t = 0;; ++t) {
-    int nrun = run, nt0 = t0 + kTile;
-    if (nt0 >= a.seg[run].len) {
-      ++nrun;
-      nt0 = 0;
-    }
-    const bool has_next = nrun < a.n_seg;
-    if (has_next) issue(nrun, nt0);
-    const char* ks = ks2[t & 1];
-    const char* vs = vs2[t & 1];
-    const int valid = min(kTile, a.seg[run].len - t0);
+  // dQ^T += K^T dS^T for one key tile: V from a transposed tile (kVt) or
+  // row-major rows.
+  auto compute = [&](const DqStage<D>& s, int valid, auto vt_tag) __attribute__((always_inline)) {
+    constexpr bool kVt = decltype(vt_tag)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
+      f32x16 sc, dp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 ka = row_read<KT>(ks, kb * 32 + r32, 2 * j + half);
-        const char* vb = vs + j * 16 * VT::RB;
-        const bf16x8 va = __builtin_shufflevector(tr_read(vb + voff[kb][0]), tr_read(vb + voff[kb][1]), 0, 1, 2, 3, 4, 5, 6, 7);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], s, 0, 0, 0);
+        const bf16x8 ka = row_read<KT>(s.k, kb * 32 + r32, 2 * j + half);
+        bf16x8 va;
+        if constexpr (kVt) {
+          const char* vb = s.v + j * 16 * VT::RB;
+          va = __builtin_shufflevector(tr_read(vb + voff[kb][0]), tr_read(vb + voff[kb][1]), 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          va = row_read<KT>(s.v, kb * 32 + r32, 2 * j + half);
+        }
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
       }
       if (valid < kTile) {  // keys past the run's end: P = 0
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) s[e] = -INFINITY;
+          if (kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[e] = -INFINITY;
       }
       float ds[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(s[e] - lse2) * (dp[e] - dl);
+      for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(sc[e] - lse2) * (dp[e] - dl);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 b = pack8(ds, s2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, KT>(ks, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, KT>(s.k, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
       }
     }
-    if (has_next) stage(ks2[(t + 1) & 1], vs2[(t + 1) & 1]);
-    __syncthreads();
-    if (!has_next) break;
-    run = nrun;
-    t0 = nt0;
+  };
+
+  // Tiles in run order (runs are never empty); the runs with transposed V
+  // tiles (the cache's) come first, then the caller's row-major current
+  // chunk.  Step t: wait for this wave's loads of tile t (the only ones in
+  // flight), one barrier (every wave's tile t has landed and every wave is
+  // done with tile t-1), load tile t+1 into the other stage, compute tile t.
+  int n_vt = 0, n = 0;
+  for (int r = 0; r < a.n_seg; ++r) {
+    const int tl = (a.seg[r].len + kTile - 1) / kTile;
+    n += tl;
+    if (a.seg[r].v_tiled && n_vt == n - tl) n_vt = n;
   }
+  int run = 0, t0 = 0;    // tile being computed
+  int lrun = 0, lt0 = 0;  // next tile to load
+  auto advance = [&](int& r, int& t) __attribute__((always_inline)) {
+    t += kTile;
+    if (t >= a.seg[r].len) {
+      ++r;
+      t = 0;
+    }
+  };
+  issue(st0, 0, 0);
+  advance(lrun, lt0);
+  auto step = [&](const DqStage<D>& cur, DqStage<D>& nxt, auto vt_tag) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (lrun < a.n_seg) {
+      issue(nxt, lrun, lt0);
+      advance(lrun, lt0);
+    }
+    compute(cur, min(kTile, a.seg[run].len - t0), vt_tag);
+    advance(run, t0);
+  };
+  auto loop = [&](int tb, int te, auto vt_tag) __attribute__((always_inline)) {
+    int t = tb;
+    if (t < te && (t & 1)) {
+      step(st1, st0, vt_tag);
+      ++t;
+    }
+    for (; t + 1 < te; t += 2) {
+      step(st0, st1, vt_tag);
+      step(st1, st0, vt_tag);
+    }
+    if (t < te) step(st0, st1, vt_tag);
+  };
+  loop(0, n_vt, std::true_type{});
+  loop(n_vt, n, std::false_type{});
+
   if (!q_ok) return;
   float* out = p.dq + qrow;
 #pragma unroll
@@ -409,23 +492,6 @@ struct DkvStage {
   float lse[kTile];
   float dl[kTile];
 };
-
-// s_waitcnt vmcnt(N) (N <= 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 15, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-  __asm__ __volatile__("" ::: "memory");
-}
-
-// Workgroup barrier that waits only for this wave's LDS operations; LDS-DMA
-// loads stay in flight (their waits are explicit).
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
 
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
@@ -482,7 +548,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   const __amdgpu_buffer_rsrc_t rvec = rsrc(side ? static_cast<const void*>(p.delta + int64_t(head) * a.n_q)
                                                 : static_cast<const void*>(p.lse + int64_t(head) * a.n_q),
                                            uint32_t(a.n_q) * 4);
-  auto issue = [&](DkvStage<D>& s, int t) {
+  auto issue = [&](DkvStage<D>& s, int t) __attribute__((always_inline)) {
     // The lane's slot addresses are recomputed per tile from an opaque copy of
     // the lane id, so the compiler does not keep them in registers across the
     // loop (the MFMA accumulators and K/V fragments fill the register file).
@@ -503,7 +569,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
                                                4, uint32_t(t * kTile + ln) * 4, 0, 0, 0);
   };
 
-  auto compute = [&](const DkvStage<D>& s) {
+  auto compute = [&](const DkvStage<D>& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 sc, dp;
@@ -552,7 +618,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   const int nt = (a.n_q + kTile - 1) / kTile;
   issue(st0, 0);
   if (nt > 1) issue(st1, 1);
-  auto step = [&](const DkvStage<D>& cur_st, DkvStage<D>& next2, int t) {
+  auto step = [&](const DkvStage<D>& cur_st, DkvStage<D>& next2, int t) __attribute__((always_inline)) {
     if (t + 1 < nt) {
       if (wq == 0) wait_vmcnt<NI + 1>();
       else wait_vmcnt<NI>();
@@ -603,7 +669,8 @@ int launch_bwd_d(const AttnBwdArgs& p, void* stream) {
     err = launch(bwd_dkv_kernel<D>, dim3((len + kBwdBK - 1) / kBwdBK, a.H), dim3(kBwdThreads), &p, stream);
     if (err) return err;
   }
-  return launch(bwd_dq_kernel<D>, dim3((a.n_q + kBwdBQ - 1) / kBwdBQ, a.H), dim3(kBwdThreads), &p, stream);
+  constexpr int W = kBwdDqWaves;
+  return launch(bwd_dq_kernel<D, W>, dim3((a.n_q + 32 * W - 1) / (32 * W), a.H), dim3(64 * W), &p, stream);
 }
 
 }  // namespace
