@@ -72,9 +72,11 @@ ll_status make_geometry(const ll_cache_config* cfg, Geometry* g) {
                                     "sink chunks + ring slots must be <= " + std::to_string(kMaxKeyRuns - 1));
   if (r.vt && r.vt_head_elems > lim) return fail(LL_ERR_UNSUPPORTED, "cache too large for 32-bit indexing");
   // The kernels address a token-major chunk ([ctok][H][D] activations) with
-  // one 32-bit buffer range.
-  if (r.ctok * r.H * r.D * int64_t(dtype_bytes(r.act)) >= (int64_t(1) << 32))
-    return fail(LL_ERR_UNSUPPORTED, "a chunk of activations must be smaller than 4 GiB");
+  // one 32-bit buffer range, whose byte offsets they form for whole 64-token
+  // tiles: rows past the chunk's end must not wrap around into the range.
+  if ((r.ctok + kVtTileKeys) * r.H * r.D * int64_t(dtype_bytes(r.act)) >= (int64_t(1) << 32))
+    return fail(LL_ERR_UNSUPPORTED, "a chunk of activations, rounded up to whole 64-token tiles, must be smaller "
+                                    "than 4 GiB");
   *g = r;
   return LL_OK;
 }

@@ -602,8 +602,10 @@ ll_status ll_cross_attn(const void* q, int64_t n_q, const void* k_txt, const voi
   if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (dtype != LL_F32 && dtype != LL_BF16) return fail(LL_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
   if (n_txt < 1 || n_txt > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_txt must be in [1, 2^30)");
-  if (n_txt * num_heads * int64_t(head_dim) * ll::dtype_bytes(dtype) >= (int64_t(1) << 32))
-    return fail(LL_ERR_UNSUPPORTED, "text K/V must be smaller than 4 GiB each");
+  // 32-bit byte offsets are formed for whole 64-key tiles: rows past the end
+  // must not wrap around into the buffer range.
+  if ((n_txt + 64) * num_heads * int64_t(head_dim) * ll::dtype_bytes(dtype) >= (int64_t(1) << 32))
+    return fail(LL_ERR_UNSUPPORTED, "text K/V, rounded up to whole 64-key tiles, must be smaller than 4 GiB each");
   if (n_q < 0 || n_q > INT32_MAX / 2) return fail(LL_ERR_INVALID_ARG, "n_q out of range");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LL_ERR_INVALID_ARG, "scale must be finite and > 0");
   ll_status st;

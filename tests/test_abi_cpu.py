@@ -619,6 +619,11 @@ def test_attention_and_cross_attention_errors(libs):
     assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 2, 80, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_UNSUPPORTED"
     assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 2, 64, ll.LL_I8, 0.1, A, None, None)) == "LL_ERR_UNSUPPORTED"
     assert ok(libs.ll_cross_attn(A, 5, A, A, 3, 0, 64, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_INVALID_ARG"
+    # text K/V rows are addressed in whole 64-key tiles with 32-bit byte offsets: (n_txt + 64) * 256 < 2^32
+    n_max = (1 << 24) - 65
+    assert libs.ll_cross_attn(A, 5, A, A, n_max, 2, 64, ll.LL_BF16, 0.1, A, None, None) == 0
+    assert ok(libs.ll_cross_attn(A, 5, A, A, n_max + 1, 2, 64, ll.LL_BF16, 0.1, A, None, None)) == "LL_ERR_UNSUPPORTED"
+    assert b"4 GiB" in libs.ll_last_error()
     assert libs.ll_cross_attn(A, 5, A, A, 3, 2, 64, ll.LL_BF16, 0.1, A, A, None) == 0
     nk = ctypes.c_int64()
     runs = (ctypes.c_int64 * (RUN_FIELDS * 40))()
@@ -776,6 +781,21 @@ def test_geometry_32bit_bounds(libs, kw, ok):
     else:
         assert status(libs, st) == "LL_ERR_UNSUPPORTED"
         assert b"32-bit" in libs.ll_last_error()
+
+
+@pytest.mark.parametrize("H,ok", [(258111, True), (258112, False)])
+def test_chunk_tile_range_bound(libs, H, ok):
+    """A chunk of activations is addressed in whole 64-token tiles with 32-bit
+    byte offsets: (C_tok + 64) * H * D * 2 must stay below 4 GiB (C_tok = 1,
+    D = 128: 65 * 256 bytes a head)."""
+    c = cfg(L=1, T=1, C=1, S=0, W=2, H=H, D=128)
+    n = ctypes.c_size_t(0)
+    st = libs.ll_cache_required_bytes(ctypes.byref(c), ctypes.byref(n))
+    assert (65 * H * 256 < 1 << 32) == ok
+    if ok:
+        assert st == 0, libs.ll_last_error()
+    else:
+        assert status(libs, st) == "LL_ERR_UNSUPPORTED" and b"4 GiB" in libs.ll_last_error()
 
 
 def test_noalloc_backward_validation_and_launch(libs):
