@@ -531,20 +531,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   int toff[2][D / 32];
   tr_offsets<D, QT>(lane, toff);
 
-  // Tile loads, straight into LDS.  Waves 0-3 fill the Q' side (the delta
-  // kernel's bf16(Q c) copy at the start of dq), waves 4-7 the dO side; wave
-  // 0 also loads the tile's lse and wave 4 its delta.  Slot s of a side (one
-  // lane of instruction s / 64) is LDS row s / G, slot s % G, which holds
-  // granule (s % G) - skew(row) of that query row; the padding slots take a
-  // duplicate of an in-row granule and are never read.  Query rows past n_q
-  // lie past the end of every buffer range and load as zeros: Q' = dO = 0
-  // and lse = delta = 0 give P = 1 and dS = 0, and a zero dO row, so those
-  // rows add nothing to dK or dV.
+  // Tile loads, straight into LDS (dma_rowtile).  Waves 0-3 fill the Q' side
+  // (the delta kernel's bf16(Q c) copy at the start of dq), waves 4-7 the dO
+  // side; wave 0 also loads the tile's lse and wave 4 its delta.  Query rows
+  // past n_q lie past the end of every buffer range and load as zeros:
+  // Q' = dO = 0 and lse = delta = 0 give P = 1 and dS = 0, and a zero dO
+  // row, so those rows add nothing to dK or dV.
   const int side = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
   const uint32_t row_bytes = uint32_t(a.H) * D * 2;  // one query's row of all heads
-  const uint32_t side_bytes = uint32_t(a.n_q) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rside = rsrc(side ? p.dout : static_cast<const void*>(p.dq), side_bytes);
+  const uint32_t head_off = uint32_t(head) * D * 2;
+  const __amdgpu_buffer_rsrc_t rside =
+      rsrc(static_cast<const char*>(side ? p.dout : static_cast<const void*>(p.dq)) + head_off,
+           uint32_t(a.n_q) * row_bytes - head_off);
   const __amdgpu_buffer_rsrc_t rvec = rsrc(side ? static_cast<const void*>(p.delta + int64_t(head) * a.n_q)
                                                 : static_cast<const void*>(p.lse + int64_t(head) * a.n_q),
                                            uint32_t(a.n_q) * 4);
@@ -554,16 +553,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
     // loop (the MFMA accumulators and K/V fragments fill the register file).
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));
-    const uint32_t t0 = uint32_t(t) * kTile * row_bytes + uint32_t(head) * (D * 2);
     char* dst = side ? s.g : s.q;
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int sl = (wq * NI + k) * 64 + ln;
-      const int row = sl / G;
-      const int gran = min(max(sl % G - ((row >> 2) & 3), 0), D / 8 - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rside, (__attribute__((address_space(3))) void*)(dst + (wq * NI + k) * 1024),
-                                               16, t0 + uint32_t(row) * row_bytes + uint32_t(gran) * 16, 0, 0, 0);
-    }
+    for (int k = 0; k < NI; ++k) dma_rowtile<D, QT>(rside, dst, row_bytes, uint32_t(t) * kTile, wq * NI + k, ln);
     if (wq == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rvec, (__attribute__((address_space(3))) void*)(side ? s.dl : s.lse),
                                                4, uint32_t(t * kTile + ln) * 4, 0, 0, 0);
