@@ -68,10 +68,14 @@ def run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=True, rows=None, int8=Fals
         f"{'' if with_cur else ' (cache only)'}")
     kc, vc = (dk_, dv_) if with_cur else (None, None)
     cache.attn(0, dq_, kc, vc, scale, out, lse)
-    delta = torch.empty((H, ct), dtype=torch.float32, device="cuda")
-    gq = torch.empty((ct, H, D), dtype=torch.float32, device="cuda")
-    gk = torch.empty((ct, H, D), dtype=torch.float32, device="cuda") if with_cur else None
-    gv = torch.empty((ct, H, D), dtype=torch.float32, device="cuda") if with_cur else None
+    # The workspace and the gradient buffers start as NaN: every element the
+    # call must write is checked finite, and the Q' copy the call keeps in dq
+    # before the dQ kernel overwrites it must not survive anywhere.
+    nan = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    delta = nan(H, ct)
+    gq = nan(ct, H, D)
+    gk = nan(ct, H, D) if with_cur else None
+    gv = nan(ct, H, D) if with_cur else None
     cache.attn_bwd(0, dq_, kc, vc, scale, out, lse, ddo, delta, gq, gk, gv)
     torch.cuda.synchronize()
     hk, hv = hist.keys(k, v) if with_cur else hist.keys()
