@@ -55,6 +55,7 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -305,53 +306,88 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
   int head, qtile;
   xcd_unit(head, qtile);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int qi = qtile * BQ + wave * 32 + r32;
-  const bool q_ok = qi < a.n_q;
+  const int lane = tid & 63, wave = tid >> 6;
+  // MFMA 16x16x32 lane roles: r16 = lane % 16 is the query column of each
+  // 16-query block (and the row of an A operand), g = lane / 16 the 8-wide
+  // slice of the contraction and the 4-row slice of the result.
+  const int r16 = lane & 15, g = lane >> 4;
   const float c = a.scale * kLog2e;
-  const int64_t qrow = (int64_t(qi) * a.H + head) * D;
 
-  // B operands: Q' and dO of the lane's query, d = 16j + 8*half .. +7.
-  bf16x8 qf[D / 16], dof[D / 16];
-  {
+  // B operands: Q' and dO of query 16 qb + r16 of the wave's 32, d = 32 ks + 8 g .. +7.
+  int qi[2];
+  bool q_ok[2];
+  bf16x8 qf[2][D / 32], dof[2][D / 32];
+  float lse2[2], dl[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    qi[qb] = qtile * BQ + wave * 32 + 16 * qb + r16;
+    q_ok[qb] = qi[qb] < a.n_q;
+    const int64_t qrow = (int64_t(qi[qb]) * a.H + head) * D;
     const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.q) + qrow);
-    const u32x4* g = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.dout) + qrow);
+    const u32x4* gp = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.dout) + qrow);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const u32x4 wq = q_ok ? q[2 * j + half] : u32x4{0, 0, 0, 0};
-      const u32x4 wg = q_ok ? g[2 * j + half] : u32x4{0, 0, 0, 0};
-      qf[j] = scale_bf16x8(wq, c);
-      dof[j] = __builtin_bit_cast(bf16x8, wg);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const u32x4 wq = q_ok[qb] ? q[4 * ks + g] : u32x4{0, 0, 0, 0};
+      const u32x4 wg = q_ok[qb] ? gp[4 * ks + g] : u32x4{0, 0, 0, 0};
+      qf[qb][ks] = scale_bf16x8(wq, c);
+      dof[qb][ks] = __builtin_bit_cast(bf16x8, wg);
     }
+    // log2-domain log-sum-exp; +inf for padding queries makes their P exactly 0
+    lse2[qb] = q_ok[qb] ? p.lse[int64_t(head) * a.n_q + qi[qb]] * kLog2e : INFINITY;
+    dl[qb] = q_ok[qb] ? p.delta[int64_t(head) * a.n_q + qi[qb]] : 0.f;
   }
-  // log2-domain log-sum-exp; +inf for padding lanes makes their P exactly 0
-  const float lse2 = q_ok ? p.lse[int64_t(head) * a.n_q + qi] * kLog2e : INFINITY;
-  const float dl = q_ok ? p.delta[int64_t(head) * a.n_q + qi] : 0.f;
 
-  f32x16 dq[D / 32];
+  f32x4 sinit[2], dinit[2];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
-  int toff[2][D / 32];
-  tr_offsets<D, KT>(lane, toff);
-  // V rows (A of dP^T: key 32*kb + r32, d = 16j + 8*half + 0..7) from a
-  // transposed tile by two transpose reads: the address lane (e = j16 >> 2,
-  // m = j16 & 3) of a 16-lane group points at row d = 16j + 8*half + 4*aa + e,
-  // at the column holding keys 32*kb + 16*(g16 & 1) + 4m .. +3, i.e. column
-  // 32*kb + 16*(g16 & 1) + 4*swap(m) where swap exchanges m's two bits.  The
-  // swizzle depends on (d >> 1) & 1 = (e >> 1) & 1 only, so 16j is a plain
-  // offset.  (Row-major V rows are read like K rows.)
-  int voff[2][2];
-  {
-    const int g16 = lane >> 4, j16 = lane & 15, m = j16 & 3;
+    for (int r = 0; r < 4; ++r) {
+      sinit[qb][r] = -lse2[qb];
+      dinit[qb][r] = -dl[qb];
+    }
+
+  // dQ^T accumulators: element i of lane (r16, g) in block (db, qb) is
+  // dimension 16 db + 4 g + i of query 16 qb + r16.
+  f32x4 dq[D / 16][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        const int col = 32 * kb + 16 * (g16 & 1) + 4 * (((m & 1) << 1) | (m >> 1));
-        voff[kb][aa] = VT::off(8 * (g16 >> 1) + 4 * aa + (j16 >> 2), col >> 3) + (col & 7) * 2;
-      }
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dq[db][qb][r] = 0.f;
+  // Byte offsets of this lane's LDS operand reads.  Both tile layouts depend
+  // on the row mod 16 only, so the key block (16 rows), the upper half of a
+  // key step (16 rows) and the key step (32 rows) are plain offsets.
+  //  * K rows (A of S^T) and row-major V rows (A of dP^T): key 16 kb + r16,
+  //    granule 4 ks + g.
+  int koff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) koff[ks] = KT::off(r16, 4 * ks + g);
+  //  * K^T (A of dQ^T) by two transpose reads: the address lane (e = r16 >> 2,
+  //    m = r16 & 3) of group g points at key row 4 g + e (+16 for the second
+  //    read) at dimensions 16 db + 4 m .. +3, so lane r16 receives dimension
+  //    16 db + r16 of keys 4 g .. 4 g + 3 (and 16 + 4 g .. 16 + 4 g + 3): the
+  //    key order in which the S^T accumulators of the step's two key blocks
+  //    pack into the dS^T operand.
+  int ktoff[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const int col = 16 * db + 4 * (r16 & 3);
+    ktoff[db] = KT::off(4 * g + (r16 >> 2), col >> 3) + (col & 7) * 2;
+  }
+  //  * V rows from a transposed [D][64] tile (A of dP^T) by two transpose
+  //    reads: the address lane (e, m) of group g points at dimension row
+  //    8 g + e (+4 for the second read, +32 per ks) at the columns holding
+  //    keys 16 kb + 4 m .. +3, i.e. columns 16 kb + 4 swap(m), where swap
+  //    exchanges m's two bits (the cache's column order); lane r16 receives
+  //    key 16 kb + r16 at four consecutive dimensions.  The tile's swizzle
+  //    depends on (d >> 1) & 1 = (e >> 1) & 1 only.
+  int vtoff[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int m = r16 & 3;
+    const int col = 16 * kb + 4 * (((m & 1) << 1) | (m >> 1));
+    vtoff[kb] = VT::off(8 * g + (r16 >> 2), col >> 3) + (col & 7) * 2;
   }
 
   const int side = __builtin_amdgcn_readfirstlane(wave / HW);
@@ -379,42 +415,72 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
     }
   };
 
-  // dQ^T += K^T dS^T for one key tile: V from a transposed tile (kVt) or
-  // row-major rows.
+  // dQ^T += K^T dS^T for one key tile, one 32-key step at a time: S^T and
+  // dP^T of the step's two 16-key blocks (MFMA 16x16x32, each A read serving
+  // both query blocks), dS^T = P (dP^T - delta) in fp32, packed to bf16 as the
+  // B operand of dQ^T.  V comes from a transposed tile (kVt) or row-major rows.
   auto compute = [&](const DqStage<D>& s, int valid, auto vt_tag) __attribute__((always_inline)) {
     constexpr bool kVt = decltype(vt_tag)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sc, dp;
+    for (int kst = 0; kst < 2; ++kst) {
+      // The accumulators start at -lse2 and -delta of their query, so S^T
+      // comes out as the log2 P and dP^T as dP - delta.
+      f32x4 sc[2][2], dp[2][2];  // [key block of the step][query block]
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 ka = row_read<KT>(s.k, kb * 32 + r32, 2 * j + half);
-        bf16x8 va;
-        if constexpr (kVt) {
-          const char* vb = s.v + j * 16 * VT::RB;
-          va = __builtin_shufflevector(tr_read(vb + voff[kb][0]), tr_read(vb + voff[kb][1]), 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          va = row_read<KT>(s.v, kb * 32 + r32, 2 * j + half);
+        for (int qb = 0; qb < 2; ++qb) {
+          sc[kk][qb] = sinit[qb];
+          dp[kk][qb] = dinit[qb];
         }
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[j], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[j], dp, 0, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int kb = 2 * kst + kk;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(s.k + 16 * kb * KT::RB + koff[ks]);
+          bf16x8 va;
+          if constexpr (kVt) {
+            const char* vb = s.v + (32 * ks) * VT::RB + vtoff[kb];
+            va = __builtin_shufflevector(tr_read(vb), tr_read(vb + 4 * VT::RB), 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            va = *reinterpret_cast<const bf16x8*>(s.v + 16 * kb * KT::RB + koff[ks]);
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sc[kk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][ks], sc[kk][qb], 0, 0, 0);
+            dp[kk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, dof[qb][ks], dp[kk][qb], 0, 0, 0);
+          }
+        }
       }
+      // element i of lane (r16, g) in block (kk, qb): key 32 kst + 16 kk + 4 g + i
       if (valid < kTile) {  // keys past the run's end: P = 0
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[e] = -INFINITY;
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              if (32 * kst + 16 * kk + 4 * g + i >= valid) sc[kk][qb][i] = -INFINITY;
       }
-      float ds[16];
+      bf16x8 bds[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(sc[e] - lse2) * (dp[e] - dl);
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x8 f;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 b = pack8(ds, s2);
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, KT>(s.k, 2 * kb + s2, toff, db), b, dq[db], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            f[4 * kk + i] = __builtin_amdgcn_exp2f(sc[kk][qb][i]) * dp[kk][qb][i];
+        bds[qb] = __builtin_convertvector(f, bf16x8);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const char* kt = s.k + (32 * kst) * KT::RB + ktoff[db];
+        const bf16x8 ka = __builtin_shufflevector(tr_read(kt), tr_read(kt + 16 * KT::RB), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          dq[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bds[qb], dq[db][qb], 0, 0, 0);
       }
     }
   };
@@ -466,16 +532,16 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
   loop(0, n_vt, std::true_type{});
   loop(n_vt, n, std::false_type{});
 
-  if (!q_ok) return;
-  float* out = p.dq + qrow;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!q_ok[qb]) continue;
+    float* out = p.dq + (int64_t(qi[qb]) * a.H + head) * D;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d0 = db * 32 + 8 * gq + 4 * half;
-      *reinterpret_cast<float4*>(out + d0) = make_float4(dq[db][4 * gq] * a.scale, dq[db][4 * gq + 1] * a.scale,
-                                                         dq[db][4 * gq + 2] * a.scale, dq[db][4 * gq + 3] * a.scale);
-    }
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<float4*>(out + 16 * db + 4 * g) =
+          make_float4(dq[db][qb][0] * a.scale, dq[db][qb][1] * a.scale, dq[db][qb][2] * a.scale,
+                      dq[db][qb][3] * a.scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
