@@ -15,21 +15,25 @@
 // Three kernels on the stream:
 //   bwd_delta_kernel  delta[h][i] = dO_i . O_i (fp32); when dK/dV are asked
 //                     for, also Q' (below) as bf16 into the first half of dq.
-//   bwd_dkv_kernel    per 256 keys of the current chunk: loop over 64-query
-//                     tiles; S = Q' K^T, dP = dO V^T (K/V fragments in
-//                     registers), then dV^T += dO^T P and dK^T += Q'^T dS with
-//                     dO^T and Q'^T from transpose reads.  The Q' and dO
-//                     tiles stream straight into a 3-stage LDS ring (LDS-DMA),
-//                     two tiles ahead.
+//   bwd_dkv_kernel    per 256 keys of the current chunk (8 waves x 32):
+//                     loop over 64-query tiles; S = Q' K^T, dP = dO V^T (K/V
+//                     fragments in registers), then dV^T += dO^T P and
+//                     dK^T += Q'^T dS with dO^T and Q'^T from transpose reads.
+//                     The Q' and dO tiles stream straight into a 3-stage LDS
+//                     ring (LDS-DMA), two tiles ahead.
 //   bwd_dq_kernel     per 256 queries of one head (8 waves x 32): walk every
 //                     64-key tile of every run; S^T = K Q'^T and dP^T = V dO^T
-//                     (bf16 MFMA 32x32x16, K/V rows from LDS, Q' and dO in
-//                     registers), P = 2^(S^T - lse2) from the forward's
+//                     (K/V rows from LDS, Q' and dO in registers), starting
+//                     from -lse2 and -delta, P = 2^(S^T) from the forward's
 //                     log-sum-exp, dS^T in fp32 rounded to bf16, then
 //                     dQ^T += K^T dS^T with K^T from gfx950 transpose reads.
 //                     The K/V tiles stream straight into a 2-stage LDS ring
 //                     (LDS-DMA), one tile ahead.  It runs last: it
 //                     overwrites the Q' copy in dq.
+// Both MFMA kernels use bf16 MFMA 16x16x32 with two 16-row blocks per wave
+// sharing every LDS operand read; the accumulators of the two 16-row blocks
+// of a 32-row step pack into the B operand of the next product, and the
+// transpose reads that form its A operand take rows in that same order.
 // Q' = bf16(Q * scale * log2 e) exactly as the forward kernel forms it, so P is
 // recomputed from the same rounded scores the forward normalised.  Gradients
 // are written in fp32 (token-major [n][H][D]).
@@ -132,48 +136,10 @@ struct VtTile {
   static __device__ __forceinline__ int off(int d, int gran) { return d * RB + ((gran ^ (((d >> 1) & 1) << 2)) << 4); }
 };
 
-// Byte offsets (within a RowTile) of the two transpose
-// reads that give lane (r32, half) the A operand of a 32x32x16 MFMA whose
-// rows are the tile's columns 32*db + r32 and whose 16 k values are tile rows
-// 16*step + {0..3, 8..11} (half 0) or {4..7, 12..15} (half 1): the row order
-// in which the C accumulator of the previous MFMA packs into a B operand.
-// (The swizzle depends on row mod 16 only, so the offsets of rows 0..15 serve
-// every 16-row step.)
-template <int D, typename T>
-__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
-  const int g16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-  for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int row = 8 * aa + 4 * (g16 >> 1) + (j16 >> 2);
-      const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
-      if constexpr (T::kSwz) off[aa][db] = T::off(row, col >> 3) + (col & 7) * 2;
-      else off[aa][db] = row * T::RB + (((col >> 3) + ((row >> 2) & 3)) << 4) + (col & 7) * 2;
-    }
-}
-
-// 16-byte read of granule gran of row `row` of a RowTile.
-template <typename T>
-__device__ __forceinline__ bf16x8 row_read(const char* tile, int row, int gran) {
-  return *reinterpret_cast<const bf16x8*>(tile + T::off(row, gran));
-}
-
-template <int D, typename T>
-__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int step, const int (&off)[2][D / 32], int db) {
-  constexpr int RB = T::RB;
-  const char* base = tile + 16 * step * RB;
-  const bf16x4 lo = tr_read(base + off[0][db]);
-  const bf16x4 hi = tr_read(base + off[1][db]);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Pack C accumulator elements 8*s2 .. 8*s2+7 (scaled) as one bf16 B operand.
-__device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int s2) {
-  f32x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = x[8 * s2 + e];
-  return __builtin_convertvector(f, bf16x8);
+// The A operand of an MFMA 16x16x32 (8 bf16 per lane) from two transpose
+// reads, at `lo` and `hi_off` bytes further on.
+__device__ __forceinline__ bf16x8 tr_pair(const char* lo, int hi_off) {
+  return __builtin_shufflevector(tr_read(lo), tr_read(lo + hi_off), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -441,8 +407,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(s.k + 16 * kb * KT::RB + koff[ks]);
           bf16x8 va;
           if constexpr (kVt) {
-            const char* vb = s.v + (32 * ks) * VT::RB + vtoff[kb];
-            va = __builtin_shufflevector(tr_read(vb), tr_read(vb + 4 * VT::RB), 0, 1, 2, 3, 4, 5, 6, 7);
+            va = tr_pair(s.v + (32 * ks) * VT::RB + vtoff[kb], 4 * VT::RB);
           } else {
             va = *reinterpret_cast<const bf16x8*>(s.v + 16 * kb * KT::RB + koff[ks]);
           }
@@ -476,8 +441,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
       }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const char* kt = s.k + (32 * kst) * KT::RB + ktoff[db];
-        const bf16x8 ka = __builtin_shufflevector(tr_read(kt), tr_read(kt + 16 * KT::RB), 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 ka = tr_pair(s.k + (32 * kst) * KT::RB + ktoff[db], 16 * KT::RB);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           dq[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bds[qb], dq[db][qb], 0, 0, 0);
@@ -573,29 +537,57 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   int head, ktile;
   xcd_unit(head, ktile);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, r32 = lane & 31, half = lane >> 5;
-  const int key = ktile * kBwdBK + wave * 32 + r32;
-  const bool k_ok = key < cur.len;
+  const int lane = tid & 63, wave = tid >> 6;
+  // MFMA 16x16x32 lane roles: r16 = lane % 16 is the key column of each
+  // 16-key block (and the row of an A operand), g = lane / 16 the 8-wide
+  // slice of the contraction and the 4-row slice of the result.
+  const int r16 = lane & 15, g = lane >> 4;
 
-  // B operands: K and V of the lane's key, d = 16j + 8*half .. +7.
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const int64_t off = int64_t(key) * cur.row_stride + int64_t(head) * cur.head_stride;
+  // B operands: K and V of key 16 kb + r16 of the wave's 32, d = 32 ks + 8 g .. +7.
+  int key[2];
+  bool k_ok[2];
+  bf16x8 kf[2][D / 32], vf[2][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    key[kb] = ktile * kBwdBK + wave * 32 + 16 * kb + r16;
+    k_ok[kb] = key[kb] < cur.len;
+    const int64_t off = int64_t(key[kb]) * cur.row_stride + int64_t(head) * cur.head_stride;
     const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(cur.k) + off);
     const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(cur.v) + off);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      kf[j] = __builtin_bit_cast(bf16x8, k_ok ? kp[2 * j + half] : u32x4{0, 0, 0, 0});
-      vf[j] = __builtin_bit_cast(bf16x8, k_ok ? vp[2 * j + half] : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 32; ++ks) {
+      kf[kb][ks] = __builtin_bit_cast(bf16x8, k_ok[kb] ? kp[4 * ks + g] : u32x4{0, 0, 0, 0});
+      vf[kb][ks] = __builtin_bit_cast(bf16x8, k_ok[kb] ? vp[4 * ks + g] : u32x4{0, 0, 0, 0});
     }
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  // dK^T and dV^T accumulators: element i of lane (r16, g) in block (db, kb)
+  // is dimension 16 db + 4 g + i of key 16 kb + r16.
+  f32x4 dk[D / 16][2], dv[D / 16][2];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
-  int toff[2][D / 32];
-  tr_offsets<D, QT>(lane, toff);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[db][kb][r] = dv[db][kb][r] = 0.f;
+  // Byte offsets of this lane's LDS operand reads (the padded, skewed layout
+  // depends on the row mod 16 only, so query blocks and steps are plain
+  // offsets):
+  //  * Q' and dO rows (A of S and dP): query 16 qb + r16, granule 4 ks + g;
+  //  * dO^T and Q'^T (A of dV^T and dK^T) by two transpose reads: the address
+  //    lane (e = r16 >> 2, m = r16 & 3) of group g points at query row
+  //    4 g + e (+16 for the second read, +32 per query step) at dimensions
+  //    16 db + 4 m .. +3, so lane r16 receives dimension 16 db + r16 of
+  //    queries 4 g .. 4 g + 3 (and 16 + 4 g ..): the query order in which the
+  //    S and dS accumulators of the step's two query blocks pack into the
+  //    P and dS operands.
+  int qoff[D / 32], toff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qoff[ks] = QT::off(r16, 4 * ks + g);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const int col = 16 * db + 4 * (r16 & 3);
+    toff[db] = QT::off(4 * g + (r16 >> 2), col >> 3) + (col & 7) * 2;
+  }
 
   // Tile loads, straight into LDS (dma_rowtile).  Waves 0-3 fill the Q' side
   // (the delta kernel's bf16(Q c) copy at the start of dq), waves 4-7 the dO
@@ -627,43 +619,68 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
                                                4, uint32_t(t * kTile + ln) * 4, 0, 0, 0);
   };
 
+  // One 64-query tile, one 32-query step at a time: S and dP of the step's
+  // two 16-query blocks (MFMA 16x16x32, each A read serving both key blocks),
+  // P = 2^(S - lse2) and dS = P (dP - delta) in fp32, packed to bf16 as the
+  // B operands of dV^T += dO^T P and dK^T += Q'^T dS.
   auto compute = [&](const DkvStage<D>& s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sc, dp;
+    for (int qs = 0; qs < 2; ++qs) {
+      f32x4 sc[2][2], dp[2][2];  // [query block of the step][key block]
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-        const bf16x8 qa = row_read<QT>(s.q, qb * 32 + r32, 2 * j + half);
-        const bf16x8 ga = row_read<QT>(s.g, qb * 32 + r32, 2 * j + half);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[j], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[j], dp, 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[qq][kb][r] = dp[qq][kb][r] = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int row0 = 16 * (2 * qs + qq) * QT::RB;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(s.q + row0 + qoff[ks]);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(s.g + row0 + qoff[ks]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sc[qq][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kb][ks], sc[qq][kb], 0, 0, 0);
+            dp[qq][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[kb][ks], dp[qq][kb], 0, 0, 0);
+          }
+        }
       }
-      // rows of the accumulators: queries qb*32 + 8*(e >> 2) + 4*half + (e & 3)
-      float pr[16], ds[16];
+      // element i of lane (r16, g) in block (qq, kb): query 32 qs + 16 qq + 4 g + i
+      bf16x8 pb[2], db8[2];
+      {
+        f32x8 pf[2], df[2];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int q4 = qb * 32 + 8 * g4 + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(&s.lse[q4]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[q4]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int qq = 0; qq < 2; ++qq) {
+          const int q4 = 32 * qs + 16 * qq + 4 * g;
+          const float4 l4 = *reinterpret_cast<const float4*>(&s.lse[q4]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[q4]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g4 + i;
-          pr[e] = __builtin_amdgcn_exp2f(fmaf(-lv[i], kLog2e, sc[e]));  // scores are in log2 units
-          ds[e] = pr[e] * (dp[e] - dv4[i]);
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pr = __builtin_amdgcn_exp2f(fmaf(-lv[i], kLog2e, sc[qq][kb][i]));  // log2 units
+              pf[kb][4 * qq + i] = pr;
+              df[kb][4 * qq + i] = pr * (dp[qq][kb][i] - dv4[i]);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          pb[kb] = __builtin_convertvector(pf[kb], bf16x8);
+          db8[kb] = __builtin_convertvector(df[kb], bf16x8);
         }
       }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pb = pack8(pr, s2);
-        const bf16x8 db8 = pack8(ds, s2);
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 ga = tr_pair(s.g + (32 * qs) * QT::RB + toff[db], 16 * QT::RB);
+        const bf16x8 qa = tr_pair(s.q + (32 * qs) * QT::RB + toff[db], 16 * QT::RB);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(s.g, 2 * qb + s2, toff, db), pb, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D, QT>(s.q, 2 * qb + s2, toff, db), db8, dk[db], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          dv[db][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, pb[kb], dv[db][kb], 0, 0, 0);
+          dk[db][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, db8[kb], dk[db][kb], 0, 0, 0);
         }
       }
     }
@@ -692,21 +709,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
     if (t + 1 < nt) step(st1, st0, t + 1);
     if (t + 2 < nt) step(st2, st1, t + 2);
   }
-  if (!k_ok) return;
   // dK = scale dS^T Q = (dS^T Q') / log2 e
   const float kscale = 1.f / kLog2e;
-  const int64_t orow = (int64_t(key) * a.H + head) * D;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!k_ok[kb]) continue;
+    const int64_t orow = (int64_t(key[kb]) * a.H + head) * D;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d0 = db * 32 + 8 * gq + 4 * half;
+    for (int db = 0; db < D / 16; ++db) {
+      const int d0 = 16 * db + 4 * g;
       *reinterpret_cast<float4*>(p.dv + orow + d0) =
-          make_float4(dv[db][4 * gq], dv[db][4 * gq + 1], dv[db][4 * gq + 2], dv[db][4 * gq + 3]);
+          make_float4(dv[db][kb][0], dv[db][kb][1], dv[db][kb][2], dv[db][kb][3]);
       *reinterpret_cast<float4*>(p.dk + orow + d0) =
-          make_float4(dk[db][4 * gq] * kscale, dk[db][4 * gq + 1] * kscale, dk[db][4 * gq + 2] * kscale,
-                      dk[db][4 * gq + 3] * kscale);
+          make_float4(dk[db][kb][0] * kscale, dk[db][kb][1] * kscale, dk[db][kb][2] * kscale,
+                      dk[db][kb][3] * kscale);
     }
+  }
 }
 
 template <typename K>
