@@ -104,36 +104,52 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(u32x4 w, float c) {
 // the dQ kernel's transpose-read offsets undo it.
 
 // Row-major [kTile][D] bf16 LDS tile (K, Q' or dO), read both as rows
-// (16-byte reads, 16 consecutive rows at one granule) and by transpose reads
-// (per 32 lanes: 4 consecutive rows x 4 granules).  For D = 128 rows are 256
-// bytes and granule g of row r is stored at g ^ f(r), f(r) = ((r & 3) << 2) |
-// ((r >> 2) & 3), a rotation of r mod 16: both patterns then cover 16
-// distinct granules, i.e. all 64 banks.  Otherwise (D = 64, or the dK/dV
-// kernel, whose registers cannot spare the XOR's per-read address arithmetic)
-// rows are padded by 64 bytes and skewed: granule g of row r is stored at
-// granule g + ((r >> 2) & 3).  16 rows at one granule, and the 4 rows x 4
-// granules of a 32-lane transpose read, then fall in distinct bank groups.
-template <int D, bool kSwzOn = true>
+// (16-byte reads: per 16 lanes, 16 consecutive rows at one granule) and by
+// transpose reads (8-byte reads: 16 lanes read 4 consecutive rows 4 j .. at
+// two adjacent granules, j being the lane group).  For D = 128 rows are 256
+// bytes (all 64 banks) and granule g of row r is stored at g ^ swz(r), with
+// swz(r) = (a << 1) | ((b ^ c) << 3) | c for a = r & 3, b = (r >> 2) & 1,
+// c = (r >> 3) & 1: swz is a bijection on r mod 16, so the row reads cover 16
+// distinct granules; and swz(r) >> 1 is a bijection on the 8 rows of any two
+// lane groups served together (rows 0..7 or 8..15, and rows {0..3, 8..11} or
+// {4..7, 12..15}), so the transpose reads' granule pairs {x, x ^ 1} are
+// disjoint however the hardware pairs the groups.
+// For D = 64, and in the dK/dV kernel (whose register allocation holds with
+// it), rows are padded by 64 bytes and skewed: granule g of row r is stored
+// at granule g + skew(r), skew(r) = (b << 1) | c.  Rows r and r + 4 start on
+// the same bank (a row is 80 or 48 banks) and their skews differ by two
+// granules, so the transpose reads of lane groups j and j + 1 do not overlap
+// (those of groups j and j + 2, rows r and r + 8, overlap by one granule if
+// the hardware serves them together); the four skews of a 16-row block are
+// distinct, so the row reads do not overlap either.
+template <int D, bool kPadded = false>
 struct RowTile {
-  static constexpr bool kSwz = kSwzOn && D == 128;
+  static constexpr bool kSwz = !kPadded && D == 128;
   static constexpr int RB = kSwz ? D * 2 : (D + 32) * 2;
   static constexpr int kBytes = kTile * RB;
-  static __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+  static __device__ __forceinline__ int swz(int row) {
+    return ((row & 3) << 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 3) | ((row >> 3) & 1);
+  }
+  static __device__ __forceinline__ int skew(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
   static __device__ __forceinline__ int off(int row, int gran) {
     if constexpr (kSwz) return row * RB + ((gran ^ swz(row)) << 4);
-    else return row * RB + ((gran + ((row >> 2) & 3)) << 4);
+    else return row * RB + ((gran + skew(row)) << 4);
   }
 };
 
 // Transposed [D][64] bf16 V tile of the dQ kernel, read by transpose reads
-// only (per 32 lanes: 4 consecutive rows d, two of each parity).  Rows are
-// 128 bytes; granule g of row d is stored at g ^ (((d >> 1) & 1) << 2) so the
-// two rows of one parity fall in different halves of their 32 banks.
+// only (16 lanes read rows d = 8 j + {0..3} at two adjacent granules, j being
+// the lane group).  Rows are 128 bytes, so rows of one parity share 32
+// banks; granule g of row d is stored at g ^ swz(d), swz(d) =
+// (((d >> 1) & 1) << 2) | ((((d >> 3) ^ (d >> 4)) & 1) << 1), which gives the
+// four same-parity rows of any two lane groups served together distinct
+// granule pairs.
 template <int D>
 struct VtTile {
   static constexpr int RB = kTile * 2;
   static constexpr int kBytes = D * RB;
-  static __device__ __forceinline__ int off(int d, int gran) { return d * RB + ((gran ^ (((d >> 1) & 1) << 2)) << 4); }
+  static __device__ __forceinline__ int swz(int d) { return (((d >> 1) & 1) << 2) | ((((d >> 3) ^ (d >> 4)) & 1) << 1); }
+  static __device__ __forceinline__ int off(int d, int gran) { return d * RB + ((gran ^ swz(d)) << 4); }
 };
 
 // The A operand of an MFMA 16x16x32 (8 bf16 per lane) from two transpose
@@ -213,8 +229,8 @@ __device__ __forceinline__ void wg_barrier() {
 template <int D>
 struct DqStage {
   static constexpr int kVBytes =
-      RowTile<D, true>::kBytes > VtTile<D>::kBytes ? RowTile<D, true>::kBytes : VtTile<D>::kBytes;
-  char k[RowTile<D, true>::kBytes];
+      RowTile<D>::kBytes > VtTile<D>::kBytes ? RowTile<D>::kBytes : VtTile<D>::kBytes;
+  char k[RowTile<D>::kBytes];
   char v[kVBytes];
 };
 
@@ -232,19 +248,19 @@ __device__ __forceinline__ void dma_rowtile(__amdgpu_buffer_rsrc_t r, char* lds,
   const int row = s / G, sg = s % G;
   int gran;
   if constexpr (T::kSwz) gran = sg ^ T::swz(row);
-  else gran = min(max(sg - ((row >> 2) & 3), 0), D / 8 - 1);
+  else gran = min(max(sg - T::skew(row), 0), D / 8 - 1);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + ins * 1024), 16,
                                            (row0 + uint32_t(row)) * rs + uint32_t(gran) * 16, 0, 0, 0);
 }
 
 // LDS-DMA load `ins` of a transposed [D][64] V tile stored at byte offset
 // `tile` of the buffer: slot s is row d = s / 8, slot s % 8, holding granule
-// slot ^ (((d >> 1) & 1) << 2) (VtTile's layout, an involution).
+// slot ^ swz(d) (VtTile's layout, an involution).
 template <int D>
 __device__ __forceinline__ void dma_vttile(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t tile, int ins, int lane) {
   const int s = ins * 64 + lane;
   const int d = s >> 3, sg = s & 7;
-  const int gran = sg ^ (((d >> 1) & 1) << 2);
+  const int gran = sg ^ VtTile<D>::swz(d);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + ins * 1024), 16,
                                            tile + uint32_t(d) * 128 + uint32_t(gran) * 16, 0, 0, 0);
 }
@@ -259,7 +275,7 @@ __device__ __forceinline__ void dma_vttile(__amdgpu_buffer_rsrc_t r, char* lds, 
 // being read and inserts no wait for the fill before the reads.
 template <int D, int W>
 __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
-  using KT = RowTile<D, true>;
+  using KT = RowTile<D>;
   using VT = VtTile<D>;
   constexpr int BQ = 32 * W;           // queries per workgroup
   constexpr int HW = W / 2;            // waves per tile side
@@ -517,15 +533,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq_kernel(AttnBwdArgs p) {
 // LDS-DMA from the stage being read and does not wait for the fill.
 template <int D>
 struct DkvStage {
-  char q[RowTile<D, false>::kBytes];
-  char g[RowTile<D, false>::kBytes];
+  char q[RowTile<D, true>::kBytes];
+  char g[RowTile<D, true>::kBytes];
   float lse[kTile];
   float dl[kTile];
 };
 
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
-  using QT = RowTile<D, false>;  // padded and skewed: the XOR swizzle's address arithmetic spills here
+  using QT = RowTile<D, true>;  // padded and skewed
   constexpr int G = QT::RB / 16;  // 16-byte slots per LDS row, padding included
   constexpr int NI = G / 4;       // 1 KB LDS-DMA loads per wave per tile side (4 waves per side)
   static_assert(G % 4 == 0, "tile side splits over four waves");
@@ -569,9 +585,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dk[db][kb][r] = dv[db][kb][r] = 0.f;
-  // Byte offsets of this lane's LDS operand reads (the padded, skewed layout
-  // depends on the row mod 16 only, so query blocks and steps are plain
-  // offsets):
+  // Byte offsets of this lane's LDS operand reads (the tile layout depends
+  // on the row mod 16 only, so query blocks and steps are plain offsets):
   //  * Q' and dO rows (A of S and dP): query 16 qb + r16, granule 4 ks + g;
   //  * dO^T and Q'^T (A of dV^T and dK^T) by two transpose reads: the address
   //    lane (e = r16 >> 2, m = r16 & 3) of group g points at query row
