@@ -17,7 +17,8 @@
 //                     for, also Q' (below) as bf16 into the first half of dq.
 //   bwd_dkv_kernel    per 256 keys of the current chunk (8 waves x 32):
 //                     loop over 64-query tiles; S = Q' K^T, dP = dO V^T (K/V
-//                     fragments in registers), then dV^T += dO^T P and
+//                     fragments in registers, starting from -lse2 and
+//                     -delta of each query), then dV^T += dO^T P and
 //                     dK^T += Q'^T dS with dO^T and Q'^T from transpose reads.
 //                     The Q' and dO tiles stream straight into a 3-stage LDS
 //                     ring (LDS-DMA), two tiles ahead.
@@ -641,13 +642,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   auto compute = [&](const DkvStage<D>& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
+      // element i of lane (r16, g) in block (qq, kb): query 32 qs + 16 qq + 4 g + i.
+      // The accumulators start at -lse2 and -delta of their query, so S comes
+      // out as log2 P and dP as dP - delta.
       f32x4 sc[2][2], dp[2][2];  // [query block of the step][key block]
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q4 = 32 * qs + 16 * qq + 4 * g;
+        const float4 l4 = *reinterpret_cast<const float4*>(&s.lse[q4]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[q4]);
+        const f32x4 si = {-l4.x * kLog2e, -l4.y * kLog2e, -l4.z * kLog2e, -l4.w * kLog2e};
+        const f32x4 di = {-d4.x, -d4.y, -d4.z, -d4.w};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[qq][kb][r] = dp[qq][kb][r] = 0.f;
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[qq][kb] = si;
+          dp[qq][kb] = di;
+        }
+      }
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const int row0 = 16 * (2 * qs + qq) * QT::RB;
@@ -662,26 +673,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
           }
         }
       }
-      // element i of lane (r16, g) in block (qq, kb): query 32 qs + 16 qq + 4 g + i
       bf16x8 pb[2], db8[2];
       {
         f32x8 pf[2], df[2];
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const int q4 = 32 * qs + 16 * qq + 4 * g;
-          const float4 l4 = *reinterpret_cast<const float4*>(&s.lse[q4]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[q4]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pr = __builtin_amdgcn_exp2f(fmaf(-lv[i], kLog2e, sc[qq][kb][i]));  // log2 units
+              const float pr = __builtin_amdgcn_exp2f(sc[qq][kb][i]);
               pf[kb][4 * qq + i] = pr;
-              df[kb][4 * qq + i] = pr * (dp[qq][kb][i] - dv4[i]);
+              df[kb][4 * qq + i] = pr * dp[qq][kb][i];
             }
-        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           pb[kb] = __builtin_convertvector(pf[kb], bf16x8);
