@@ -123,3 +123,30 @@ def test_bwd_int8_cache():
     """INT8 cache: the detached context is the exactly dequantised stored K/V
     (the oracle's int8 history); the current chunk stays bf16."""
     run_bwd(166, 50, 2, 2, 6, 2, 128, 4, int8=True)
+
+
+def _random_bwd_geometries(n=12, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        C = int(rng.integers(1, 4))
+        T = int(rng.integers(3, 90))
+        nsc = int(rng.integers(0, 3))
+        R = int(rng.integers(0, 4))
+        H = int(rng.integers(1, 4))
+        D = int(rng.choice([64, 128]))
+        n_pre = int(rng.integers(0, nsc + R + 3))
+        with_cur = bool(n_pre == 0 or i % 4 != 3)  # every fourth: cache-only (dQ alone)
+        out.append((300 + i, T, C, nsc * C, (R + 1) * C, H, D, n_pre, with_cur, i % 3 == 2))
+    return out
+
+
+@pytest.mark.parametrize("geom", _random_bwd_geometries(),
+                         ids=lambda g: f"cfg{g[0]}-D{g[6]}{'-i8' if g[9] else ''}{'' if g[8] else '-dq'}")
+def test_bwd_random_geometries(geom):
+    """A fixed draw of small geometries (tokens per frame, frames per chunk,
+    sink chunks, ring slots, heads, head dim, chunks already cached, bf16 or
+    int8 cache, with or without the current chunk): every row of every
+    gradient against the float64 oracle."""
+    cfg_id, T, C, S, W, H, D, n_pre, with_cur, int8 = geom
+    run_bwd(cfg_id, T, C, S, W, H, D, n_pre, with_cur=with_cur, int8=int8)
