@@ -40,8 +40,9 @@
 // are written in fp32 (token-major [n][H][D]).
 //
 // Tiles sit in LDS in layouts (RowTile, VtTile) whose XOR swizzles or skewed
-// padding keep both the 16-byte row reads and the transpose reads free of
-// bank conflicts.  In the dQ kernel the cache's V stays transposed ([D][64]
+// padding spread the 16-byte row reads and the transpose reads over the LDS
+// banks (conflict-free in the dQ kernel; the dK/dV kernel's padded tile
+// leaves its transpose reads one 2-way conflict).  In the dQ kernel the cache's V stays transposed ([D][64]
 // per 64 keys, as the bf16 cache stores it) and its rows are read back with
 // transpose reads; the caller's row-major current chunk is read as rows.
 
