@@ -597,14 +597,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
   //    queries 4 g .. 4 g + 3 (and 16 + 4 g ..): the query order in which the
   //    S and dS accumulators of the step's two query blocks pack into the
   //    P and dS operands.
-  int qoff[D / 32], toff[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qoff[ks] = QT::off(r16, 4 * ks + g);
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    const int col = 16 * db + 4 * (r16 & 3);
-    toff[db] = QT::off(4 * g + (r16 >> 2), col >> 3) + (col & 7) * 2;
-  }
+  //  The skewed layout advances a row's granules linearly, so one base
+  //  offset serves every ks (+64 bytes a step) and one every db (+32 bytes).
+  const int qoff0 = QT::off(r16, g);
+  const int toff0 = QT::off(4 * g + (r16 >> 2), (4 * (r16 & 3)) >> 3) + ((4 * (r16 & 3)) & 7) * 2;
 
   // Tile loads, straight into LDS (dma_rowtile).  Waves 0-3 fill the Q' side
   // (the delta kernel's bf16(Q c) copy at the start of dq), waves 4-7 the dO
@@ -665,8 +661,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
         const int row0 = 16 * (2 * qs + qq) * QT::RB;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(s.q + row0 + qoff[ks]);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(s.g + row0 + qoff[ks]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(s.q + row0 + 64 * ks + qoff0);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(s.g + row0 + 64 * ks + qoff0);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             sc[qq][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kb][ks], sc[qq][kb], 0, 0, 0);
@@ -695,8 +691,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(AttnBwdArgs p) {
       }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 ga = tr_pair(s.g + (32 * qs) * QT::RB + toff[db], 16 * QT::RB);
-        const bf16x8 qa = tr_pair(s.q + (32 * qs) * QT::RB + toff[db], 16 * QT::RB);
+        const int to = (32 * qs) * QT::RB + 32 * db + toff0;
+        const bf16x8 ga = tr_pair(s.g + to, 16 * QT::RB);
+        const bf16x8 qa = tr_pair(s.q + to, 16 * QT::RB);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           dv[db][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, pb[kb], dv[db][kb], 0, 0, 0);
